@@ -1,0 +1,91 @@
+"""Scalar-loop twin of the oracle for tiny shapes.  TEST INFRASTRUCTURE ONLY.
+
+Written independently of rmx_oracle.py from the same definitions (pages cited by title
+in rmx_oracle.py): every sum is an explicit Python loop over plain floats and GELU
+uses ``math.erf``.  It exists to catch vectorisation mistakes in the NumPy oracle
+(a wrong axis, a broadcast, a transposed operand); it is far too slow for anything
+but a few hundred multiply-adds per sample.
+"""
+from __future__ import annotations
+
+import math
+
+
+def _mix(x, T, D):
+    q = D // T
+    out = [[0.0] * D for _ in range(T)]
+    for h in range(T):
+        for c in range(D):
+            t, r = divmod(c, q)          # output column c of row h takes head h of token t
+            out[h][c] = x[t][h * q + r]
+    return out
+
+
+def _ln_row(r, g, b, eps):
+    n = len(r)
+    mu = 0.0
+    for v in r:
+        mu += v
+    mu /= n
+    var = 0.0
+    for v in r:
+        var += (v - mu) * (v - mu)
+    var /= n
+    inv = 1.0 / math.sqrt(var + eps)
+    return [g[j] * (r[j] - mu) * inv + b[j] for j in range(n)]
+
+
+def _gelu(u):
+    return u * 0.5 * (1.0 + math.erf(u / math.sqrt(2.0)))
+
+
+def _linear(x, W, bias):
+    # x: [n_in], W: [n_in][n_out] (row-vector convention), bias: [n_out]
+    n_out = len(bias)
+    y = []
+    for j in range(n_out):
+        acc = 0.0
+        for i in range(len(x)):
+            acc += x[i] * W[i][j]
+        y.append(acc + bias[j])
+    return y
+
+
+def _tolist(a):
+    return a.tolist() if hasattr(a, "tolist") else a
+
+
+def forward_sample(x, layers, eps=1e-5):
+    """One sample x[T][D] through all blocks; returns (o[D], x_L[T][D], gates)."""
+    x = [[float(v) for v in row] for row in _tolist(x)]
+    T, D = len(x), len(x[0])
+    gates_all = []
+    for p in layers:
+        p = {key: _tolist(v) for key, v in p.items()}
+        m = _mix(x, T, D)
+        s = [_ln_row([m[t][j] + x[t][j] for j in range(D)], p["ln1_g"], p["ln1_b"], eps)
+             for t in range(T)]
+        v = []
+        gates = []
+        for t in range(T):
+            if "Wg" in p:
+                E = len(p["Wg"][t][0])
+                g = [max(0.0, sum(s[t][i] * p["Wg"][t][i][e] for i in range(D))) for e in range(E)]
+                gates.append(g)
+                acc = [0.0] * D
+                for e in range(E):
+                    if g[e] <= 0.0:
+                        continue
+                    hid = [_gelu(u) for u in _linear(s[t], p["We1"][t][e], p["be1"][t][e])]
+                    y = _linear(hid, p["We2"][t][e], p["be2"][t][e])
+                    for j in range(D):
+                        acc[j] += g[e] * y[j]
+                v.append(acc)
+            else:
+                hid = [_gelu(u) for u in _linear(s[t], p["W1"][t], p["b1"][t])]
+                v.append(_linear(hid, p["W2"][t], p["b2"][t]))
+        x = [_ln_row([v[t][j] + s[t][j] for j in range(D)], p["ln2_g"], p["ln2_b"], eps)
+             for t in range(T)]
+        gates_all.append(gates if gates else None)
+    o = [sum(x[t][j] for t in range(T)) / T for j in range(D)]
+    return o, x, gates_all
