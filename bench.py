@@ -1,0 +1,201 @@
+"""Benchmark of the RankMixer block forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--batch B] [--workload NAME] [--sweep]
+
+A step is one forward pass of the whole hot path (L blocks of mixing + LayerNorm +
+per-token FFN + LayerNorm, then the mean pool) over one batch of synthetic input that is
+already resident in HBM.  Prints ONE JSON line: samples/s of the RankMixer-1B shape
+(T=32, D=1536, k=4, L=2, bf16, B=2048), its TFLOP/s (GEMM FLOPs, 4 k L T D^2 per sample)
+and fraction of the bf16 dense MFMA peak, the roofline of the dominant kernel (timed
+with HIP events on the stream it runs on), and the fp64 CPU oracle timed on a bounded
+sample on this host's cores.  --sweep prints one line per serving batch size instead.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "samples/sec + achieved TFLOP/s (% bf16 MFMA peak) for RankMixer-1B block fwd"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+GEMM_SOURCE = os.path.join(ROOT, "rankmixer_block_forward_amd", "csrc", "rmx_gemm.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="rankmixer-1b")
+    p.add_argument("--batch", type=int, default=None)
+    p.add_argument("--sweep", action="store_true", help="one line per serving batch size")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-samples", type=int, default=384)
+    return p.parse_args()
+
+
+def gemm_counts(cfg, B):
+    """Algorithmic FLOPs and HBM bytes of one launch of each grouped GEMM.
+
+    GEMM1: S[T,B,D] x W1[T,D,kD] -> H[T,B,kD];  GEMM2: H x W2[T,kD,D] + S -> Y[T,B,D] fp32.
+    Bytes: weights once + activations read once + output written once (bf16 = 2 B)."""
+    T, D, kD = cfg.T, cfg.D, cfg.kD
+    flops = 2.0 * B * T * D * kD
+    w = 2.0 * T * D * kD
+    g1 = w + 2.0 * B * T * D + 2.0 * B * T * kD
+    g2 = w + 2.0 * B * T * kD + 2.0 * B * T * D + 4.0 * B * T * D
+    return {"gemm1_gelu": (flops, g1), "gemm2_residual": (flops, g2)}
+
+
+def file_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel, cfg, B):
+    """Per-launch HBM bytes measured with rocprofv3 counters, if taken on the current
+    kernel source at this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemm_source_sha256_16") != file_hash(GEMM_SOURCE):
+        return None
+    entry = rec.get("kernels", {}).get(kernel)
+    if not entry or entry.get("workload") != f"{cfg.name} B={B}":
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def time_forward(cfg, B, steps, warmup):
+    import torch
+    import rankmixer_block_forward_amd as rmx
+    from rankmixer_block_forward_amd import synth
+
+    t0 = time.time()
+    inp = synth.make_inputs(cfg.with_(B=B), seed=0)
+    X, w = rmx.upload(inp)
+    del inp
+    print(f"[bench] inputs {cfg.name} B={B} generated and resident in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+    h = rmx.Handle.for_config(cfg, max_batch=B)
+    out = torch.empty((B, cfg.D), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        h.forward(X, w, out=out)
+    torch.cuda.synchronize()
+    h.profile_reset()
+    h.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        h.forward(X, w, out=out)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    h.profile_enable(False)
+    prof = h.profile_read()
+    assert torch.isfinite(out).all().item(), "non-finite output"
+    h.close()
+    return elapsed, prof
+
+
+def roofline(cfg, B, prof):
+    counts = gemm_counts(cfg, B)
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    # dominant kernel: the grouped GEMM with the larger total time
+    kern = max(counts, key=lambda k: prof.get(k, {}).get("total_ms", 0.0))
+    flops, nbytes = counts[kern]
+    avg_s = prof[kern]["avg_ms"] / 1e3
+    mfma_bound = flops / nbytes > ridge
+    traffic = traffic_for(kern, cfg, B)
+    if mfma_bound:
+        achieved = flops / avg_s / 1e12
+        r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = nbytes / avg_s / 1e9
+        r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    r["traffic"] = traffic
+    r["kernel"] = kern
+    r["avg_launch_ms"] = round(prof[kern]["avg_ms"], 4)
+    r["algorithmic_flops_per_launch"] = flops
+    r["algorithmic_bytes_per_launch"] = nbytes
+    return r
+
+
+def cpu_baseline(cfg, n):
+    """The fp64 oracle, as it stands, on n samples of the same workload."""
+    import numpy as np
+    import oracle
+    from rankmixer_block_forward_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    inp = synth.make_inputs(cfg.with_(B=n), seed=0)
+    t0 = time.perf_counter()
+    o, _, _ = oracle.forward(inp.X, inp.layers(), cfg.eps)
+    el = time.perf_counter() - t0
+    assert np.isfinite(o).all()
+    return {"value": round(n / el, 3), "unit": "samples/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} samples of {cfg.name} (T={cfg.T}, D={cfg.D}, k={cfg.k}, L={cfg.L}), "
+                      f"fp64 NumPy, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from rankmixer_block_forward_amd import synth
+    cfg = synth.CONFIGS[args.workload]
+    batches = list(synth.SWEEP_BATCHES) if args.sweep else [args.batch or cfg.B]
+    if args.sweep:
+        cfg = synth.SWEEP
+    for B in batches:
+        elapsed, prof = time_forward(cfg, B, args.steps, args.warmup)
+        ms = elapsed / args.steps * 1e3
+        flops = B * 4.0 * cfg.k * cfg.L * cfg.T * cfg.D * cfg.D
+        tflops = flops / (ms / 1e3) / 1e12
+        line = {
+            "metric": METRIC,
+            "value": round(B / (ms / 1e3), 1),
+            "unit": "samples/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(ms, 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": cfg.dtype,
+            "data": "synthetic (seeded Gaussian inputs and random-init weights at the workload's shapes)",
+            "config": {"workload": cfg.name, "B": B, "T": cfg.T, "H": cfg.T, "D": cfg.D, "k": cfg.k,
+                       "L": cfg.L, "zeroed_token_rows": cfg.zero_frac, "parallelism": "single GPU"},
+            "tflops": round(tflops, 2),
+            "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "kernels_ms_per_step": {k: round(v["total_ms"] / args.steps, 4) for k, v in prof.items()
+                                    if k != "_dropped"},
+            "roofline": roofline(cfg, B, prof),
+        }
+        if not args.sweep and not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_samples)
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

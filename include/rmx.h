@@ -1,0 +1,176 @@
+/*
+ * rmx.h -- C ABI of the MI355X (gfx950) RankMixer block forward library (librmx.so).
+ *
+ * What it computes.  For a batch of feature-token matrices X[B, T, D] and L blocks,
+ * each block n = 1..L does (pages cited by title and section):
+ *   S   = LN1(TokenMixing(X) + X)          "RankMixer: Scaling Up Ranking Models in
+ *   X'  = LN2(PFFN(S) + S)                  Industrial Recommenders" (translation),
+ *                                           section 3.1 eq (1) and 3.3.1 eq (5)
+ *   TokenMixing with H = T heads:  M[h, t*q + r] = X[t, h*q + r],  q = D / T
+ *                                           (same paper, section 3.3.1 eq (3)-(4);
+ *                                           "RankMixer 详解（1）", section 3.1)
+ *   PFFN: token t has its own FFN,  v_t = GELU(s_t W1[t] + b1[t]) W2[t] + b2[t],
+ *         GELU exact (u * Phi(u))       (paper section 3.3.2 eq (6)-(9);
+ *                                        "RankMixer 详解（1）", section 4.1)
+ *   Sparse-MoE PFFN (optional): v_t = sum_e g_e * expert_e(s_t), g = ReLU(s_t Wg[t])
+ *                                       (paper section 3.4 eq (10))
+ *   LN: per row over D, biased variance, eps inside the square root, one gamma/beta
+ *       of length D per LayerNorm shared by the T rows ("RankMixer 详解（1）", 3.3)
+ * and the output is the mean over tokens of X_L: out[b, :] = (1/T) sum_t X_L[b, t, :]
+ * (paper section 3.1; "RankMixer 详解（1）", section 5.1).
+ *
+ * Conventions shared by every entry point.
+ *   - Pointers named as device pointers must point to device memory of the current
+ *     HIP device (hipMalloc'd, or torch CUDA tensors on ROCm); every such pointer must
+ *     be 16-byte aligned.  All arrays are dense, row-major, last index fastest.
+ *   - The caller owns every buffer it passes, and the stream.  The library keeps no
+ *     caller pointer after a call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the
+ *     call returns without synchronising.  Outputs are overwritten, never accumulated.
+ *   - Errors: every argument and shape check runs on the host before anything is
+ *     enqueued; on any error nothing is enqueued and the outputs are untouched.
+ *     A failed launch returns RMX_ERR_HIP.  A fault during execution surfaces at the
+ *     caller's next synchronisation of the stream.  rmx_last_error() gives the detail.
+ *   - A handle may be used by one stream at a time; distinct handles are independent.
+ */
+#ifndef RMX_H
+#define RMX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RMX_ABI_VERSION 1
+
+typedef struct rmx_handle rmx_handle; /* opaque, owned by the library */
+
+typedef enum {
+  RMX_OK = 0,
+  RMX_ERR_INVALID_ARG = 1,   /* a null/misaligned/host pointer, a shape or size mismatch */
+  RMX_ERR_UNSUPPORTED = 2,   /* valid but not supported here: device not gfx950, a size limit */
+  RMX_ERR_OUT_OF_MEMORY = 3, /* workspace allocation failed in rmx_create */
+  RMX_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} rmx_status;
+
+typedef enum { RMX_FP32 = 0, RMX_BF16 = 1 } rmx_dtype;
+
+/* Model configuration, fixed for the life of a handle.
+ *   T, D     tokens per sample and width; H = T always, D % T == 0 required
+ *            (paper section 3.3.1: H = T keeps the token count for the residual).
+ *   k        FFN expansion: the hidden width is k*D (paper section 3.3.2 eq (7)).
+ *   L        number of stacked blocks (paper section 3.1 eq (1)), L >= 1.
+ *   dtype    storage and MFMA input type of X, every weight, S and the hidden
+ *            activations.  Accumulation, LayerNorm and GELU are always fp32.
+ *   ln_eps   LayerNorm epsilon (1e-5 in "RankMixer 详解（1）", section 6.1).
+ *   max_batch  largest B a forward call may pass; the workspace is sized for it.
+ *   moe_experts  0 = dense per-token FFN; E > 0 = Sparse-MoE PFFN with E experts per
+ *            token (paper section 3.4 eq (10)); moe_hidden = hidden width of one expert.
+ * Limits: dtype BF16 needs D % 8 == 0 and (D/T) % 8 == 0, dtype FP32 needs nothing
+ * more; D <= 4096; T*D*sizeof(dtype) <= 96 KiB (one sample must fit the on-chip LDS
+ * of one workgroup).  Beyond a limit rmx_create returns RMX_ERR_UNSUPPORTED. */
+typedef struct {
+  int32_t T;
+  int32_t D;
+  int32_t k;
+  int32_t L;
+  int32_t dtype;      /* rmx_dtype */
+  float ln_eps;
+  int64_t max_batch;
+  int32_t moe_experts;
+  int32_t moe_hidden;
+} rmx_config;
+
+/* Device pointers to the parameters of all L blocks, each stacked over L, in the
+ * config's dtype.  Row-vector convention x W + b (paper section 3.3.2 eq (7)).
+ *   W1 [L, T, D, kD]   b1 [L, T, kD]   (b1 may be NULL: zeros)
+ *   W2 [L, T, kD, D]   b2 [L, T, D]    (b2 may be NULL: zeros)
+ *   ln1_g, ln1_b, ln2_g, ln2_b  [L, D]  (gamma/beta of the two LayerNorms of a block)
+ * Sparse-MoE only (else NULL; W1/b1/W2/b2 are then unused and may be NULL):
+ *   Wg  [L, T, D, E]              router weights, no bias
+ *   We1 [L, T, E, D, h]  be1 [L, T, E, h]   (be1 may be NULL)
+ *   We2 [L, T, E, h, D]  be2 [L, T, E, D]   (be2 may be NULL)                        */
+typedef struct {
+  const void* W1;
+  const void* b1;
+  const void* W2;
+  const void* b2;
+  const void* ln1_g;
+  const void* ln1_b;
+  const void* ln2_g;
+  const void* ln2_b;
+  const void* Wg;
+  const void* We1;
+  const void* be1;
+  const void* We2;
+  const void* be2;
+} rmx_weights;
+
+/* Validates cfg, checks that the current HIP device is gfx950, and allocates the
+ * workspace for cfg->max_batch samples on it.  On success *out_handle is a new handle;
+ * on failure it is set to NULL and nothing stays allocated. */
+rmx_status rmx_create(const rmx_config* cfg, rmx_handle** out_handle);
+
+/* Frees the handle and its workspace (synchronises the device first).  NULL is a no-op. */
+rmx_status rmx_destroy(rmx_handle* h);
+
+/* The forward pass.  X [B, T, D] (device, dtype) -> out [B, D] (device, fp32), the mean
+ * pool of X_L.  L and k must equal the handle's (they are restated so that a caller's
+ * mismatch is caught).  0 <= B <= max_batch; B == 0 enqueues nothing and returns OK. */
+rmx_status rmx_block_forward(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w,
+                             int32_t L, int32_t k, float* out, void* stream);
+
+/* rmx_block_forward plus optional diagnostic outputs (either may be NULL):
+ *   xl_out   [B, T, D] (device, dtype)  X_L, the last block's output, rounded to dtype
+ *   gate_out [L, B, T, E] (device, fp32) the Sparse-MoE gate values of every block
+ *            (MoE handles only; must be NULL for a dense handle). */
+rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w,
+                                int32_t L, int32_t k, float* out, void* xl_out,
+                                float* gate_out, void* stream);
+
+/* Token Mixing alone (H = T): Y[b, h, t*q + r] = X[b, t, h*q + r], q = D/T, for every
+ * sample; X and Y are device arrays [B, T, D] of `dtype` and must not overlap.  Uses
+ * the same device index map as the forward pass.  Exact: values are copied bit for bit.
+ * (Paper section 3.3.1 eq (3)-(4); "RankMixer 详解（1）", section 3.1.) */
+rmx_status rmx_token_mix(const void* X, void* Y, int64_t B, int32_t T, int32_t D,
+                         int32_t dtype, void* stream);
+
+/* Kernel-level timing.  While enabled, every kernel the handle launches is bracketed by
+ * a pair of HIP events recorded on the caller's stream; rmx_profile_read() waits for the
+ * recorded events and returns, per kernel kind, the summed duration in ms and the
+ * number of launches since the last reset.  Up to 65536 launches are kept between
+ * reads; later ones are counted in `dropped` and not timed. */
+typedef enum {
+  RMX_KERNEL_ROWS = 0,     /* LN2 of the previous block (if any) + mixing + residual + LN1 */
+  RMX_KERNEL_GEMM1 = 1,    /* per-token S W1 + b1, GELU -> hidden */
+  RMX_KERNEL_GEMM2 = 2,    /* per-token hidden W2 + b2 + S -> pre-LN2 rows */
+  RMX_KERNEL_POOL = 3,     /* LN2 of the last block + mean pool (+ X_L) */
+  RMX_KERNEL_MOE_GATE = 4, /* router + token -> expert lists */
+  RMX_KERNEL_MOE_FFN1 = 5, /* expert first layer (gathered rows) + GELU */
+  RMX_KERNEL_MOE_FFN2 = 6, /* expert second layer, gate-weighted */
+  RMX_KERNEL_MOE_COMBINE = 7, /* sum of expert outputs + S -> pre-LN2 rows */
+  RMX_KERNEL_COUNT = 8
+} rmx_kernel_kind;
+
+rmx_status rmx_profile_enable(rmx_handle* h, int32_t enable);
+rmx_status rmx_profile_read(rmx_handle* h, double* total_ms /*[RMX_KERNEL_COUNT]*/,
+                            int64_t* launches /*[RMX_KERNEL_COUNT]*/, int64_t* dropped);
+rmx_status rmx_profile_reset(rmx_handle* h);
+const char* rmx_kernel_name(int32_t kind);
+
+/* Short text for a status code; never NULL. */
+const char* rmx_status_string(rmx_status s);
+
+/* Detail of the last failure: of this handle's last call when h != NULL, else of the
+ * calling thread's last call (rmx_create, rmx_token_mix).  Never NULL; "" if none. */
+const char* rmx_last_error(const rmx_handle* h);
+
+/* RMX_ABI_VERSION of the built library. */
+int32_t rmx_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMX_H */

@@ -1,0 +1,237 @@
+"""Python binding of librmx.so (include/rmx.h): argument marshalling only.
+
+Every step of the forward pass runs in the library's HIP kernels; this module only
+checks that tensors are on the GPU with the right dtype and layout and passes their
+device pointers and the current HIP stream.  PyTorch provides the device memory and
+streams.  There is no fallback: if librmx.so is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "librmx.so")
+
+RMX_OK, RMX_ERR_INVALID_ARG, RMX_ERR_UNSUPPORTED, RMX_ERR_OUT_OF_MEMORY, RMX_ERR_HIP = range(5)
+RMX_FP32, RMX_BF16 = 0, 1
+KERNEL_COUNT = 8
+
+# Every symbol include/rmx.h declares.
+EXPORTS = (
+    "rmx_create", "rmx_destroy", "rmx_block_forward", "rmx_block_forward_ex", "rmx_token_mix",
+    "rmx_profile_enable", "rmx_profile_read", "rmx_profile_reset", "rmx_kernel_name",
+    "rmx_status_string", "rmx_last_error", "rmx_abi_version",
+)
+
+
+class RmxError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"rmx status {status}: {message}")
+        self.status = status
+
+
+class rmx_config(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("D", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("L", ctypes.c_int32), ("dtype", ctypes.c_int32), ("ln_eps", ctypes.c_float),
+                ("max_batch", ctypes.c_int64), ("moe_experts", ctypes.c_int32),
+                ("moe_hidden", ctypes.c_int32)]
+
+
+WEIGHT_NAMES = ("W1", "b1", "W2", "b2", "ln1_g", "ln1_b", "ln2_g", "ln2_b",
+                "Wg", "We1", "be1", "We2", "be2")
+
+
+class rmx_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads librmx.so once; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run python -m rankmixer_block_forward_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.rmx_create.argtypes = [ctypes.POINTER(rmx_config), ctypes.POINTER(vp)]
+    lib.rmx_destroy.argtypes = [vp]
+    lib.rmx_block_forward.argtypes = [vp, vp, i64, ctypes.POINTER(rmx_weights), i32, i32, vp, vp]
+    lib.rmx_block_forward_ex.argtypes = [vp, vp, i64, ctypes.POINTER(rmx_weights), i32, i32, vp,
+                                         vp, vp, vp]
+    lib.rmx_token_mix.argtypes = [vp, vp, i64, i32, i32, i32, vp]
+    lib.rmx_profile_enable.argtypes = [vp, i32]
+    lib.rmx_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
+                                     ctypes.POINTER(i64)]
+    lib.rmx_profile_reset.argtypes = [vp]
+    lib.rmx_kernel_name.argtypes = [i32]
+    lib.rmx_kernel_name.restype = ctypes.c_char_p
+    lib.rmx_status_string.argtypes = [ctypes.c_int]
+    lib.rmx_status_string.restype = ctypes.c_char_p
+    lib.rmx_last_error.argtypes = [vp]
+    lib.rmx_last_error.restype = ctypes.c_char_p
+    lib.rmx_abi_version.restype = i32
+    for name in EXPORTS:
+        if name not in ("rmx_kernel_name", "rmx_status_string", "rmx_last_error", "rmx_abi_version"):
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int, handle=None):
+    if status != RMX_OK:
+        lib = load_library()
+        msg = lib.rmx_last_error(handle).decode()
+        raise RmxError(status, f"{lib.rmx_status_string(status).decode()}: {msg}")
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+    if dtype in ("bf16", torch.bfloat16, RMX_BF16):
+        return RMX_BF16
+    if dtype in ("fp32", torch.float32, RMX_FP32):
+        return RMX_FP32
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def _torch_dtype(code: int):
+    import torch
+    return torch.bfloat16 if code == RMX_BF16 else torch.float32
+
+
+def _ptr(t, name, dtype=None, shape=None):
+    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Handle:
+    """One rmx_handle: a model configuration and its workspace on the current device."""
+
+    def __init__(self, T: int, D: int, k: int, L: int, dtype="bf16", ln_eps: float = 1e-5,
+                 max_batch: int = 2048, moe_experts: int = 0, moe_hidden: int = 0):
+        self._lib = load_library()
+        self.cfg = rmx_config(T, D, k, L, _dtype_code(dtype), ln_eps, max_batch, moe_experts, moe_hidden)
+        self.dtype = _torch_dtype(self.cfg.dtype)
+        h = ctypes.c_void_p()
+        _check(self._lib.rmx_create(ctypes.byref(self.cfg), ctypes.byref(h)))
+        self._h = h
+
+    @classmethod
+    def for_config(cls, cfg, max_batch: int | None = None) -> "Handle":
+        """Handle for a synth.Config workload."""
+        return cls(cfg.T, cfg.D, cfg.k, cfg.L, cfg.dtype, cfg.eps,
+                   cfg.B if max_batch is None else max_batch, cfg.E, cfg.moe_hidden)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.rmx_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def _weights(self, w: dict) -> rmx_weights:
+        s = rmx_weights()
+        for n in WEIGHT_NAMES:
+            t = w.get(n)
+            setattr(s, n, _ptr(t, n, self.dtype))
+        return s
+
+    def forward(self, X, weights: dict, out=None, xl_out=None, gate_out=None, stream=None,
+                L: int | None = None, k: int | None = None):
+        """out[B, D] (fp32) = mean-pooled X_L of the L blocks over X[B, T, D]."""
+        import torch
+        c = self.cfg
+        B = X.shape[0]
+        _ptr(X, "X", self.dtype, (B, c.T, c.D))
+        if out is None:
+            out = torch.empty((B, c.D), dtype=torch.float32, device=X.device)
+        _ptr(out, "out", torch.float32, (B, c.D))
+        _ptr(xl_out, "xl_out", self.dtype, (B, c.T, c.D))
+        if gate_out is not None:
+            _ptr(gate_out, "gate_out", torch.float32, (c.L, B, c.T, c.moe_experts))
+        ws = self._weights(weights)
+        st = self._lib.rmx_block_forward_ex(
+            self._h, _ptr(X, "X"), B, ctypes.byref(ws), c.L if L is None else L, c.k if k is None else k,
+            _ptr(out, "out"), _ptr(xl_out, "xl_out"), _ptr(gate_out, "gate_out"), _stream(stream))
+        _check(st, self._h)
+        return out
+
+    # ---- kernel timing
+    def profile_enable(self, on: bool = True):
+        _check(self._lib.rmx_profile_enable(self._h, int(on)), self._h)
+
+    def profile_reset(self):
+        _check(self._lib.rmx_profile_reset(self._h), self._h)
+
+    def profile_read(self) -> dict:
+        ms = (ctypes.c_double * KERNEL_COUNT)()
+        n = (ctypes.c_int64 * KERNEL_COUNT)()
+        dropped = ctypes.c_int64()
+        _check(self._lib.rmx_profile_read(self._h, ms, n, ctypes.byref(dropped)), self._h)
+        out = {}
+        for i in range(KERNEL_COUNT):
+            if n[i]:
+                out[self._lib.rmx_kernel_name(i).decode()] = {"total_ms": ms[i], "launches": n[i],
+                                                              "avg_ms": ms[i] / n[i]}
+        out["_dropped"] = dropped.value
+        return out
+
+
+def token_mix(X, Y=None, stream=None):
+    """Y[b, h, t*q + r] = X[b, t, h*q + r] on the GPU (the library's mixing kernel)."""
+    import torch
+    lib = load_library()
+    B, T, D = X.shape
+    code = _dtype_code(X.dtype)
+    _ptr(X, "X")
+    if Y is None:
+        Y = torch.empty_like(X)
+    _ptr(Y, "Y", X.dtype, X.shape)
+    _check(lib.rmx_token_mix(_ptr(X, "X"), _ptr(Y, "Y"), B, T, D, code, _stream(stream)))
+    return Y
+
+
+def upload(inputs, device="cuda"):
+    """Device copies of a synth.Inputs: (X, weights dict), in the workload's dtype."""
+    import torch
+    dt = _torch_dtype(_dtype_code(inputs.cfg.dtype))
+
+    def dev(a):
+        return torch.from_numpy(a).to(device=device).to(dt).contiguous()
+
+    w = {n: dev(getattr(inputs, n)) for n in ("W1", "b1", "W2", "b2", "ln1_g", "ln1_b", "ln2_g", "ln2_b")}
+    for n, a in inputs.moe.items():
+        w[n] = dev(a)
+    return dev(inputs.X), w

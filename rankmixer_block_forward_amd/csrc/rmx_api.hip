@@ -1,0 +1,463 @@
+// C ABI of the RankMixer block forward (declared in include/rmx.h): handle and workspace,
+// argument checks, the launch sequence of one forward pass, and kernel timing.
+//
+// Launch sequence for L blocks (all on the caller's stream):
+//   n = 1..L:  rows   (LN2 of block n-1, or X0 for n = 1; mixing; residual; LN1) -> S
+//              gemm1  S[t] W1[t] + b1[t], GELU                                   -> H
+//              gemm2  H[t] W2[t] + b2[t] + S[t]                                   -> Y
+//   then:      rows   LN2 of block L, mean pool over tokens (+ X_L)              -> out
+// (RankMixer paper translation, section 3.1 eq (1) and 3.3; "RankMixer 详解（1）",
+// sections 3-5.)  Workspace, all token-major [T, max_batch, *]: S and H in the model
+// dtype, Y in fp32.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/rmx.h"
+#include "rmx_internal.h"
+
+using namespace rmx;
+
+namespace {
+
+thread_local std::string g_thread_error;
+
+struct ProfPair {
+  int kind;
+  hipEvent_t start, stop;
+};
+
+constexpr size_t PROF_CAP = 65536;
+
+}  // namespace
+
+struct rmx_handle {
+  rmx_config cfg{};
+  int device = -1;
+  void* S = nullptr;   // [T, max_batch, D]   dtype
+  void* H = nullptr;   // [T, max_batch, kD]  dtype
+  float* Y = nullptr;  // [T, max_batch, D]   fp32
+  std::string last_error;
+  bool prof = false;
+  std::vector<ProfPair> pending;
+  std::vector<hipEvent_t> free_events;
+  double total_ms[RMX_KERNEL_COUNT] = {};
+  int64_t launches[RMX_KERNEL_COUNT] = {};
+  int64_t dropped = 0;
+};
+
+namespace {
+
+rmx_status fail(rmx_handle* h, rmx_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  if (h)
+    h->last_error = buf;
+  else
+    g_thread_error = buf;
+  return s;
+}
+
+void clear_error(rmx_handle* h) {
+  if (h)
+    h->last_error.clear();
+  else
+    g_thread_error.clear();
+}
+
+// A device pointer is acceptable when it is 16-byte aligned and the bytes
+// [p, p + bytes) lie inside one allocation of `device`.
+rmx_status check_dev(rmx_handle* h, const void* p, size_t bytes, int device, const char* name) {
+  if (!p) return fail(h, RMX_ERR_INVALID_ARG, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % 16) return fail(h, RMX_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(h, RMX_ERR_INVALID_ARG, "%s is not a HIP allocation", name);
+  }
+  if (attr.type != hipMemoryTypeDevice)
+    return fail(h, RMX_ERR_INVALID_ARG, "%s is not device memory", name);
+  if (attr.device != device)
+    return fail(h, RMX_ERR_INVALID_ARG, "%s lives on device %d, not %d", name, attr.device, device);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(h, RMX_ERR_INVALID_ARG, "%s: allocation range unknown", name);
+  }
+  const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+  if (q + bytes > b + size)
+    return fail(h, RMX_ERR_INVALID_ARG, "%s: %zu bytes needed but only %zu remain in its allocation",
+                name, bytes, size_t(b + size - q));
+  return RMX_OK;
+}
+
+rmx_status check_dev_opt(rmx_handle* h, const void* p, size_t bytes, int device, const char* name) {
+  return p ? check_dev(h, p, bytes, device, name) : RMX_OK;
+}
+
+rmx_status check_device_arch(rmx_handle* h, int* device_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(h, RMX_ERR_UNSUPPORTED, "no HIP device");
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(h, RMX_ERR_HIP, "hipGetDeviceProperties failed");
+  }
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(h, RMX_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev,
+                prop.gcnArchName);
+  *device_out = dev;
+  return RMX_OK;
+}
+
+rmx_status validate_config(const rmx_config* c) {
+  if (!c) return fail(nullptr, RMX_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->T < 1 || c->D < 1 || c->k < 1 || c->L < 1)
+    return fail(nullptr, RMX_ERR_INVALID_ARG, "T, D, k, L must all be >= 1 (got %d, %d, %d, %d)", c->T,
+                c->D, c->k, c->L);
+  if (c->D % c->T)
+    return fail(nullptr, RMX_ERR_INVALID_ARG, "D=%d is not divisible by H=T=%d", c->D, c->T);
+  if (c->dtype != RMX_FP32 && c->dtype != RMX_BF16)
+    return fail(nullptr, RMX_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
+  if (!(c->ln_eps > 0.f)) return fail(nullptr, RMX_ERR_INVALID_ARG, "ln_eps must be > 0");
+  if (c->max_batch < 0) return fail(nullptr, RMX_ERR_INVALID_ARG, "max_batch < 0");
+  if (c->moe_experts < 0 || c->moe_hidden < 0)
+    return fail(nullptr, RMX_ERR_INVALID_ARG, "moe_experts, moe_hidden must be >= 0");
+  if (c->moe_experts > 0)
+    return fail(nullptr, RMX_ERR_UNSUPPORTED, "the Sparse-MoE PFFN is not built in this library version");
+  const bool vec = rows_vectorized(c->T, c->D);
+  if (c->dtype == RMX_BF16 && !vec)
+    return fail(nullptr, RMX_ERR_UNSUPPORTED, "bf16 needs D %% 8 == 0 and (D/T) %% 8 == 0");
+  if (c->D > (vec ? ROWS_MAX_D : ROWS_MAX_D_SCALAR))
+    return fail(nullptr, RMX_ERR_UNSUPPORTED, "D=%d exceeds the row kernel limit %d", c->D,
+                vec ? ROWS_MAX_D : ROWS_MAX_D_SCALAR);
+  if (rows_lds_bytes(c->dtype, c->T, c->D) > ROWS_MAX_LDS)
+    return fail(nullptr, RMX_ERR_UNSUPPORTED, "one sample (T*D*%d = %zu bytes) exceeds %zu bytes of LDS",
+                dtype_size(c->dtype), rows_lds_bytes(c->dtype, c->T, c->D), ROWS_MAX_LDS);
+  const int64_t kD = int64_t(c->k) * c->D;
+  const int64_t rows = int64_t(c->T) * c->max_batch;
+  if (kD > (int64_t(1) << 30) || c->max_batch > (int64_t(1) << 30) || rows * kD > (int64_t(1) << 46))
+    return fail(nullptr, RMX_ERR_UNSUPPORTED, "sizes too large");
+  return RMX_OK;
+}
+
+// ---- kernel timing
+void prof_begin(rmx_handle* h, hipStream_t s, ProfPair* pp, int kind) {
+  pp->kind = -1;
+  if (!h->prof) return;
+  if (h->pending.size() >= PROF_CAP) {
+    ++h->dropped;
+    return;
+  }
+  auto take = [&]() {
+    hipEvent_t e = nullptr;
+    if (!h->free_events.empty()) {
+      e = h->free_events.back();
+      h->free_events.pop_back();
+    } else if (hipEventCreate(&e) != hipSuccess) {
+      (void)hipGetLastError();
+      e = nullptr;
+    }
+    return e;
+  };
+  pp->start = take();
+  pp->stop = take();
+  if (!pp->start || !pp->stop) {
+    if (pp->start) h->free_events.push_back(pp->start);
+    if (pp->stop) h->free_events.push_back(pp->stop);
+    ++h->dropped;
+    return;
+  }
+  pp->kind = kind;
+  (void)hipEventRecord(pp->start, s);
+}
+
+void prof_end(rmx_handle* h, hipStream_t s, ProfPair* pp) {
+  if (pp->kind < 0) return;
+  (void)hipEventRecord(pp->stop, s);
+  h->pending.push_back(*pp);
+}
+
+hipError_t run_rows(rmx_handle* h, hipStream_t s, int mode, const RowsArgs& a) {
+  ProfPair pp;
+  prof_begin(h, s, &pp, mode == ROWS_FINAL ? RMX_KERNEL_POOL : RMX_KERNEL_ROWS);
+  hipError_t e = launch_rows(h->cfg.dtype, mode, a, s);
+  prof_end(h, s, &pp);
+  return e;
+}
+
+hipError_t run_gemm(rmx_handle* h, hipStream_t s, int epi, const GemmArgs& a) {
+  ProfPair pp;
+  prof_begin(h, s, &pp, epi == EPI_GELU ? RMX_KERNEL_GEMM1 : RMX_KERNEL_GEMM2);
+  hipError_t e = launch_gemm(h->cfg.dtype, epi, a, s);
+  prof_end(h, s, &pp);
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t rmx_abi_version(void) { return RMX_ABI_VERSION; }
+
+const char* rmx_status_string(rmx_status s) {
+  switch (s) {
+    case RMX_OK: return "ok";
+    case RMX_ERR_INVALID_ARG: return "invalid argument";
+    case RMX_ERR_UNSUPPORTED: return "unsupported";
+    case RMX_ERR_OUT_OF_MEMORY: return "out of memory";
+    case RMX_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* rmx_last_error(const rmx_handle* h) { return h ? h->last_error.c_str() : g_thread_error.c_str(); }
+
+const char* rmx_kernel_name(int32_t kind) {
+  static const char* names[RMX_KERNEL_COUNT] = {"rows_ln2_mix_ln1", "gemm1_gelu", "gemm2_residual",
+                                                "rows_ln2_pool",   "moe_gate",   "moe_ffn1",
+                                                "moe_ffn2",        "moe_combine"};
+  return (kind >= 0 && kind < RMX_KERNEL_COUNT) ? names[kind] : "unknown";
+}
+
+rmx_status rmx_create(const rmx_config* cfg, rmx_handle** out_handle) {
+  clear_error(nullptr);
+  if (!out_handle) return fail(nullptr, RMX_ERR_INVALID_ARG, "out_handle is NULL");
+  *out_handle = nullptr;
+  rmx_status st = validate_config(cfg);
+  if (st != RMX_OK) return st;
+  int dev = -1;
+  if ((st = check_device_arch(nullptr, &dev)) != RMX_OK) return st;
+  hipError_t e;
+  if ((e = rows_init()) != hipSuccess || (e = gemm_init()) != hipSuccess)
+    return fail(nullptr, RMX_ERR_HIP, "kernel set-up failed: %s", hipGetErrorString(e));
+
+  rmx_handle* h = new (std::nothrow) rmx_handle();
+  if (!h) return fail(nullptr, RMX_ERR_OUT_OF_MEMORY, "host allocation failed");
+  h->cfg = *cfg;
+  h->device = dev;
+  const size_t esz = dtype_size(cfg->dtype);
+  const size_t rows = size_t(cfg->T) * size_t(cfg->max_batch);
+  const size_t nS = rows * cfg->D, nH = rows * size_t(cfg->k) * cfg->D;
+  if (rows > 0) {
+    if (hipMalloc(&h->S, nS * esz) != hipSuccess || hipMalloc(&h->H, nH * esz) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void**>(&h->Y), nS * sizeof(float)) != hipSuccess) {
+      (void)hipGetLastError();
+      rmx_destroy(h);
+      return fail(nullptr, RMX_ERR_OUT_OF_MEMORY, "workspace of %zu bytes could not be allocated",
+                  nS * esz + nH * esz + nS * 4);
+    }
+  }
+  *out_handle = h;
+  return RMX_OK;
+}
+
+rmx_status rmx_destroy(rmx_handle* h) {
+  if (!h) return RMX_OK;
+  if (h->S || h->H || h->Y || !h->pending.empty() || !h->free_events.empty()) {
+    (void)hipDeviceSynchronize();
+  }
+  if (h->S) (void)hipFree(h->S);
+  if (h->H) (void)hipFree(h->H);
+  if (h->Y) (void)hipFree(h->Y);
+  for (auto& p : h->pending) {
+    (void)hipEventDestroy(p.start);
+    (void)hipEventDestroy(p.stop);
+  }
+  for (auto e : h->free_events) (void)hipEventDestroy(e);
+  delete h;
+  return RMX_OK;
+}
+
+rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w,
+                                int32_t L, int32_t k, float* out, void* xl_out, float* gate_out,
+                                void* stream) {
+  if (!h) return fail(nullptr, RMX_ERR_INVALID_ARG, "handle is NULL");
+  clear_error(h);
+  const rmx_config& c = h->cfg;
+  if (!w) return fail(h, RMX_ERR_INVALID_ARG, "weights is NULL");
+  if (L != c.L) return fail(h, RMX_ERR_INVALID_ARG, "L=%d but the handle was created with L=%d", L, c.L);
+  if (k != c.k) return fail(h, RMX_ERR_INVALID_ARG, "k=%d but the handle was created with k=%d", k, c.k);
+  if (B < 0 || B > c.max_batch)
+    return fail(h, RMX_ERR_INVALID_ARG, "B=%lld outside [0, max_batch=%lld]", (long long)B,
+                (long long)c.max_batch);
+  if (gate_out) return fail(h, RMX_ERR_INVALID_ARG, "gate_out must be NULL for a dense handle");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
+    (void)hipGetLastError();
+    return fail(h, RMX_ERR_INVALID_ARG, "current device %d is not the handle's device %d", dev, h->device);
+  }
+  if (B == 0) return RMX_OK;
+
+  const size_t esz = dtype_size(c.dtype);
+  const size_t T = c.T, D = c.D, kD = size_t(c.k) * c.D, Ls = c.L;
+  rmx_status st;
+  if ((st = check_dev(h, X, size_t(B) * T * D * esz, dev, "X")) != RMX_OK) return st;
+  if ((st = check_dev(h, out, size_t(B) * D * 4, dev, "out")) != RMX_OK) return st;
+  if ((st = check_dev_opt(h, xl_out, size_t(B) * T * D * esz, dev, "xl_out")) != RMX_OK) return st;
+  if ((st = check_dev(h, w->W1, Ls * T * D * kD * esz, dev, "W1")) != RMX_OK) return st;
+  if ((st = check_dev(h, w->W2, Ls * T * kD * D * esz, dev, "W2")) != RMX_OK) return st;
+  if ((st = check_dev_opt(h, w->b1, Ls * T * kD * esz, dev, "b1")) != RMX_OK) return st;
+  if ((st = check_dev_opt(h, w->b2, Ls * T * D * esz, dev, "b2")) != RMX_OK) return st;
+  if ((st = check_dev(h, w->ln1_g, Ls * D * esz, dev, "ln1_g")) != RMX_OK) return st;
+  if ((st = check_dev(h, w->ln1_b, Ls * D * esz, dev, "ln1_b")) != RMX_OK) return st;
+  if ((st = check_dev(h, w->ln2_g, Ls * D * esz, dev, "ln2_g")) != RMX_OK) return st;
+  if ((st = check_dev(h, w->ln2_b, Ls * D * esz, dev, "ln2_b")) != RMX_OK) return st;
+  if (w->Wg || w->We1 || w->We2 || w->be1 || w->be2)
+    return fail(h, RMX_ERR_INVALID_ARG, "MoE weights given to a dense handle");
+  // The outputs must not overlap the inputs: out and xl_out are written while X is read.
+  auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+  };
+  if (overlap(out, size_t(B) * D * 4, X, size_t(B) * T * D * esz) ||
+      (xl_out && overlap(xl_out, size_t(B) * T * D * esz, X, size_t(B) * T * D * esz)) ||
+      (xl_out && overlap(xl_out, size_t(B) * T * D * esz, out, size_t(B) * D * 4)))
+    return fail(h, RMX_ERR_INVALID_ARG, "out / xl_out overlap X or each other");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* bytes = nullptr;
+  auto at = [&](const void* base, size_t off_elems) -> const void* {
+    if (!base) return nullptr;
+    bytes = static_cast<const char*>(base);
+    return bytes + off_elems * esz;
+  };
+  hipError_t e = hipSuccess;
+  const int Bi = int(B);
+  for (int n = 0; n < c.L && e == hipSuccess; ++n) {
+    RowsArgs ra{};
+    ra.in = n == 0 ? X : static_cast<const void*>(h->Y);
+    ra.ln2_g = n == 0 ? nullptr : at(w->ln2_g, size_t(n - 1) * D);
+    ra.ln2_b = n == 0 ? nullptr : at(w->ln2_b, size_t(n - 1) * D);
+    ra.ln1_g = at(w->ln1_g, size_t(n) * D);
+    ra.ln1_b = at(w->ln1_b, size_t(n) * D);
+    ra.S = h->S;
+    ra.B = Bi;
+    ra.T = c.T;
+    ra.D = c.D;
+    ra.eps = c.ln_eps;
+    e = run_rows(h, s, n == 0 ? ROWS_FIRST : ROWS_MID, ra);
+    if (e != hipSuccess) break;
+
+    GemmArgs g1{};
+    g1.A = h->S;
+    g1.W = at(w->W1, size_t(n) * T * D * kD);
+    g1.bias = at(w->b1, size_t(n) * T * kD);
+    g1.C = h->H;
+    g1.G = c.T;
+    g1.M = Bi;
+    g1.N = int(kD);
+    g1.K = c.D;
+    e = run_gemm(h, s, EPI_GELU, g1);
+    if (e != hipSuccess) break;
+
+    GemmArgs g2{};
+    g2.A = h->H;
+    g2.W = at(w->W2, size_t(n) * T * kD * D);
+    g2.bias = at(w->b2, size_t(n) * T * D);
+    g2.R = h->S;
+    g2.C = h->Y;
+    g2.G = c.T;
+    g2.M = Bi;
+    g2.N = c.D;
+    g2.K = int(kD);
+    e = run_gemm(h, s, EPI_RESID, g2);
+  }
+  if (e == hipSuccess) {
+    RowsArgs ra{};
+    ra.in = h->Y;
+    ra.ln2_g = at(w->ln2_g, size_t(c.L - 1) * D);
+    ra.ln2_b = at(w->ln2_b, size_t(c.L - 1) * D);
+    ra.pool = out;
+    ra.xl = xl_out;
+    ra.B = Bi;
+    ra.T = c.T;
+    ra.D = c.D;
+    ra.eps = c.ln_eps;
+    e = run_rows(h, s, ROWS_FINAL, ra);
+  }
+  if (e != hipSuccess) return fail(h, RMX_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return RMX_OK;
+}
+
+rmx_status rmx_block_forward(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w, int32_t L,
+                             int32_t k, float* out, void* stream) {
+  return rmx_block_forward_ex(h, X, B, w, L, k, out, nullptr, nullptr, stream);
+}
+
+rmx_status rmx_token_mix(const void* X, void* Y, int64_t B, int32_t T, int32_t D, int32_t dtype,
+                         void* stream) {
+  clear_error(nullptr);
+  if (T < 1 || D < 1 || B < 0) return fail(nullptr, RMX_ERR_INVALID_ARG, "T, D must be >= 1 and B >= 0");
+  if (D % T) return fail(nullptr, RMX_ERR_INVALID_ARG, "D=%d is not divisible by H=T=%d", D, T);
+  if (dtype != RMX_FP32 && dtype != RMX_BF16) return fail(nullptr, RMX_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (B == 0) return RMX_OK;
+  int dev = -1;
+  rmx_status st = check_device_arch(nullptr, &dev);
+  if (st != RMX_OK) return st;
+  const size_t bytes = size_t(B) * T * D * dtype_size(dtype);
+  if ((st = check_dev(nullptr, X, bytes, dev, "X")) != RMX_OK) return st;
+  if ((st = check_dev(nullptr, Y, bytes, dev, "Y")) != RMX_OK) return st;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(X), y = reinterpret_cast<uintptr_t>(Y);
+  if (x < y + bytes && y < x + bytes) return fail(nullptr, RMX_ERR_INVALID_ARG, "X and Y overlap");
+  hipError_t e = launch_token_mix(dtype, X, Y, B, T, D, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, RMX_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return RMX_OK;
+}
+
+rmx_status rmx_profile_enable(rmx_handle* h, int32_t enable) {
+  if (!h) return fail(nullptr, RMX_ERR_INVALID_ARG, "handle is NULL");
+  h->prof = enable != 0;
+  return RMX_OK;
+}
+
+rmx_status rmx_profile_read(rmx_handle* h, double* total_ms, int64_t* launches, int64_t* dropped) {
+  if (!h) return fail(nullptr, RMX_ERR_INVALID_ARG, "handle is NULL");
+  for (auto& p : h->pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.stop) == hipSuccess && hipEventElapsedTime(&ms, p.start, p.stop) == hipSuccess) {
+      h->total_ms[p.kind] += ms;
+      h->launches[p.kind] += 1;
+    } else {
+      (void)hipGetLastError();
+      ++h->dropped;
+    }
+    h->free_events.push_back(p.start);
+    h->free_events.push_back(p.stop);
+  }
+  h->pending.clear();
+  for (int i = 0; i < RMX_KERNEL_COUNT; ++i) {
+    if (total_ms) total_ms[i] = h->total_ms[i];
+    if (launches) launches[i] = h->launches[i];
+  }
+  if (dropped) *dropped = h->dropped;
+  return RMX_OK;
+}
+
+rmx_status rmx_profile_reset(rmx_handle* h) {
+  if (!h) return fail(nullptr, RMX_ERR_INVALID_ARG, "handle is NULL");
+  double t[RMX_KERNEL_COUNT];
+  int64_t n[RMX_KERNEL_COUNT];
+  int64_t d;
+  rmx_profile_read(h, t, n, &d);  // retire pending events
+  for (int i = 0; i < RMX_KERNEL_COUNT; ++i) {
+    h->total_ms[i] = 0.0;
+    h->launches[i] = 0;
+  }
+  h->dropped = 0;
+  return RMX_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,296 @@
+// Row kernel of the RankMixer block: everything between two grouped GEMMs.
+//
+// One workgroup owns one sample b (its T x D token matrix).  Depending on the mode it
+//   - reads the previous block's pre-LN2 rows Y[t, b, :] (fp32) and applies LN2, or
+//     reads the input X0[b, t, :] as is (first block);
+//   - keeps the resulting X[b] in LDS, then for every output row h forms
+//     R[h, c] = X[h, c] + X[t, h*q + r] (c = t*q + r: Token Mixing with H = T folded into
+//     the LDS read address, residual added on the fly) and applies LN1, writing
+//     S[h, b, :] token-major for the grouped GEMMs;
+//   - or, after the last block, mean-pools the LN2 output over tokens.
+// RankMixer paper translation, section 3.1 eq (1), 3.3.1 eq (3)-(5);
+// "RankMixer 详解（1）", sections 3.1 (index map), 3.3 (LayerNorm), 5.1 (pool).
+//
+// LayerNorm statistics are two-pass (mean, then mean of squared deviations) in fp32
+// over values held in registers, reduced across the 64 lanes of one wavefront.
+#include "rmx_device.h"
+#include "rmx_internal.h"
+
+namespace rmx {
+
+namespace {
+
+template <int W, typename T>
+__device__ __forceinline__ void loadw(const T* p, float* v) {
+  if constexpr (W == 8) {
+    load8(p, v);
+  } else {
+    v[0] = load1(p);
+  }
+}
+template <int W, typename T>
+__device__ __forceinline__ void storew(T* p, const float* v) {
+  if constexpr (W == 8) {
+    store8(p, v);
+  } else {
+    store1(p, v[0]);
+  }
+}
+
+// LayerNorm of one row held as v[MAXC][W] by the 64 lanes of a wave (chunk c = lane + 64 i),
+// in place: v = gamma * (v - mu) / sqrt(var + eps) + beta.
+template <int W, int MAXC, typename T>
+__device__ __forceinline__ void wave_layernorm(float (&v)[MAXC][W], int lane, int nchunks, int D,
+                                               const T* gamma, const T* beta, float eps) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nchunks) {
+#pragma unroll
+      for (int e = 0; e < W; ++e) s += v[i][e];
+    }
+  }
+  const float mu = wave_sum(s) / float(D);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nchunks) {
+#pragma unroll
+      for (int e = 0; e < W; ++e) {
+        const float d = v[i][e] - mu;
+        ss += d * d;
+      }
+    }
+  }
+  const float var = wave_sum(ss) / float(D);
+  const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nchunks) {
+      float g[W], bt[W];
+      loadw<W>(gamma + c * W, g);
+      loadw<W>(beta + c * W, bt);
+#pragma unroll
+      for (int e = 0; e < W; ++e) v[i][e] = g[e] * ((v[i][e] - mu) * rstd) + bt[e];
+    }
+  }
+}
+
+template <typename T, int W, int MODE>
+__global__ __launch_bounds__(512) void rows_kernel(RowsArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  constexpr int MAXC = (W == 8) ? ROWS_MAX_D / (64 * 8) : ROWS_MAX_D_SCALAR / 64;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int Tn = a.T, D = a.D, B = a.B;
+  const int q = D / Tn;
+  const int nchunks = D / W;
+  T* xs = reinterpret_cast<T*>(smem_raw);  // [T][D] rows of sample b (FIRST / MID)
+
+  float pacc[MAXC][W];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i)
+#pragma unroll
+    for (int e = 0; e < W; ++e) pacc[i][e] = 0.f;
+
+  // Phase A: the block input rows X[b, t, :] for t = wave, wave + nw, ...
+  for (int t = wave; t < Tn; t += nw) {
+    float v[MAXC][W];
+    if constexpr (MODE == ROWS_FIRST) {
+      const T* src = static_cast<const T*>(a.in) + (size_t(b) * Tn + t) * D;
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nchunks) {
+          loadw<W>(src + c * W, v[i]);
+          storew<W>(xs + t * D + c * W, v[i]);
+        }
+      }
+    } else {
+      const float* src = static_cast<const float*>(a.in) + (size_t(t) * B + b) * D;
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nchunks) loadw<W>(src + c * W, v[i]);
+      }
+      wave_layernorm<W, MAXC>(v, lane, nchunks, D, static_cast<const T*>(a.ln2_g),
+                              static_cast<const T*>(a.ln2_b), a.eps);
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nchunks) {
+          if constexpr (MODE == ROWS_MID) {
+            storew<W>(xs + t * D + c * W, v[i]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < W; ++e) pacc[i][e] += v[i][e];
+            if (a.xl) storew<W>(static_cast<T*>(a.xl) + (size_t(b) * Tn + t) * D + c * W, v[i]);
+          }
+        }
+      }
+    }
+  }
+
+  if constexpr (MODE == ROWS_FINAL) {
+    // Mean pool: per-wave partial sums meet in LDS, then sum over waves in wave order.
+    float* red = reinterpret_cast<float*>(smem_raw);  // [nw][D]
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunks)
+#pragma unroll
+        for (int e = 0; e < W; ++e) red[wave * D + c * W + e] = pacc[i][e];
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+      float s = 0.f;
+      for (int w = 0; w < nw; ++w) s += red[w * D + d];
+      a.pool[size_t(b) * D + d] = s / float(Tn);
+    }
+    return;
+  }
+
+  __syncthreads();
+  // Phase B: output rows h = wave, wave + nw, ...:  S[h] = LN1(X[h] + mix(X)[h]).
+  for (int h = wave; h < Tn; h += nw) {
+    float r[MAXC][W];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunks) {
+        const int col = c * W;
+        int t;
+        const int sc = mix_source(h, col, q, &t);  // W consecutive columns stay in one head
+        float own[W], mixed[W];
+        loadw<W>(xs + h * D + col, own);
+        loadw<W>(xs + t * D + sc, mixed);
+#pragma unroll
+        for (int e = 0; e < W; ++e) r[i][e] = own[e] + mixed[e];
+      }
+    }
+    wave_layernorm<W, MAXC>(r, lane, nchunks, D, static_cast<const T*>(a.ln1_g),
+                            static_cast<const T*>(a.ln1_b), a.eps);
+    T* dst = static_cast<T*>(a.S) + (size_t(h) * B + b) * D;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunks) storew<W>(dst + c * W, r[i]);
+    }
+  }
+}
+
+// Standalone Token Mixing: Y[b, h, c] = X[b, t, mix_source(h, c)], W columns per thread.
+template <typename T, int W>
+__global__ __launch_bounds__(256) void token_mix_kernel(const T* __restrict__ X, T* __restrict__ Y,
+                                                        int64_t total, int Tn, int D) {
+  const int q = D / Tn;
+  const int per_row = D / W;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int c = int(i % per_row) * W;
+    const int64_t bh = i / per_row;
+    const int h = int(bh % Tn);
+    const int64_t b = bh / Tn;
+    int t;
+    const int sc = mix_source(h, c, q, &t);
+    const T* src = X + (b * Tn + t) * D + sc;
+    T* dst = Y + bh * D + c;
+    if constexpr (W == 8) {
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      if constexpr (sizeof(T) == 4) reinterpret_cast<uint4*>(dst)[1] = reinterpret_cast<const uint4*>(src)[1];
+    } else {
+      *dst = *src;
+    }
+  }
+}
+
+template <typename T, int W>
+hipError_t launch_rows_t(int mode, const RowsArgs& a, hipStream_t stream) {
+  int nw = a.T < 8 ? a.T : 8;
+  size_t lds;
+  if (mode == ROWS_FINAL) {
+    while (nw > 1 && size_t(nw) * a.D * 4 > 64 * 1024) --nw;
+    lds = size_t(nw) * a.D * 4;
+  } else {
+    lds = size_t(a.T) * a.D * sizeof(T);
+  }
+  dim3 grid(a.B), block(64 * nw);
+  switch (mode) {
+    case ROWS_FIRST:
+      hipLaunchKernelGGL((rows_kernel<T, W, ROWS_FIRST>), grid, block, lds, stream, a);
+      break;
+    case ROWS_MID:
+      hipLaunchKernelGGL((rows_kernel<T, W, ROWS_MID>), grid, block, lds, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL((rows_kernel<T, W, ROWS_FINAL>), grid, block, lds, stream, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int W>
+hipError_t set_rows_lds_limit() {
+  const int bytes = int(ROWS_MAX_LDS);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_kernel<T, W, ROWS_FIRST>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_kernel<T, W, ROWS_MID>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_kernel<T, W, ROWS_FINAL>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+}  // namespace
+
+bool rows_vectorized(int T, int D) { return D % 8 == 0 && (D / T) % 8 == 0; }
+
+size_t rows_lds_bytes(int dtype, int T, int D) { return size_t(T) * D * dtype_size(dtype); }
+
+hipError_t rows_init() {
+  hipError_t e;
+  if ((e = set_rows_lds_limit<float, 8>()) != hipSuccess) return e;
+  if ((e = set_rows_lds_limit<float, 1>()) != hipSuccess) return e;
+  if ((e = set_rows_lds_limit<bf16_t, 8>()) != hipSuccess) return e;
+  return set_rows_lds_limit<bf16_t, 1>();
+}
+
+hipError_t launch_rows(int dtype, int mode, const RowsArgs& a, hipStream_t stream) {
+  const bool vec = rows_vectorized(a.T, a.D);
+  if (dtype == DT_BF16)
+    return vec ? launch_rows_t<bf16_t, 8>(mode, a, stream) : launch_rows_t<bf16_t, 1>(mode, a, stream);
+  return vec ? launch_rows_t<float, 8>(mode, a, stream) : launch_rows_t<float, 1>(mode, a, stream);
+}
+
+hipError_t launch_token_mix(int dtype, const void* X, void* Y, int64_t B, int T, int D,
+                            hipStream_t stream) {
+  const bool vec = rows_vectorized(T, D);
+  const int W = vec ? 8 : 1;
+  const int64_t total = B * T * (D / W);
+  const int64_t want = (total + 255) / 256;
+  const int blocks = int(want < 65536 ? want : 65536);
+  if (dtype == DT_BF16) {
+    if (vec)
+      hipLaunchKernelGGL((token_mix_kernel<bf16_t, 8>), dim3(blocks), dim3(256), 0, stream,
+                         static_cast<const bf16_t*>(X), static_cast<bf16_t*>(Y), total, T, D);
+    else
+      hipLaunchKernelGGL((token_mix_kernel<bf16_t, 1>), dim3(blocks), dim3(256), 0, stream,
+                         static_cast<const bf16_t*>(X), static_cast<bf16_t*>(Y), total, T, D);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((token_mix_kernel<float, 8>), dim3(blocks), dim3(256), 0, stream,
+                         static_cast<const float*>(X), static_cast<float*>(Y), total, T, D);
+    else
+      hipLaunchKernelGGL((token_mix_kernel<float, 1>), dim3(blocks), dim3(256), 0, stream,
+                         static_cast<const float*>(X), static_cast<float*>(Y), total, T, D);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rmx

@@ -1,0 +1,215 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on seeded inputs.
+
+Small shapes are compared element by element in full; the full-size workloads
+(RankMixer-100M at B=512, RankMixer-1B at B=2048, the serving sweep) run on the GPU at
+their real size, in the launch configuration the benchmark times, and are compared on
+sampled samples that the oracle computes one by one (samples are independent: mixing,
+LayerNorm and the per-token FFN never cross samples).
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from rankmixer_block_forward_amd import synth
+from tests.parity import check, run_gpu, run_oracle, sample_rows, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _rmx():
+    import rankmixer_block_forward_amd as rmx
+    return rmx
+
+
+# ------------------------------------------------------------------ Token Mixing
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("B,T,D", [(3, 4, 8), (7, 4, 12), (5, 16, 768), (2, 32, 1536), (4, 2, 6), (1, 1, 16)])
+def test_token_mix_bit_exact(dtype, B, T, D):
+    rmx = _rmx()
+    cfg = synth.Config("mix", B=B, T=T, D=D, k=1, L=1, dtype=dtype)
+    X = synth.make_x(cfg, seed=B * 131 + D)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    Xd = torch.from_numpy(X).cuda().to(tdt)
+    Y = rmx.token_mix(Xd)
+    Z = rmx.token_mix(Y)
+    torch.cuda.synchronize()
+    want = oracle.token_mix(X.astype(np.float64))
+    assert np.array_equal(to_np(Y).astype(np.float64), want)
+    assert torch.equal(Z, Xd)  # H = T: the permutation is its own inverse
+
+
+# ------------------------------------------------------------------------ fp32
+
+def test_tiny_workload_fp32():
+    cfg = synth.TINY
+    inp = synth.make_inputs(cfg, seed=0)
+    o, xl = run_gpu(cfg, inp)
+    o_ref, xl_ref = run_oracle(cfg, inp)
+    check(cfg, o, xl, o_ref, xl_ref, "tiny")
+
+
+@pytest.mark.parametrize("B,T,D,k,L", [(37, 4, 64, 2, 2), (5, 3, 12, 3, 1), (130, 8, 128, 4, 2),
+                                       (1, 2, 6, 1, 3), (65, 4, 8, 2, 1)])
+def test_fp32_shapes(B, T, D, k, L):
+    cfg = synth.Config("fp32", B=B, T=T, D=D, k=k, L=L, dtype="fp32", bias_std=0.05)
+    inp = synth.make_inputs(cfg, seed=B + D)
+    o, xl = run_gpu(cfg, inp)
+    o_ref, xl_ref = run_oracle(cfg, inp)
+    check(cfg, o, xl, o_ref, xl_ref, f"fp32 {B}x{T}x{D} k{k} L{L}")
+
+
+def test_zero_token_rows_fp32():
+    cfg = synth.TINY.with_(B=16, zero_frac=0.25, bias_std=0.1, ln_init="jitter")
+    inp = synth.make_inputs(cfg, seed=3)
+    o, xl = run_gpu(cfg, inp)
+    o_ref, xl_ref = run_oracle(cfg, inp)
+    check(cfg, o, xl, o_ref, xl_ref, "fp32 zero rows")
+
+
+# ------------------------------------------------------------------------ bf16
+
+@pytest.mark.parametrize("B,T,D,k,L", [
+    (300, 4, 256, 4, 2),   # MFMA path: 2 M tiles (ragged), 4 N tiles in GEMM1
+    (77, 5, 320, 2, 1),    # MFMA path, ragged N tiles (640 = 2.5 x 256, 320 = 1.25 x 256)
+    (50, 4, 96, 2, 2),     # K = 96 not a multiple of 64: generic kernel in bf16
+    (1, 16, 768, 4, 2),    # one sample at the 100M width
+    (513, 16, 768, 4, 1),  # one row past a tile boundary
+])
+def test_bf16_shapes(B, T, D, k, L):
+    cfg = synth.Config("bf16", B=B, T=T, D=D, k=k, L=L, dtype="bf16", bias_std=0.02)
+    inp = synth.make_inputs(cfg, seed=B + D + L)
+    o, xl = run_gpu(cfg, inp)
+    rows = sample_rows(B, 64)
+    o_ref, xl_ref = run_oracle(cfg, inp, rows)
+    check(cfg, o[rows], xl[rows], o_ref, xl_ref, f"bf16 {B}x{T}x{D} k{k} L{L}")
+
+
+def test_bf16_zero_rows_and_biases():
+    cfg = synth.Config("bf16z", B=200, T=8, D=128, k=4, L=2, dtype="bf16", bias_std=0.05, zero_frac=0.3)
+    inp = synth.make_inputs(cfg, seed=9)
+    o, xl = run_gpu(cfg, inp)
+    o_ref, xl_ref = run_oracle(cfg, inp)
+    check(cfg, o, xl, o_ref, xl_ref, "bf16 zero rows")
+
+
+def test_bf16_deterministic():
+    cfg = synth.Config("det", B=300, T=4, D=256, k=4, L=2, dtype="bf16")
+    inp = synth.make_inputs(cfg, seed=1)
+    o1, x1 = run_gpu(cfg, inp)
+    o2, x2 = run_gpu(cfg, inp)
+    assert np.array_equal(o1, o2) and np.array_equal(x1, x2)
+
+
+# ------------------------------------------------------- full-size workloads
+
+def test_rankmixer_100m_full_size():
+    cfg = synth.M100
+    inp = synth.make_inputs(cfg, seed=0)
+    o, xl = run_gpu(cfg, inp)
+    rows = sample_rows(cfg.B, 24)
+    o_ref, xl_ref = run_oracle(cfg, inp, rows)
+    check(cfg, o[rows], xl[rows], o_ref, xl_ref, "100M B=512")
+
+
+def test_rankmixer_1b_full_size():
+    cfg = synth.B1
+    inp = synth.make_inputs(cfg, seed=0)
+    o, xl = run_gpu(cfg, inp)
+    assert np.isfinite(o).all()
+    rows = sample_rows(cfg.B, 6)
+    o_ref, xl_ref = run_oracle(cfg, inp, rows)
+    check(cfg, o[rows], xl[rows], o_ref, xl_ref, "1B B=2048")
+
+
+@pytest.mark.parametrize("B", [64, 16384])
+def test_rankmixer_1b_sweep_sizes(B):
+    cfg = synth.SWEEP.with_(B=B)
+    inp = synth.make_inputs(cfg, seed=0)
+    o, xl = run_gpu(cfg, inp, with_xl=(B <= 4096))
+    rows = sample_rows(B, 4)
+    o_ref, xl_ref = run_oracle(cfg, inp, rows)
+    check(cfg, o[rows], None if xl is None else xl[rows], o_ref, xl_ref, f"1B sweep B={B}")
+
+
+# ------------------------------------------------------------ boundary cases
+
+def test_batch_zero_and_smaller_batches_reuse_handle():
+    rmx = _rmx()
+    cfg = synth.Config("reuse", B=40, T=4, D=64, k=2, L=2, dtype="bf16", bias_std=0.02)
+    inp = synth.make_inputs(cfg, seed=5)
+    X, w = rmx.upload(inp)
+    with rmx.Handle.for_config(cfg, max_batch=64) as h:
+        out0 = torch.empty((0, cfg.D), dtype=torch.float32, device="cuda")
+        h.forward(X[:0], w, out=out0)  # B = 0: nothing enqueued
+        for B in (40, 7, 1):
+            out = h.forward(X[:B].contiguous(), w)
+            torch.cuda.synchronize()
+            o_ref, _ = oracle.forward(inp.X[:B], inp.layers(), cfg.eps)[:2]
+            check(cfg, to_np(out), None, o_ref, None, f"reuse B={B}")
+
+
+def test_errors_enqueue_nothing_and_leave_outputs_untouched():
+    rmx = _rmx()
+    cfg = synth.Config("err", B=8, T=4, D=64, k=2, L=1, dtype="bf16")
+    inp = synth.make_inputs(cfg, seed=6)
+    X, w = rmx.upload(inp)
+    with rmx.Handle.for_config(cfg, max_batch=4) as h:
+        out = torch.full((8, cfg.D), 7.0, device="cuda")
+        with pytest.raises(rmx.RmxError) as e:
+            h.forward(X, w, out=out)  # B = 8 > max_batch = 4
+        assert e.value.status == 1
+        with pytest.raises(rmx.RmxError):
+            h.forward(X[:4].contiguous(), w, out=out[:4], L=2)  # L differs from the handle's
+        with pytest.raises(rmx.RmxError):
+            h.forward(X[:4].contiguous(), w, out=out[:4], k=4)
+        # W1 in an allocation too small for T*D*kD elements (raw hipMalloc of half the bytes)
+        hip = ctypes.CDLL("libamdhip64.so")
+        half = ctypes.c_void_p()
+        assert hip.hipMalloc(ctypes.byref(half), ctypes.c_size_t(w["W1"].numel())) == 0
+        try:
+            lib = rmx.load_library()
+            ws = h._weights(w)
+            ws.W1 = half.value
+            st = lib.rmx_block_forward(h._h, ctypes.c_void_p(X.data_ptr()), 4, ctypes.byref(ws), 1, 2,
+                                       ctypes.c_void_p(out.data_ptr()), None)
+            assert st == 1 and "W1" in lib.rmx_last_error(h._h).decode()
+        finally:
+            hip.hipFree(half)
+        # a host pointer is refused by the library itself
+        lib = rmx.load_library()
+        host = np.zeros(4 * 4 * 64, dtype=np.uint16)
+        ws = h._weights(w)
+        st = lib.rmx_block_forward(h._h, host.ctypes.data_as(ctypes.c_void_p), 4, ctypes.byref(ws), 1, 2,
+                                   ctypes.c_void_p(out.data_ptr()), None)
+        assert st == 1 and "X" in lib.rmx_last_error(h._h).decode()
+        torch.cuda.synchronize()
+        assert torch.all(out == 7.0)
+
+
+def test_profile_counts_launches():
+    rmx = _rmx()
+    cfg = synth.Config("prof", B=64, T=4, D=64, k=2, L=2, dtype="bf16")
+    inp = synth.make_inputs(cfg, seed=7)
+    X, w = rmx.upload(inp)
+    with rmx.Handle.for_config(cfg) as h:
+        h.profile_enable(True)
+        for _ in range(3):
+            h.forward(X, w)
+        p = h.profile_read()
+        assert p["rows_ln2_mix_ln1"]["launches"] == 6
+        assert p["gemm1_gelu"]["launches"] == 6 and p["gemm2_residual"]["launches"] == 6
+        assert p["rows_ln2_pool"]["launches"] == 3 and p["_dropped"] == 0
+        assert all(v["total_ms"] > 0 for k, v in p.items() if k != "_dropped")
+        h.profile_reset()
+        assert h.profile_read() == {"_dropped": 0}
