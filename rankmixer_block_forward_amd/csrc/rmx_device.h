@@ -80,7 +80,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Exact GELU, u * Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), erf from the device math library.
-__device__ __forceinline__ float gelu_exact(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+// GELU(u) = u * Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), the exact (erf) form.
+// erf is evaluated with Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26 (|error| <= 1.5e-7 for all x >= 0, odd extension for x < 0):
+//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),  t = 1 / (1 + p x).
+// 1 + erf(x) is formed directly as 2 - q (x >= 0) or q (x < 0), q = poly(t) exp(-x^2), so
+// the left tail keeps its relative accuracy.  Branch-free: one reciprocal, one exp2.
+__device__ __forceinline__ float gelu_erf(float u) {
+  const float x = u * 0.70710678118654752f;
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float q = poly * __builtin_amdgcn_exp2f(-(ax * ax) * 1.4426950408889634f);
+  const float one_plus_erf = x >= 0.f ? 2.0f - q : q;
+  return 0.5f * u * one_plus_erf;
+}
 
 }  // namespace rmx

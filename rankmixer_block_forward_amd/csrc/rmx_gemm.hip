@@ -6,7 +6,7 @@
 //
 // Two kernels:
 //   gemm_bf16_mfma  bf16 inputs, fp32 accumulation on the CDNA4 matrix cores
-//                   (v_mfma_f32_32x32x16_bf16).  Needs K % 64 == 0 and N % 8 == 0;
+//                   (v_mfma_f32_32x32x16_bf16).  Needs K % 32 == 0 and N % 8 == 0;
 //                   any M (rows past M are zero-filled and never stored).
 //   gemm_generic    any shape, fp32 or bf16 inputs, fp32 FMA on the vector ALUs
 //                   (the fp32 path and shapes the MFMA kernel does not take).
@@ -23,20 +23,41 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // ------------------------------------------------------------------ MFMA kernel
-// Workgroup tile 256 x 256, K step 64, 4 waves in a 2 x 2 grid, each wave 128 x 128 as
-// 4 x 4 blocks of 32 x 32 MFMA accumulators (256 fp32 accumulator registers per lane).
-// Both operands are staged through LDS with the reduction index K contiguous: A rows as
-// they are in memory, W (stored K x N, N contiguous) transposed 8 x 8 in registers on
-// the way in.  LDS rows are padded to 72 elements (144 B) so that the 16-byte fragment
-// reads of 8 or 16 consecutive rows fall in distinct banks.  Two LDS stages: the global
-// loads of step i+1 are in flight while step i runs on the matrix cores.
-constexpr int BM = 256, BN = 256, BK = 64, LDK = 72;
-constexpr int A_STAGE = BM * LDK;  // elements
-constexpr int B_STAGE = BN * LDK;
-constexpr int STAGE = A_STAGE + B_STAGE;
+// Workgroup tile 256 x 256, 4 waves in a 2 x 2 grid, each wave 128 x 128 as 4 x 4 blocks
+// of 32 x 32 MFMA accumulators (256 fp32 accumulator registers per lane, 1 wave per SIMD).
+//
+// Operand staging: K steps of 32 stream through a ring of NS = 4 LDS stages (32 KB each:
+// A 256 x 32 and W 32 x 256, both as they lie in memory).  Global -> LDS copies are
+// buffer loads with the LDS destination (no VGPR round trip, no LDS store instructions);
+// each wave issues 8 of 16 bytes per lane per K step, K step i+4 issued while step i is
+// consumed, so each load has three steps of compute to arrive.  A fragments are plain
+// 16-byte LDS reads; W fragments come out of the [k][n] tile already transposed through
+// the gfx950 transposing LDS read (ds_read_b64_tr_b16, two per 32 x 32 block).
+// 16-byte chunks are XOR-swizzled per row so that both fragment reads are free of bank
+// conflicts for 32- and 64-bank LDS models; the copy-in applies the same swizzle through
+// its per-lane source address.
+//
+// The copies are issued from inline assembly on purpose: the compiler cannot tell which
+// ring stage an LDS-destination load writes, and for a builtin it waits for every such
+// load before any transposing read, which would serialize the ring.  All waits on the
+// copies are therefore explicit: a wave waits for its own copies of the next stage, then
+// the workgroup barrier publishes them.  Buffer loads return zero outside the token's
+// slice, so ragged M and N need no branches; rows >= M and columns >= N of the tile are
+// computed on zeros and never stored.
+constexpr int BM = 256, BN = 256, BK = 32, NS = 4;
+constexpr int A_STAGE_BYTES = BM * BK * 2;                 // 16 KB, rows of 64 B
+constexpr int STAGE_BYTES = A_STAGE_BYTES + BK * BN * 2;   // + 16 KB, rows of 512 B
 constexpr int MFMA_THREADS = 256;
 constexpr int EPI_LD = 132;        // fp32 row stride of the epilogue staging tile
 constexpr int NUM_XCD = 8;         // MI355X: 8 accelerator complex dies, each with its own L2
+
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 // Workgroups are dealt to the XCDs round-robin.  Remap so that each XCD receives a
 // contiguous range of tile indices, and order tiles M-fastest within a token so that the
@@ -47,9 +68,37 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd * base + (xcd < extra ? xcd : extra) + pos;
 }
 
+// Chunk swizzles.  A rows hold 4 chunks (64 B): 16 consecutive rows read one chunk each.
+// W rows hold 32 chunks (512 B): a transposing read takes 4 consecutive k rows x 32 B.
+__device__ __forceinline__ int swz_a(int m) { return ((m >> 1) ^ (m >> 2)) & 3; }
+__device__ __forceinline__ int swz_w(int k) { return (0x0C0A0600u >> (8 * (k & 3))) & 0xff; }
+
+struct Frags {
+  u32x4_t a[4];  // A rows of the 4 row blocks: 8 bf16 each
+  u32x2_t b[8];  // W columns of the 4 column blocks: k 0..3 and 4..7, 4 bf16 each
+};
+
+// MFMA 32x32x16 operand layout: lane l supplies row (l % 32) of A and column (l % 32) of
+// B, each with the 8 consecutive k at 8 (l / 32) of the 16-k sub-step.
+__device__ __forceinline__ void mfma_block(f32x16_t (&acc)[4][4], const Frags& f, int i, int j) {
+  const bf16x8_t a = __builtin_bit_cast(bf16x8_t, f.a[i]);
+  u32x2_t both[2] = {f.b[2 * j], f.b[2 * j + 1]};
+  const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(both);
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i][j], 0, 0, 0);
+}
+
+// One LDS-destination buffer load: 64 lanes x 16 B to lds_dst + 16 * lane.
+__device__ __forceinline__ void copy_to_lds(uint32_t lds_dst, uint32_t voff, __amdgpu_buffer_rsrc_t rsrc,
+                                            int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_dst), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
 template <int EPI>
 __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[NS * STAGE_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_g;  // the generic pointer of a __shared__ array is in LDS
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -61,60 +110,77 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
   const int nt = rem / nMt, mt = rem - nt * nMt;
   const int m0 = mt * BM, n0 = nt * BN;
 
-  const uint16_t* __restrict__ A = static_cast<const uint16_t*>(p.A) + size_t(g) * M * K;
-  const uint16_t* __restrict__ W = static_cast<const uint16_t*>(p.W) + size_t(g) * K * N;
+  // Slices are < 2^31 bytes (checked at launch); an offset equal to the slice size is out
+  // of range whether or not the uniform offset takes part in the range check.
+  const uint32_t bytesA = uint32_t(M) * uint32_t(K) * 2u, bytesW = uint32_t(K) * uint32_t(N) * 2u;
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(p.A) + size_t(g) * M * K), 0, int(bytesA), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(p.W) + size_t(g) * K * N), 0, int(bytesW), 0x00020000);
 
-  // Global -> register mapping.  A: 16 B chunk ac (8 consecutive k) of rows ar + 32 i.
-  // W: rows wk0 .. wk0+7 (k) of the 8 columns starting at wn0 (n).
-  const int ac = tid & 7, ar = tid >> 3;
-  const int wkg = tid & 7, wnc = tid >> 3;
-  const int wn0 = n0 + wnc * 8;
-  const bool wcol_ok = wn0 < N;
-  uint4 ra[8];
-  uint32_t rb[8][4];
-
-  auto gload = [&](int k0) {
+  // Copy-in: wave w fills A rows 64w .. 64w+63 (4 loads of 16 rows) and W k-rows
+  // 8w .. 8w+7 (4 loads of 2 rows) of a stage; lane q lands in LDS chunk q of its load,
+  // so the swizzle is applied by choosing the chunk each lane fetches.
+  uint32_t offA[4], offW[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = m0 + ar + 32 * i;
-      if (row < M)
-        ra[i] = *reinterpret_cast<const uint4*>(A + size_t(row) * K + k0 + ac * 8);
-      else
-        ra[i] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (wcol_ok) v = *reinterpret_cast<const uint4*>(W + size_t(k0 + wkg * 8 + i) * N + wn0);
-      rb[i][0] = v.x; rb[i][1] = v.y; rb[i][2] = v.z; rb[i][3] = v.w;
-    }
-  };
-
-  auto lstore = [&](int stage) {
-    uint16_t* As = smem + stage * STAGE;
-    uint16_t* Bs = As + A_STAGE;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<uint4*>(As + (ar + 32 * i) * LDK + ac * 8) = ra[i];
-    // 8 x 8 transpose: rb[i] holds W[k = i][n = 0..7] as 4 words of 2 bf16; column n of
-    // the result holds k = 0..7, word u = (k = 2u) | (k = 2u + 1) << 16.
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint4 lo, hi;  // columns n = 2w (low halves) and n = 2w + 1 (high halves)
-      lo.x = __builtin_amdgcn_perm(rb[1][w], rb[0][w], 0x05040100u);
-      lo.y = __builtin_amdgcn_perm(rb[3][w], rb[2][w], 0x05040100u);
-      lo.z = __builtin_amdgcn_perm(rb[5][w], rb[4][w], 0x05040100u);
-      lo.w = __builtin_amdgcn_perm(rb[7][w], rb[6][w], 0x05040100u);
-      hi.x = __builtin_amdgcn_perm(rb[1][w], rb[0][w], 0x07060302u);
-      hi.y = __builtin_amdgcn_perm(rb[3][w], rb[2][w], 0x07060302u);
-      hi.z = __builtin_amdgcn_perm(rb[5][w], rb[4][w], 0x07060302u);
-      hi.w = __builtin_amdgcn_perm(rb[7][w], rb[6][w], 0x07060302u);
-      *reinterpret_cast<uint4*>(Bs + (wnc * 8 + 2 * w) * LDK + wkg * 8) = lo;
-      *reinterpret_cast<uint4*>(Bs + (wnc * 8 + 2 * w + 1) * LDK + wkg * 8) = hi;
+  for (int a = 0; a < 4; ++a) {
+    const int r = 64 * wave + 16 * a + (lane >> 2);
+    const int c = (lane & 3) ^ swz_a(r);
+    offA[a] = (m0 + r < M) ? (uint32_t(m0 + r) * uint32_t(K) + uint32_t(c * 8)) * 2u : bytesA;
+    const int kr = 8 * wave + 2 * a + (lane >> 5);
+    const int col = n0 + (((lane & 31) ^ swz_w(kr)) * 8);
+    offW[a] = col < N ? (uint32_t(kr) * uint32_t(N) + uint32_t(col)) * 2u : bytesW;
+  }
+  const int nk = K / BK;
+  // Copy q (0..7) of K step kt into ring stage `stage`; steps past the end reload the last
+  // step (in bounds, never read) so that every K step issues the same number of loads.
+  auto copy = [&](int kt, int stage, int q) {
+    kt = kt < nk ? kt : nk - 1;
+    const uint32_t sbase = lds0 + uint32_t(stage) * STAGE_BYTES;
+    if (q < 4) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(sbase + uint32_t(64 * wave + 16 * q) * 64u);
+      copy_to_lds(dst, offA[q], rA, kt * BK * 2);
+    } else {
+      const uint32_t dst =
+          __builtin_amdgcn_readfirstlane(sbase + A_STAGE_BYTES + uint32_t(8 * wave + 2 * (q - 4)) * 512u);
+      copy_to_lds(dst, offW[q - 4], rW, kt * BK * N * 2);
     }
   };
 
   const int wm = wave >> 1, wn = wave & 1;
+  // Per-lane byte offsets of this wave's fragments within a stage.
+  uint32_t aoff[2][4], boff[4];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = wm * 128 + i * 32 + (lane & 31);
+      const int c = kk * 2 + (lane >> 5);
+      aoff[kk][i] = uint32_t(m * 64 + ((c ^ swz_a(m)) << 4));
+    }
+  {
+    // transposing read: lane l of each 16-lane group addresses k row kb + (l % 16) / 4 and
+    // 4 consecutive columns at 4 (l % 4); it receives column (l % 16) of that 4 x 16 block
+    const int kb = 8 * (lane >> 5) + ((lane & 15) >> 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = wn * 128 + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      boff[j] = uint32_t(A_STAGE_BYTES + kb * 512 + (((n >> 3) ^ swz_w(kb)) << 4) + (n & 7) * 2);
+    }
+  }
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  auto read_frags = [&](Frags& f, const lds_u8* stage_ptr, int kk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const lds_u32x4*>(stage_ptr + aoff[kk][i]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const lds_u8* q = stage_ptr + boff[j] + kk * 16 * 512;
+      f.b[2 * j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)q));
+      f.b[2 * j + 1] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * 512)));
+    }
+  };
+
   f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -123,43 +189,60 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  // Prologue: K steps 0..NS-1 into the NS stages; wait for step 0 (8 loads per step).
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) copy(s, s, q);
+  asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+  Frags f0, f1;
+  read_frags(f0, smem, 0);
 
+  int stage = 0;
   for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < nk) gload((it + 1) * BK);
-    const uint16_t* As = smem + cur * STAGE;
-    const uint16_t* Bs = As + A_STAGE;
+    const lds_u8* sp = smem + stage * STAGE_BYTES;
+    const int nstage = stage + 1 == NS ? 0 : stage + 1;
+    // sub-step 0: MFMAs on f0 while the fragments of sub-step 1 are read
+    read_frags(f1, sp, 1);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      // MFMA 32x32x16 operand layout: lane l supplies row (l % 32) of A and column
-      // (l % 32) of B, each with the 8 consecutive k at 8 * (l / 32) of this 16-k step.
-      const int kc = kk * 16 + (lane >> 5) * 8;
-      bf16x8_t af[4], bfr[4];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 128 + i * 32 + (lane & 31)) * LDK + kc);
+      for (int j = 0; j < 4; ++j) mfma_block(acc, f0, i, j);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * 128 + j * 32 + (lane & 31)) * LDK + kc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
     }
-    if (it + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
+    // Every read of this stage has returned (f1 included) before the barrier; after it,
+    // step it+1 is visible (each wave waited for its own copies: 16 later loads may be
+    // outstanding) and this stage may be refilled with step it+NS.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // sub-step 1: MFMAs on f1, the copies of step it+NS spread between them, and the first
+    // fragments of the next stage read
+    read_frags(f0, smem + nstage * STAGE_BYTES, 0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      mfma_block(acc, f1, q >> 1, (q & 1) * 2);
+      mfma_block(acc, f1, q >> 1, (q & 1) * 2 + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      copy(it + NS, stage, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    stage = nstage;
   }
+  // Drain the trailing copies before the ring memory is reused for the epilogue.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // Epilogue.  Accumulator layout of a 32 x 32 block: lane l, register r holds
   // row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.  Each wave stages 32 rows x 128
   // columns at a time through LDS so that every lane then owns 8 consecutive columns of
   // one row: 16-byte global stores, and coalesced bias / residual loads.
-  float* st = reinterpret_cast<float*>(smem) + wave * 32 * EPI_LD;
+  float* st = reinterpret_cast<float*>(smem_g) + wave * 32 * EPI_LD;
   const int col8 = (lane & 15) * 8;
   const int rsub = lane >> 4;
   const int n = n0 + wn * 128 + col8;
@@ -192,7 +275,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
         const size_t off = (size_t(g) * M + m) * N + n;
         if constexpr (EPI == EPI_GELU) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = gelu_exact(v[e] + bias[e]);
+          for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[e]);
           store8(static_cast<bf16_t*>(p.C) + off, v);
         } else {
           float rr[8];
@@ -260,7 +343,7 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs p) {
       const float bias = p.bias ? load1(static_cast<const T*>(p.bias) + size_t(g) * N + n) : 0.f;
       const size_t off = (size_t(g) * M + m) * N + n;
       if constexpr (EPI == EPI_GELU) {
-        store1(static_cast<T*>(p.C) + off, gelu_exact(acc[i][j] + bias));
+        store1(static_cast<T*>(p.C) + off, gelu_erf(acc[i][j] + bias));
       } else {
         static_cast<float*>(p.C)[off] = acc[i][j] + bias + load1(static_cast<const T*>(p.R) + off);
       }
@@ -270,13 +353,16 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs p) {
 
 }  // namespace
 
-bool gemm_uses_mfma(int dtype, int N, int K) { return dtype == DT_BF16 && K % BK == 0 && N % 8 == 0; }
+bool gemm_uses_mfma(int dtype, int M, int N, int K) {
+  const uint64_t lim = uint64_t(1) << 31;
+  return dtype == DT_BF16 && K % BK == 0 && N % 8 == 0 && uint64_t(M) * K * 2 < lim && uint64_t(K) * N * 2 < lim;
+}
 
 hipError_t gemm_init() { return hipSuccess; }
 
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t stream) {
   if (a.G == 0 || a.M == 0 || a.N == 0) return hipSuccess;
-  if (gemm_uses_mfma(dtype, a.N, a.K)) {
+  if (gemm_uses_mfma(dtype, a.M, a.N, a.K)) {
     const int tiles = a.G * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (epi == EPI_GELU)
       hipLaunchKernelGGL((gemm_bf16_mfma<EPI_GELU>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);

@@ -63,7 +63,7 @@ struct GemmArgs {
 };
 
 // True when the bf16 MFMA kernel handles this shape (else the generic kernel runs).
-bool gemm_uses_mfma(int dtype, int N, int K);
+bool gemm_uses_mfma(int dtype, int M, int N, int K);
 hipError_t gemm_init();
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t stream);
 
