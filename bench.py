@@ -76,6 +76,19 @@ def traffic_for(kernel, cfg, B):
     return entry.get("bytes_per_launch")
 
 
+def moe_active_flops(h, X, w, cfg, B):
+    """GEMM FLOPs of one Sparse-MoE forward counted on active experts only: per active
+    (sample, token, expert) 2 * (D * h + h * D), plus the router's 2 * D * E per (sample,
+    token); the activity pattern is read from the gates of one forward."""
+    import torch
+    gates = torch.empty((cfg.L, B, cfg.T, cfg.E), dtype=torch.float32, device="cuda")
+    h.forward(X, w, gate_out=gates)
+    torch.cuda.synchronize()
+    active = int((gates > 0).sum().item())
+    flops = active * 4.0 * cfg.D * cfg.moe_hidden + cfg.L * B * cfg.T * 2.0 * cfg.D * cfg.E
+    return flops, active / gates.numel()
+
+
 def time_forward(cfg, B, steps, warmup):
     import torch
     import rankmixer_block_forward_amd as rmx
@@ -89,6 +102,7 @@ def time_forward(cfg, B, steps, warmup):
           file=sys.stderr, flush=True)
     h = rmx.Handle.for_config(cfg, max_batch=B)
     out = torch.empty((B, cfg.D), dtype=torch.float32, device="cuda")
+    moe = moe_active_flops(h, X, w, cfg, B) if cfg.E > 0 else None
     for _ in range(warmup):
         h.forward(X, w, out=out)
     torch.cuda.synchronize()
@@ -104,7 +118,7 @@ def time_forward(cfg, B, steps, warmup):
     prof = h.profile_read()
     assert torch.isfinite(out).all().item(), "non-finite output"
     h.close()
-    return elapsed, prof
+    return elapsed, prof, moe
 
 
 def roofline(cfg, B, prof):
@@ -130,6 +144,19 @@ def roofline(cfg, B, prof):
     r["algorithmic_flops_per_launch"] = flops
     r["algorithmic_bytes_per_launch"] = nbytes
     return r
+
+
+def moe_roofline(cfg, B, prof, moe):
+    """Roofline of the dominant Sparse-MoE kernel (the expert GEMM with the larger time),
+    its FLOPs being half of the active expert FLOPs (each expert layer does D * h MACs)."""
+    kern = max(("moe_ffn1", "moe_ffn2"), key=lambda k: prof.get(k, {}).get("total_ms", 0.0))
+    active_flops = moe[0] - cfg.L * B * cfg.T * 2.0 * cfg.D * cfg.E
+    flops = active_flops / 2.0 / cfg.L
+    avg_s = prof[kern]["avg_ms"] / 1e3
+    achieved = flops / avg_s / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": kern,
+            "avg_launch_ms": round(prof[kern]["avg_ms"], 4), "algorithmic_flops_per_launch": flops}
 
 
 def cpu_baseline(cfg, n):
@@ -167,9 +194,9 @@ def main():
     if args.sweep:
         cfg = synth.SWEEP
     for B in batches:
-        elapsed, prof = time_forward(cfg, B, args.steps, args.warmup)
+        elapsed, prof, moe = time_forward(cfg, B, args.steps, args.warmup)
         ms = elapsed / args.steps * 1e3
-        flops = B * 4.0 * cfg.k * cfg.L * cfg.T * cfg.D * cfg.D
+        flops = B * 4.0 * cfg.k * cfg.L * cfg.T * cfg.D * cfg.D if moe is None else moe[0]
         tflops = flops / (ms / 1e3) / 1e12
         line = {
             "metric": METRIC,
@@ -190,8 +217,10 @@ def main():
             "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
             "kernels_ms_per_step": {k: round(v["total_ms"] / args.steps, 4) for k, v in prof.items()
                                     if k != "_dropped"},
-            "roofline": roofline(cfg, B, prof),
+            "roofline": roofline(cfg, B, prof) if moe is None else moe_roofline(cfg, B, prof, moe),
         }
+        if moe is not None:
+            line["config"].update(experts=cfg.E, expert_hidden=cfg.moe_hidden, active_fraction=round(moe[1], 4))
         if not args.sweep and not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_samples)
         print(json.dumps(line), flush=True)

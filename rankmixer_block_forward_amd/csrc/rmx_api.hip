@@ -6,6 +6,8 @@
 //              gemm1  S[t] W1[t] + b1[t], GELU                                   -> H
 //              gemm2  H[t] W2[t] + b2[t] + S[t]                                   -> Y
 //   then:      rows   LN2 of block L, mean pool over tokens (+ X_L)              -> out
+// With the Sparse-MoE PFFN (moe_experts > 0) gemm1 / gemm2 are replaced by: route (gate,
+// scan, scatter), the grouped expert GEMMs over the compacted row lists, and combine.
 // (RankMixer paper translation, section 3.1 eq (1) and 3.3; "RankMixer 详解（1）",
 // sections 3-5.)  Workspace, all token-major [T, max_batch, *]: S and H in the model
 // dtype, Y in fp32.
@@ -15,6 +17,7 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <type_traits>
 #include <string>
 #include <vector>
 
@@ -42,6 +45,19 @@ struct rmx_handle {
   void* S = nullptr;   // [T, max_batch, D]   dtype
   void* H = nullptr;   // [T, max_batch, kD]  dtype
   float* Y = nullptr;  // [T, max_batch, D]   fp32
+  // Sparse-MoE workspace (moe_experts > 0); G = T * E groups, R = G * max_batch rows
+  float* moe_g = nullptr;        // [G, max_batch]
+  int* moe_cnt = nullptr;        // [G, nchunk]
+  int* moe_chunk_off = nullptr;  // [G, nchunk]
+  int* moe_group_rows = nullptr; // [G]
+  int* moe_group_start = nullptr;// [G + 1]
+  int* moe_tile_start = nullptr; // [G + 1]
+  int* moe_src_row = nullptr;    // [R]
+  float* moe_row_gate = nullptr; // [R]
+  int* moe_pos = nullptr;        // [G, max_batch]
+  void* moe_hidden = nullptr;    // [R, h]  bf16
+  float* moe_out = nullptr;      // [R, D]  fp32
+  std::vector<void*> allocs;     // everything hipMalloc'd, freed by rmx_destroy
   std::string last_error;
   bool prof = false;
   std::vector<ProfPair> pending;
@@ -135,8 +151,17 @@ rmx_status validate_config(const rmx_config* c) {
   if (c->max_batch < 0) return fail(nullptr, RMX_ERR_INVALID_ARG, "max_batch < 0");
   if (c->moe_experts < 0 || c->moe_hidden < 0)
     return fail(nullptr, RMX_ERR_INVALID_ARG, "moe_experts, moe_hidden must be >= 0");
-  if (c->moe_experts > 0)
-    return fail(nullptr, RMX_ERR_UNSUPPORTED, "the Sparse-MoE PFFN is not built in this library version");
+  if (c->moe_experts > 0) {
+    const int E = c->moe_experts, h = c->moe_hidden;
+    if (c->dtype != RMX_BF16) return fail(nullptr, RMX_ERR_UNSUPPORTED, "the Sparse-MoE PFFN runs in bf16 only");
+    if (h < 1) return fail(nullptr, RMX_ERR_INVALID_ARG, "moe_hidden must be >= 1 when moe_experts > 0");
+    if (E > MOE_MAX_E || int64_t(c->T) * E > MOE_MAX_GROUPS || int64_t(c->D) * E > MOE_MAX_GATE_WEIGHTS)
+      return fail(nullptr, RMX_ERR_UNSUPPORTED, "MoE limits: E <= %d, T*E <= %d, D*E <= %d", MOE_MAX_E,
+                  MOE_MAX_GROUPS, MOE_MAX_GATE_WEIGHTS);
+    if (!gemm_moe_supported(h, c->D, int64_t(c->T) * c->max_batch) ||
+        !gemm_moe_supported(c->D, h, c->max_batch))
+      return fail(nullptr, RMX_ERR_UNSUPPORTED, "MoE GEMMs need D %% 32 == 0, moe_hidden %% 32 == 0 and slices < 2 GiB");
+  }
   const bool vec = rows_vectorized(c->T, c->D);
   if (c->dtype == RMX_BF16 && !vec)
     return fail(nullptr, RMX_ERR_UNSUPPORTED, "bf16 needs D %% 8 == 0 and (D/T) %% 8 == 0");
@@ -206,6 +231,30 @@ hipError_t run_gemm(rmx_handle* h, hipStream_t s, int epi, const GemmArgs& a) {
   return e;
 }
 
+hipError_t run_moe_route(rmx_handle* h, hipStream_t s, const MoeArgs& a) {
+  ProfPair pp;
+  prof_begin(h, s, &pp, RMX_KERNEL_MOE_GATE);
+  hipError_t e = launch_moe_route(a, s);
+  prof_end(h, s, &pp);
+  return e;
+}
+
+hipError_t run_moe_gemm(rmx_handle* h, hipStream_t s, int epi, const GemmArgs& a) {
+  ProfPair pp;
+  prof_begin(h, s, &pp, epi == EPI_MOE1 ? RMX_KERNEL_MOE_FFN1 : RMX_KERNEL_MOE_FFN2);
+  hipError_t e = launch_gemm_moe(epi, a, s);
+  prof_end(h, s, &pp);
+  return e;
+}
+
+hipError_t run_moe_combine(rmx_handle* h, hipStream_t s, const MoeArgs& a) {
+  ProfPair pp;
+  prof_begin(h, s, &pp, RMX_KERNEL_MOE_COMBINE);
+  hipError_t e = launch_moe_combine(a, s);
+  prof_end(h, s, &pp);
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,14 +300,44 @@ rmx_status rmx_create(const rmx_config* cfg, rmx_handle** out_handle) {
   const size_t esz = dtype_size(cfg->dtype);
   const size_t rows = size_t(cfg->T) * size_t(cfg->max_batch);
   const size_t nS = rows * cfg->D, nH = rows * size_t(cfg->k) * cfg->D;
-  if (rows > 0) {
-    if (hipMalloc(&h->S, nS * esz) != hipSuccess || hipMalloc(&h->H, nH * esz) != hipSuccess ||
-        hipMalloc(reinterpret_cast<void**>(&h->Y), nS * sizeof(float)) != hipSuccess) {
+  size_t total = 0;
+  bool ok = true;
+  auto alloc = [&](auto** ptr, size_t bytes) {
+    if (!ok || bytes == 0) return;
+    void* q = nullptr;
+    if (hipMalloc(&q, bytes) != hipSuccess) {
       (void)hipGetLastError();
-      rmx_destroy(h);
-      return fail(nullptr, RMX_ERR_OUT_OF_MEMORY, "workspace of %zu bytes could not be allocated",
-                  nS * esz + nH * esz + nS * 4);
+      ok = false;
+      return;
     }
+    h->allocs.push_back(q);
+    *ptr = static_cast<std::remove_pointer_t<std::remove_reference_t<decltype(*ptr)>>*>(q);
+    total += bytes;
+  };
+  if (rows > 0) {
+    alloc(&h->S, nS * esz);
+    alloc(&h->Y, nS * sizeof(float));
+    if (cfg->moe_experts == 0) {
+      alloc(&h->H, nH * esz);
+    } else {
+      const size_t G = size_t(cfg->T) * cfg->moe_experts, mb = size_t(cfg->max_batch);
+      const size_t nchunk = (mb + 63) / 64, R = G * mb;
+      alloc(&h->moe_g, G * mb * sizeof(float));
+      alloc(&h->moe_cnt, G * nchunk * sizeof(int));
+      alloc(&h->moe_chunk_off, G * nchunk * sizeof(int));
+      alloc(&h->moe_group_rows, G * sizeof(int));
+      alloc(&h->moe_group_start, (G + 1) * sizeof(int));
+      alloc(&h->moe_tile_start, (G + 1) * sizeof(int));
+      alloc(&h->moe_src_row, R * sizeof(int));
+      alloc(&h->moe_row_gate, R * sizeof(float));
+      alloc(&h->moe_pos, G * mb * sizeof(int));
+      alloc(&h->moe_hidden, R * size_t(cfg->moe_hidden) * 2);
+      alloc(&h->moe_out, R * size_t(cfg->D) * sizeof(float));
+    }
+  }
+  if (!ok) {
+    rmx_destroy(h);
+    return fail(nullptr, RMX_ERR_OUT_OF_MEMORY, "workspace allocation failed after %zu bytes", total);
   }
   *out_handle = h;
   return RMX_OK;
@@ -266,12 +345,10 @@ rmx_status rmx_create(const rmx_config* cfg, rmx_handle** out_handle) {
 
 rmx_status rmx_destroy(rmx_handle* h) {
   if (!h) return RMX_OK;
-  if (h->S || h->H || h->Y || !h->pending.empty() || !h->free_events.empty()) {
+  if (!h->allocs.empty() || !h->pending.empty() || !h->free_events.empty()) {
     (void)hipDeviceSynchronize();
   }
-  if (h->S) (void)hipFree(h->S);
-  if (h->H) (void)hipFree(h->H);
-  if (h->Y) (void)hipFree(h->Y);
+  for (void* q : h->allocs) (void)hipFree(q);
   for (auto& p : h->pending) {
     (void)hipEventDestroy(p.start);
     (void)hipEventDestroy(p.stop);
@@ -293,7 +370,8 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
   if (B < 0 || B > c.max_batch)
     return fail(h, RMX_ERR_INVALID_ARG, "B=%lld outside [0, max_batch=%lld]", (long long)B,
                 (long long)c.max_batch);
-  if (gate_out) return fail(h, RMX_ERR_INVALID_ARG, "gate_out must be NULL for a dense handle");
+  const bool moe = c.moe_experts > 0;
+  if (gate_out && !moe) return fail(h, RMX_ERR_INVALID_ARG, "gate_out must be NULL for a dense handle");
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
     (void)hipGetLastError();
@@ -307,16 +385,26 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
   if ((st = check_dev(h, X, size_t(B) * T * D * esz, dev, "X")) != RMX_OK) return st;
   if ((st = check_dev(h, out, size_t(B) * D * 4, dev, "out")) != RMX_OK) return st;
   if ((st = check_dev_opt(h, xl_out, size_t(B) * T * D * esz, dev, "xl_out")) != RMX_OK) return st;
-  if ((st = check_dev(h, w->W1, Ls * T * D * kD * esz, dev, "W1")) != RMX_OK) return st;
-  if ((st = check_dev(h, w->W2, Ls * T * kD * D * esz, dev, "W2")) != RMX_OK) return st;
-  if ((st = check_dev_opt(h, w->b1, Ls * T * kD * esz, dev, "b1")) != RMX_OK) return st;
-  if ((st = check_dev_opt(h, w->b2, Ls * T * D * esz, dev, "b2")) != RMX_OK) return st;
+  const size_t E = size_t(c.moe_experts), hid = size_t(c.moe_hidden);
+  if (moe) {
+    if ((st = check_dev(h, w->Wg, Ls * T * D * E * esz, dev, "Wg")) != RMX_OK) return st;
+    if ((st = check_dev(h, w->We1, Ls * T * E * D * hid * esz, dev, "We1")) != RMX_OK) return st;
+    if ((st = check_dev(h, w->We2, Ls * T * E * hid * D * esz, dev, "We2")) != RMX_OK) return st;
+    if ((st = check_dev_opt(h, w->be1, Ls * T * E * hid * esz, dev, "be1")) != RMX_OK) return st;
+    if ((st = check_dev_opt(h, w->be2, Ls * T * E * D * esz, dev, "be2")) != RMX_OK) return st;
+    if ((st = check_dev_opt(h, gate_out, Ls * size_t(B) * T * E * 4, dev, "gate_out")) != RMX_OK) return st;
+  } else {
+    if ((st = check_dev(h, w->W1, Ls * T * D * kD * esz, dev, "W1")) != RMX_OK) return st;
+    if ((st = check_dev(h, w->W2, Ls * T * kD * D * esz, dev, "W2")) != RMX_OK) return st;
+    if ((st = check_dev_opt(h, w->b1, Ls * T * kD * esz, dev, "b1")) != RMX_OK) return st;
+    if ((st = check_dev_opt(h, w->b2, Ls * T * D * esz, dev, "b2")) != RMX_OK) return st;
+    if (w->Wg || w->We1 || w->We2 || w->be1 || w->be2)
+      return fail(h, RMX_ERR_INVALID_ARG, "MoE weights given to a dense handle");
+  }
   if ((st = check_dev(h, w->ln1_g, Ls * D * esz, dev, "ln1_g")) != RMX_OK) return st;
   if ((st = check_dev(h, w->ln1_b, Ls * D * esz, dev, "ln1_b")) != RMX_OK) return st;
   if ((st = check_dev(h, w->ln2_g, Ls * D * esz, dev, "ln2_g")) != RMX_OK) return st;
   if ((st = check_dev(h, w->ln2_b, Ls * D * esz, dev, "ln2_b")) != RMX_OK) return st;
-  if (w->Wg || w->We1 || w->We2 || w->be1 || w->be2)
-    return fail(h, RMX_ERR_INVALID_ARG, "MoE weights given to a dense handle");
   // The outputs must not overlap the inputs: out and xl_out are written while X is read.
   auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -350,6 +438,58 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
     ra.eps = c.ln_eps;
     e = run_rows(h, s, n == 0 ? ROWS_FIRST : ROWS_MID, ra);
     if (e != hipSuccess) break;
+
+    if (moe) {
+      // Sparse-MoE PFFN: route, expert FFN1 over gathered rows, gate-scaled FFN2, combine.
+      MoeArgs ma{};
+      ma.S = h->S;
+      ma.Wg = at(w->Wg, size_t(n) * T * D * E);
+      ma.g = h->moe_g;
+      ma.gate_out = gate_out ? gate_out + size_t(n) * size_t(B) * T * E : nullptr;
+      ma.cnt = h->moe_cnt;
+      ma.chunk_off = h->moe_chunk_off;
+      ma.group_rows = h->moe_group_rows;
+      ma.group_start = h->moe_group_start;
+      ma.tile_start = h->moe_tile_start;
+      ma.src_row = h->moe_src_row;
+      ma.row_gate = h->moe_row_gate;
+      ma.pos = h->moe_pos;
+      ma.Ye = h->moe_out;
+      ma.Y = h->Y;
+      ma.B = Bi;
+      ma.T = c.T;
+      ma.D = c.D;
+      ma.E = c.moe_experts;
+      ma.nchunk = (Bi + 63) / 64;
+      if ((e = run_moe_route(h, s, ma)) != hipSuccess) break;
+      GemmArgs m1{};
+      m1.A = h->S;
+      m1.W = at(w->We1, size_t(n) * T * E * D * hid);
+      m1.bias = at(w->be1, size_t(n) * T * E * hid);
+      m1.C = h->moe_hidden;
+      m1.G = int(T * E);
+      m1.N = int(hid);
+      m1.K = c.D;
+      m1.group_start = h->moe_group_start;
+      m1.tile_start = h->moe_tile_start;
+      m1.src_row = h->moe_src_row;
+      m1.a_rows = int(T) * Bi;
+      if ((e = run_moe_gemm(h, s, EPI_MOE1, m1)) != hipSuccess) break;
+      GemmArgs m2{};
+      m2.A = h->moe_hidden;
+      m2.W = at(w->We2, size_t(n) * T * E * hid * D);
+      m2.bias = at(w->be2, size_t(n) * T * E * D);
+      m2.C = h->moe_out;
+      m2.G = int(T * E);
+      m2.N = c.D;
+      m2.K = int(hid);
+      m2.group_start = h->moe_group_start;
+      m2.tile_start = h->moe_tile_start;
+      m2.row_gate = h->moe_row_gate;
+      if ((e = run_moe_gemm(h, s, EPI_MOE2, m2)) != hipSuccess) break;
+      e = run_moe_combine(h, s, ma);
+      continue;
+    }
 
     GemmArgs g1{};
     g1.A = h->S;

@@ -87,6 +87,16 @@ __device__ __forceinline__ void mfma_block(f32x16_t (&acc)[4][4], const Frags& f
   acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i][j], 0, 0, 0);
 }
 
+// Buffer descriptor over [base, base + bytes), built from wave-uniform values so that it
+// lives in scalar registers (the copies below take it as an SGPR operand).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0,
+                                           int(__builtin_amdgcn_readfirstlane(bytes)), 0x00020000);
+}
+
 // One LDS-destination buffer load: 64 lanes x 16 B to lds_dst + 16 * lane.
 __device__ __forceinline__ void copy_to_lds(uint32_t lds_dst, uint32_t voff, __amdgpu_buffer_rsrc_t rsrc,
                                             int soff) {
@@ -94,43 +104,36 @@ __device__ __forceinline__ void copy_to_lds(uint32_t lds_dst, uint32_t voff, __a
                :: "s"(lds_dst), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 
-template <int EPI>
-__global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[NS * STAGE_BYTES];
-  lds_u8* const smem = (lds_u8*)smem_g;  // the generic pointer of a __shared__ array is in LDS
-  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
+// One 256 x 256 output tile: the operand sources of its K loop.
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t rA, rW;
+  uint32_t offA[4], offW[4];  // per-lane byte offsets of this lane's copies (K step 0)
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int M = p.M, N = p.N, K = p.K;
-  const int nMt = (M + BM - 1) / BM, nNt = (N + BN - 1) / BN;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int g = id / (nMt * nNt);
-  const int rem = id - g * nMt * nNt;
-  const int nt = rem / nMt, mt = rem - nt * nMt;
-  const int m0 = mt * BM, n0 = nt * BN;
-
-  // Slices are < 2^31 bytes (checked at launch); an offset equal to the slice size is out
-  // of range whether or not the uniform offset takes part in the range check.
-  const uint32_t bytesA = uint32_t(M) * uint32_t(K) * 2u, bytesW = uint32_t(K) * uint32_t(N) * 2u;
-  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(static_cast<const uint16_t*>(p.A) + size_t(g) * M * K), 0, int(bytesA), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(static_cast<const uint16_t*>(p.W) + size_t(g) * K * N), 0, int(bytesW), 0x00020000);
-
-  // Copy-in: wave w fills A rows 64w .. 64w+63 (4 loads of 16 rows) and W k-rows
-  // 8w .. 8w+7 (4 loads of 2 rows) of a stage; lane q lands in LDS chunk q of its load,
-  // so the swizzle is applied by choosing the chunk each lane fetches.
-  uint32_t offA[4], offW[4];
+// Per-lane copy offsets.  Copy-in: wave w fills A rows 64w .. 64w+63 (4 loads of 16 rows)
+// and W k-rows 8w .. 8w+7 (4 loads of 2 rows) of a stage; lane q lands in LDS chunk q of
+// its load, so the swizzle is applied by choosing the chunk each lane fetches.  `a_row`
+// maps a tile row to the byte offset of its first element in A, or `a_oob` when the row
+// does not exist (the buffer load then returns zeros).
+template <typename RowOff>
+__device__ __forceinline__ void tile_offsets(TileSrc& ts, int wave, int lane, int n0, int N, RowOff a_row,
+                                             uint32_t bytesW) {
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const int r = 64 * wave + 16 * a + (lane >> 2);
     const int c = (lane & 3) ^ swz_a(r);
-    offA[a] = (m0 + r < M) ? (uint32_t(m0 + r) * uint32_t(K) + uint32_t(c * 8)) * 2u : bytesA;
+    ts.offA[a] = a_row(r, c * 16);
     const int kr = 8 * wave + 2 * a + (lane >> 5);
     const int col = n0 + (((lane & 31) ^ swz_w(kr)) * 8);
-    offW[a] = col < N ? (uint32_t(kr) * uint32_t(N) + uint32_t(col)) * 2u : bytesW;
+    ts.offW[a] = col < N ? (uint32_t(kr) * uint32_t(N) + uint32_t(col)) * 2u : bytesW;
   }
+}
+
+// The K loop of one tile: acc (zeroed here) += A_tile (256 x K) * W_tile (K x 256).
+// Ends with every copy drained and the workgroup synchronized, so that the ring memory
+// can be reused by the caller.
+__device__ __forceinline__ void mfma_tile(f32x16_t (&acc)[4][4], const TileSrc& ts, lds_u8* smem, uint32_t lds0,
+                                          int K, int N, int wave, int lane) {
   const int nk = K / BK;
   // Copy q (0..7) of K step kt into ring stage `stage`; steps past the end reload the last
   // step (in bounds, never read) so that every K step issues the same number of loads.
@@ -139,11 +142,11 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
     const uint32_t sbase = lds0 + uint32_t(stage) * STAGE_BYTES;
     if (q < 4) {
       const uint32_t dst = __builtin_amdgcn_readfirstlane(sbase + uint32_t(64 * wave + 16 * q) * 64u);
-      copy_to_lds(dst, offA[q], rA, kt * BK * 2);
+      copy_to_lds(dst, ts.offA[q], ts.rA, kt * BK * 2);
     } else {
       const uint32_t dst =
           __builtin_amdgcn_readfirstlane(sbase + A_STAGE_BYTES + uint32_t(8 * wave + 2 * (q - 4)) * 512u);
-      copy_to_lds(dst, offW[q - 4], rW, kt * BK * N * 2);
+      copy_to_lds(dst, ts.offW[q - 4], ts.rW, kt * BK * N * 2);
     }
   };
 
@@ -181,7 +184,6 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
     }
   };
 
-  f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -234,15 +236,22 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
     }
     stage = nstage;
   }
-  // Drain the trailing copies before the ring memory is reused for the epilogue.
+  // Drain the trailing copies before the ring memory is reused.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+}
 
-  // Epilogue.  Accumulator layout of a 32 x 32 block: lane l, register r holds
-  // row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.  Each wave stages 32 rows x 128
-  // columns at a time through LDS so that every lane then owns 8 consecutive columns of
-  // one row: 16-byte global stores, and coalesced bias / residual loads.
-  float* st = reinterpret_cast<float*>(smem_g) + wave * 32 * EPI_LD;
+// Epilogue of one tile.  Accumulator layout of a 32 x 32 block: lane l, register r holds
+// row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.  Each wave stages 32 rows x 128
+// columns at a time through LDS so that every lane then owns 8 consecutive columns of one
+// row: 16-byte global stores, and coalesced bias / residual loads.  `out_row(m)` is the
+// output row of tile row m, or -1 if it does not exist.
+template <int EPI, typename OutRow>
+__device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[4][4], float* smem_f, const GemmArgs& p,
+                                              const bf16_t* bias_g, int n0, int wave, int lane, OutRow out_row) {
+  const int N = p.N;
+  const int wm = wave >> 1, wn = wave & 1;
+  float* st = smem_f + wave * 32 * EPI_LD;
   const int col8 = (lane & 15) * 8;
   const int rsub = lane >> 4;
   const int n = n0 + wn * 128 + col8;
@@ -250,7 +259,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
   float bias[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) bias[e] = 0.f;
-  if (p.bias && n_ok) load8(static_cast<const bf16_t*>(p.bias) + size_t(g) * N + n, bias);
+  if (bias_g && n_ok) load8(bias_g + n, bias);
 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -265,28 +274,132 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
 #pragma unroll
     for (int pass = 0; pass < 8; ++pass) {
       const int row = pass * 4 + rsub;
-      const int m = m0 + wm * 128 + i * 32 + row;
+      const int orow = out_row(wm * 128 + i * 32 + row);
       float v[8];
       const float4 x0 = *reinterpret_cast<const float4*>(st + row * EPI_LD + col8);
       const float4 x1 = *reinterpret_cast<const float4*>(st + row * EPI_LD + col8 + 4);
       v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
       v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-      if (m < M && n_ok) {
-        const size_t off = (size_t(g) * M + m) * N + n;
-        if constexpr (EPI == EPI_GELU) {
+      if (orow >= 0 && n_ok) {
+        const size_t off = size_t(orow) * N + n;
+        if constexpr (EPI == EPI_GELU || EPI == EPI_MOE1) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[e]);
           store8(static_cast<bf16_t*>(p.C) + off, v);
-        } else {
+        } else if constexpr (EPI == EPI_RESID) {
           float rr[8];
           load8(static_cast<const bf16_t*>(p.R) + off, rr);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = v[e] + bias[e] + rr[e];
           store8(static_cast<float*>(p.C) + off, v);
+        } else {
+          const float gv = p.row_gate[orow];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = gv * (v[e] + bias[e]);
+          store8(static_cast<float*>(p.C) + off, v);
         }
       }
     }
     __syncthreads();
+  }
+}
+
+// Dense per-token GEMM: one workgroup per tile, G * ceil(M/256) * ceil(N/256) tiles.
+template <int EPI>
+__global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[NS * STAGE_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_g;  // the generic pointer of a __shared__ array is in LDS
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nMt = (M + BM - 1) / BM, nNt = (N + BN - 1) / BN;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = id / (nMt * nNt);
+  const int rem = id - g * nMt * nNt;
+  const int nt = rem / nMt, mt = rem - nt * nMt;
+  const int m0 = mt * BM, n0 = nt * BN;
+
+  // Slices are < 2^31 bytes (checked at launch); an offset equal to the slice size is out
+  // of range whether or not the uniform offset takes part in the range check.
+  const uint32_t bytesA = uint32_t(M) * uint32_t(K) * 2u, bytesW = uint32_t(K) * uint32_t(N) * 2u;
+  TileSrc ts;
+  ts.rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(g) * M * K, bytesA);
+  ts.rW = make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * K * N, bytesW);
+  tile_offsets(ts, wave, lane, n0, N,
+               [&](int r, int cbytes) {
+                 return (m0 + r < M) ? uint32_t(m0 + r) * uint32_t(K) * 2u + uint32_t(cbytes) : bytesA;
+               },
+               bytesW);
+  f32x16_t acc[4][4];
+  mfma_tile(acc, ts, smem, lds0, K, N, wave, lane);
+  const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
+  tile_epilogue<EPI>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, wave, lane,
+                     [&](int m) { return m0 + m < M ? g * M + m0 + m : -1; });
+}
+
+// Sparse-MoE grouped GEMM.  Group g has rows group_start[g] .. group_start[g+1]-1 of the
+// compacted row space and tile_start[g+1] - tile_start[g] row tiles; the grid is a fixed set
+// of workgroups that walk the tile space (its size is only known on the device).  Each XCD
+// takes a contiguous range of tiles; within a group tiles run M-fastest, so a group's
+// expert weights are reused across its row tiles.
+template <int EPI>
+__global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_moe(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[NS * STAGE_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_g;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int N = p.N, K = p.K, G = p.G;
+  const int nNt = (N + BN - 1) / BN;
+  const int total = p.tile_start[G] * nNt;
+  const int per_xcd = int(gridDim.x) / NUM_XCD;  // gridDim.x is a multiple of NUM_XCD
+  const int xcd = int(blockIdx.x) % NUM_XCD, slot = int(blockIdx.x) / NUM_XCD;
+  const int chunk = (total + NUM_XCD - 1) / NUM_XCD;
+  const int lo = xcd * chunk, hi = min(total, lo + chunk);
+  const uint32_t bytesW = uint32_t(K) * uint32_t(N) * 2u;
+
+  for (int tile = lo + slot; tile < hi; tile += per_xcd) {
+    // group of this tile: the last g with tile_start[g] * nNt <= tile
+    int glo = 0, ghi = G;  // invariant: tile_start[glo]*nNt <= tile < tile_start[ghi]*nNt
+    while (ghi - glo > 1) {
+      const int mid = (glo + ghi) >> 1;
+      if (p.tile_start[mid] * nNt <= tile) glo = mid; else ghi = mid;
+    }
+    const int g = glo;
+    const int mtiles = p.tile_start[g + 1] - p.tile_start[g];
+    const int local = tile - p.tile_start[g] * nNt;
+    const int nt = local / mtiles, mt = local - nt * mtiles;
+    const int row0 = p.group_start[g], rows = p.group_start[g + 1] - row0;
+    const int m0 = mt * BM, n0 = nt * BN;
+
+    TileSrc ts;
+    ts.rW = make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * K * N, bytesW);
+    if constexpr (EPI == EPI_MOE1) {
+      // rows gathered from A = S [a_rows, K] through src_row
+      const uint32_t bytesA = uint32_t(p.a_rows) * uint32_t(K) * 2u;
+      ts.rA = make_rsrc(p.A, bytesA);
+      tile_offsets(ts, wave, lane, n0, N,
+                   [&](int r, int cbytes) {
+                     return (m0 + r < rows) ? uint32_t(p.src_row[row0 + m0 + r]) * uint32_t(K) * 2u + uint32_t(cbytes)
+                                            : bytesA;
+                   },
+                   bytesW);
+    } else {
+      // rows of A are this group's compacted rows, contiguous
+      const uint32_t bytesA = uint32_t(rows) * uint32_t(K) * 2u;
+      ts.rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(row0) * K, bytesA);
+      tile_offsets(ts, wave, lane, n0, N,
+                   [&](int r, int cbytes) {
+                     return (m0 + r < rows) ? uint32_t(m0 + r) * uint32_t(K) * 2u + uint32_t(cbytes) : bytesA;
+                   },
+                   bytesW);
+    }
+    f32x16_t acc[4][4];
+    mfma_tile(acc, ts, smem, lds0, K, N, wave, lane);
+    const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
+    tile_epilogue<EPI>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, wave, lane,
+                       [&](int m) { return m0 + m < rows ? row0 + m0 + m : -1; });
   }
 }
 
@@ -359,6 +472,25 @@ bool gemm_uses_mfma(int dtype, int M, int N, int K) {
 }
 
 hipError_t gemm_init() { return hipSuccess; }
+
+bool gemm_moe_supported(int N, int K, int64_t a_rows) {
+  const uint64_t lim = uint64_t(1) << 31;
+  return K % BK == 0 && N % 8 == 0 && uint64_t(a_rows) * K * 2 < lim && uint64_t(K) * N * 2 < lim &&
+         uint64_t(a_rows) * N * 2 < lim;
+}
+
+hipError_t launch_gemm_moe(int epi, const GemmArgs& a, hipStream_t stream) {
+  if (a.G == 0) return hipSuccess;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int grid = ((cus + NUM_XCD - 1) / NUM_XCD) * NUM_XCD;  // one workgroup per CU, whole XCDs
+  if (epi == EPI_MOE1)
+    hipLaunchKernelGGL((gemm_bf16_moe<EPI_MOE1>), dim3(grid), dim3(MFMA_THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_bf16_moe<EPI_MOE2>), dim3(grid), dim3(MFMA_THREADS), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t stream) {
   if (a.G == 0 || a.M == 0 || a.N == 0) return hipSuccess;

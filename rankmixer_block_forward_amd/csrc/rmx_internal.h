@@ -46,12 +46,44 @@ hipError_t launch_rows(int dtype, int mode, const RowsArgs& a, hipStream_t strea
 hipError_t launch_token_mix(int dtype, const void* X, void* Y, int64_t B, int T, int D,
                             hipStream_t stream);
 
+// ---------------------------------------------------------------- Sparse-MoE routing
+// Group gi = t * E + e.  Rows of a group are listed in ascending sample order.
+constexpr int MOE_MAX_E = 16;
+constexpr int MOE_MAX_GROUPS = 1024;          // T * E
+constexpr int MOE_MAX_GATE_WEIGHTS = 16384;   // D * E (router of one token in LDS)
+constexpr int MOE_TILE_M = 256;               // rows per grouped-GEMM tile
+
+struct MoeArgs {
+  const void* S;      // [T, B, D] bf16, the LN1 output of this block
+  const void* Wg;     // [T, D, E] bf16, router weights of this block
+  float* g;           // [T, E, B] gate values
+  float* gate_out;    // [B, T, E] of this block, nullable
+  int* cnt;           // [T * E, nchunk] active rows per 64-row chunk
+  int* chunk_off;     // [T * E, nchunk] exclusive prefix of cnt within a group
+  int* group_rows;    // [T * E]
+  int* group_start;   // [T * E + 1] first compacted row of each group
+  int* tile_start;    // [T * E + 1] cumulative MOE_TILE_M-row tiles
+  int* src_row;       // [T * E * B] compacted row -> S row (t * B + b)
+  float* row_gate;    // [T * E * B] compacted row -> gate value
+  int* pos;           // [T, E, B] -> compacted row, or -1 if the expert is inactive
+  const float* Ye;    // [rows, D] fp32 gate-scaled expert outputs (combine input)
+  float* Y;           // [T, B, D] fp32 pre-LN2 rows (combine output)
+  int B, T, D, E, nchunk;
+};
+
+hipError_t launch_moe_route(const MoeArgs& a, hipStream_t stream);
+hipError_t launch_moe_combine(const MoeArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- grouped GEMM
 // G independent products C_g = A_g W_g (+ epilogue), g = 0..G-1 (one per token):
 //   A [G, M, K] (dtype)   W [G, K, N] (dtype)   bias [G, N] (dtype, nullable)
 //   EPI_GELU:  C [G, M, N] (dtype) = GELU(A W + bias)
 //   EPI_RESID: C [G, M, N] (fp32)  = A W + bias + R,  R [G, M, N] (dtype)
-enum Epilogue { EPI_GELU = 0, EPI_RESID = 1 };
+//   Sparse-MoE (grouped, variable rows per group, persistent tile loop):
+//   EPI_MOE1:  C [rows, N] (bf16) = GELU(A[src_row] W_g + bias_g), A = S [T * B, K]
+//   EPI_MOE2:  C [rows, N] (fp32) = row_gate * (A W_g + bias_g),   A = C of EPI_MOE1
+//   group g owns compacted rows group_start[g] .. group_start[g + 1] - 1.
+enum Epilogue { EPI_GELU = 0, EPI_RESID = 1, EPI_MOE1 = 2, EPI_MOE2 = 3 };
 
 struct GemmArgs {
   const void* A;
@@ -60,10 +92,18 @@ struct GemmArgs {
   const void* R;
   void* C;
   int G, M, N, K;
+  const int* group_start;
+  const int* tile_start;
+  const int* src_row;
+  const float* row_gate;
+  int a_rows;  // EPI_MOE1: rows of A (T * B)
 };
 
 // True when the bf16 MFMA kernel handles this shape (else the generic kernel runs).
 bool gemm_uses_mfma(int dtype, int M, int N, int K);
+// Sparse-MoE grouped GEMM launch (bf16 MFMA only); `max_rows` bounds every group's rows.
+hipError_t launch_gemm_moe(int epi, const GemmArgs& a, hipStream_t stream);
+bool gemm_moe_supported(int N, int K, int64_t a_rows);
 hipError_t gemm_init();
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t stream);
 

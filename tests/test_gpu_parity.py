@@ -213,3 +213,64 @@ def test_profile_counts_launches():
         assert all(v["total_ms"] > 0 for k, v in p.items() if k != "_dropped")
         h.profile_reset()
         assert h.profile_read() == {"_dropped": 0}
+
+
+# ------------------------------------------------------------------ Sparse-MoE
+
+def _run_moe(cfg, inp, with_xl=True):
+    rmx = _rmx()
+    X, w = rmx.upload(inp)
+    B = X.shape[0]
+    with rmx.Handle.for_config(cfg, max_batch=B) as h:
+        out = torch.full((B, cfg.D), float("nan"), dtype=torch.float32, device="cuda")
+        xl = torch.full_like(X, float("nan")) if with_xl else None
+        gates = torch.full((cfg.L, B, cfg.T, cfg.E), float("nan"), dtype=torch.float32, device="cuda")
+        h.forward(X, w, out=out, xl_out=xl, gate_out=gates)
+        torch.cuda.synchronize()
+    return to_np(out), (to_np(xl) if with_xl else None), to_np(gates)
+
+
+def _check_gates(g, g_ref, label):
+    # gates come from the bf16 LN1 output on the GPU and from fp64 on the CPU: compare as
+    # values (ReLU is continuous, so a sign flip near zero moves the output only by O(g))
+    g_ref = np.stack(g_ref, axis=0)
+    assert g.shape == g_ref.shape
+    err = np.linalg.norm(g - g_ref) / max(np.linalg.norm(g_ref), 1e-30)
+    assert err <= 1e-2, f"{label}: gate rel-L2 {err}"
+    flip = (g > 0) != (g_ref > 0)
+    assert np.all(np.abs(g_ref[flip]) < 2e-2), f"{label}: activity differs away from zero"
+    print(f"{label}: gate rel-L2 {err:.2e}, active {float((g_ref > 0).mean()):.3f}", flush=True)
+
+
+@pytest.mark.parametrize("B,T,D,E,h,L", [(100, 4, 64, 4, 64, 2), (300, 2, 256, 8, 96, 1), (1, 4, 64, 2, 32, 1),
+                                         (257, 8, 128, 3, 128, 2)])
+def test_moe_shapes(B, T, D, E, h, L):
+    cfg = synth.Config("moe", B=B, T=T, D=D, k=2, L=L, dtype="bf16", E=E, moe_hidden=h, bias_std=0.02)
+    inp = synth.make_inputs(cfg, seed=B + E)
+    o, xl, g = _run_moe(cfg, inp)
+    o_ref, xl_ref, g_ref = oracle.forward(inp.X, inp.layers(), cfg.eps)
+    check(cfg, o, xl, o_ref, xl_ref, f"moe {B}x{T}x{D} E{E} h{h} L{L}")
+    _check_gates(g, g_ref, f"moe {B}x{T}x{D} E{E}")
+
+
+def test_moe_zero_router_is_ffn_free_block():
+    cfg = synth.Config("moe0", B=64, T=4, D=64, k=2, L=2, dtype="bf16", E=4, moe_hidden=64)
+    inp = synth.make_inputs(cfg, seed=3)
+    inp.moe["Wg"][:] = 0.0
+    o, xl, g = _run_moe(cfg, inp)
+    assert not g.any()
+    o_ref, xl_ref, _ = oracle.forward(inp.X, inp.layers(), cfg.eps)
+    check(cfg, o, xl, o_ref, xl_ref, "moe zero router")
+
+
+def test_rankmixer_1b_moe_full_size():
+    cfg = synth.MOE
+    inp = synth.make_inputs(cfg, seed=0)
+    o, _, g = _run_moe(cfg, inp, with_xl=False)
+    assert np.isfinite(o).all()
+    rows = sample_rows(cfg.B, 4)
+    sub = synth.Inputs(cfg, inp.X[rows], inp.W1, inp.b1, inp.W2, inp.b2, inp.ln1_g, inp.ln1_b,
+                       inp.ln2_g, inp.ln2_b, inp.moe)
+    o_ref, _, g_ref = oracle.forward(sub.X, sub.layers(), cfg.eps)
+    check(cfg, o[rows], None, o_ref, None, "1B MoE B=2048")
+    _check_gates(g[:, rows], g_ref, "1B MoE B=2048")
