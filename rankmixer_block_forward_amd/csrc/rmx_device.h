@@ -15,17 +15,18 @@ struct bf16_t {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);  // NaN stays NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
+// Round to nearest even; NaN stays NaN.  gfx950 converts in one instruction
+// (v_cvt_pk_bf16_f32, two values at a time).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Two bf16 packed in one 32-bit word, element 0 in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return uint16_t(pack_bf16x2(f, 0.f)); }
 
 // ---- 8-element vector access (16 B for bf16, 32 B for fp32); pointers 16 B aligned.
 __device__ __forceinline__ void load8(const float* p, float* v) {
@@ -84,20 +85,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 // erf is evaluated with Abramowitz & Stegun, Handbook of Mathematical Functions, formula
 // 7.1.26 (|error| <= 1.5e-7 for all x >= 0, odd extension for x < 0):
 //   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),  t = 1 / (1 + p x).
-// 1 + erf(x) is formed directly as 2 - q (x >= 0) or q (x < 0), q = poly(t) exp(-x^2), so
-// the left tail keeps its relative accuracy.  Branch-free: one reciprocal, one exp2.
+// With x = |u| / sqrt 2 and q = (1 - erf(x)) / 2 (the a_k halved), Phi(u) = 1 - q for
+// u >= 0 and q for u < 0, so the left tail keeps its relative accuracy.  The 1 / sqrt 2
+// is folded into p and into the exponent: exp(-x^2) = exp2(-u^2 log2(e) / 2).
+// Branch-free: 13 VALU operations, one reciprocal, one exp2.
 __device__ __forceinline__ float gelu_erf(float u) {
-  const float x = u * 0.70710678118654752f;
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, fabsf(u), 1.0f));
+  float poly = fmaf(0.5307027145f, t, -0.7265760135f);
+  poly = fmaf(poly, t, 0.7107068705f);
+  poly = fmaf(poly, t, -0.142248368f);
+  poly = fmaf(poly, t, 0.127414796f);
   poly *= t;
-  const float q = poly * __builtin_amdgcn_exp2f(-(ax * ax) * 1.4426950408889634f);
-  const float one_plus_erf = x >= 0.f ? 2.0f - q : q;
-  return 0.5f * u * one_plus_erf;
+  const float q = poly * __builtin_amdgcn_exp2f((u * -0.72134752044448170f) * u);
+  return u * (u >= 0.f ? 1.0f - q : q);
 }
 
 }  // namespace rmx

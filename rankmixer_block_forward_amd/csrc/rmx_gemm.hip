@@ -270,7 +270,8 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[4][4], float
         const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         st[row * EPI_LD + j * 32 + (lane & 31)] = acc[i][j][r];
       }
-    __syncthreads();
+    // the staging rows are private to this wave, whose LDS operations complete in order
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int pass = 0; pass < 8; ++pass) {
       const int row = pass * 4 + rsub;
@@ -300,8 +301,10 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[4][4], float
         }
       }
     }
-    __syncthreads();
+    asm volatile("" ::: "memory");
   }
+  // every wave is done with its staging rows before the ring memory is reused
+  __syncthreads();
 }
 
 // Dense per-token GEMM: one workgroup per tile, G * ceil(M/256) * ceil(N/256) tiles.
