@@ -39,6 +39,10 @@ def parse():
     p.add_argument("--sweep", action="store_true", help="one line per serving batch size")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-samples", type=int, default=384)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="after the timed region, run the library's token-mixing kernel (a pure "
+                        "permutation copy of the input, bytes known) three times: the reference "
+                        "dispatches for scaling HBM byte counters")
     return p.parse_args()
 
 
@@ -89,7 +93,7 @@ def moe_active_flops(h, X, w, cfg, B):
     return flops, active / gates.numel()
 
 
-def time_forward(cfg, B, steps, warmup):
+def time_forward(cfg, B, steps, warmup, calibrate_copy=False):
     import torch
     import rankmixer_block_forward_amd as rmx
     from rankmixer_block_forward_amd import synth
@@ -103,6 +107,13 @@ def time_forward(cfg, B, steps, warmup):
     h = rmx.Handle.for_config(cfg, max_batch=B)
     out = torch.empty((B, cfg.D), dtype=torch.float32, device="cuda")
     moe = moe_active_flops(h, X, w, cfg, B) if cfg.E > 0 else None
+    calib = []
+    if calibrate_copy:
+        # three 1 GiB sources, written now and cold (out of L2 and the memory-side cache)
+        # by the time they are copied after the timed region
+        Bc = max(1, (1 << 30) // (cfg.T * cfg.D * X.element_size()))
+        calib = [(torch.zeros((Bc, cfg.T, cfg.D), dtype=X.dtype, device="cuda"),
+                  torch.empty((Bc, cfg.T, cfg.D), dtype=X.dtype, device="cuda")) for _ in range(3)]
     for _ in range(warmup):
         h.forward(X, w, out=out)
     torch.cuda.synchronize()
@@ -117,6 +128,14 @@ def time_forward(cfg, B, steps, warmup):
     h.profile_enable(False)
     prof = h.profile_read()
     assert torch.isfinite(out).all().item(), "non-finite output"
+    if calib:
+        for src, dst in calib:
+            rmx.token_mix(src, dst)
+        torch.cuda.synchronize()
+        src = calib[0][0]
+        print(f"[bench] calibration copies: 3 x token mix of {src.numel() * src.element_size()} bytes "
+              f"read and written, cold sources", file=sys.stderr, flush=True)
+        del calib
     h.close()
     return elapsed, prof, moe
 
@@ -194,7 +213,7 @@ def main():
     if args.sweep:
         cfg = synth.SWEEP
     for B in batches:
-        elapsed, prof, moe = time_forward(cfg, B, args.steps, args.warmup)
+        elapsed, prof, moe = time_forward(cfg, B, args.steps, args.warmup, args.calibrate_copy)
         ms = elapsed / args.steps * 1e3
         flops = B * 4.0 * cfg.k * cfg.L * cfg.T * cfg.D * cfg.D if moe is None else moe[0]
         tflops = flops / (ms / 1e3) / 1e12
