@@ -158,6 +158,9 @@ rmx_status validate_config(const rmx_config* c) {
     if (E > MOE_MAX_E || int64_t(c->T) * E > MOE_MAX_GROUPS || int64_t(c->D) * E > MOE_MAX_GATE_WEIGHTS)
       return fail(nullptr, RMX_ERR_UNSUPPORTED, "MoE limits: E <= %d, T*E <= %d, D*E <= %d", MOE_MAX_E,
                   MOE_MAX_GROUPS, MOE_MAX_GATE_WEIGHTS);
+    if (moe_gate_lds_bytes(c->D, E) > MOE_MAX_GATE_LDS)
+      return fail(nullptr, RMX_ERR_UNSUPPORTED, "MoE router weights of one token exceed %zu bytes of LDS",
+                  size_t(MOE_MAX_GATE_LDS));
     if (!gemm_moe_supported(h, c->D, int64_t(c->T) * c->max_batch) ||
         !gemm_moe_supported(c->D, h, c->max_batch))
       return fail(nullptr, RMX_ERR_UNSUPPORTED, "MoE GEMMs need D %% 32 == 0, moe_hidden %% 32 == 0 and slices < 2 GiB");
@@ -290,7 +293,7 @@ rmx_status rmx_create(const rmx_config* cfg, rmx_handle** out_handle) {
   int dev = -1;
   if ((st = check_device_arch(nullptr, &dev)) != RMX_OK) return st;
   hipError_t e;
-  if ((e = rows_init()) != hipSuccess || (e = gemm_init()) != hipSuccess)
+  if ((e = rows_init()) != hipSuccess || (e = gemm_init()) != hipSuccess || (e = moe_init()) != hipSuccess)
     return fail(nullptr, RMX_ERR_HIP, "kernel set-up failed: %s", hipGetErrorString(e));
 
   rmx_handle* h = new (std::nothrow) rmx_handle();

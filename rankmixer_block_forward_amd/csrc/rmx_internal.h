@@ -51,6 +51,7 @@ hipError_t launch_token_mix(int dtype, const void* X, void* Y, int64_t B, int T,
 constexpr int MOE_MAX_E = 16;
 constexpr int MOE_MAX_GROUPS = 1024;          // T * E
 constexpr int MOE_MAX_GATE_WEIGHTS = 16384;   // D * E (router of one token in LDS)
+constexpr size_t MOE_MAX_GATE_LDS = 128 * 1024;  // router LDS (D * E weights, padded)
 constexpr int MOE_TILE_M = 256;               // rows per grouped-GEMM tile
 
 struct MoeArgs {
@@ -71,6 +72,10 @@ struct MoeArgs {
   int B, T, D, E, nchunk;
 };
 
+// Once per process and device (raises the router kernel's LDS limit).
+hipError_t moe_init();
+// LDS bytes of the router kernel for D columns and E experts.
+size_t moe_gate_lds_bytes(int D, int E);
 hipError_t launch_moe_route(const MoeArgs& a, hipStream_t stream);
 hipError_t launch_moe_combine(const MoeArgs& a, hipStream_t stream);
 

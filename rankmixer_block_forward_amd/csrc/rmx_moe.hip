@@ -15,59 +15,92 @@ namespace {
 
 // Gate: g[t][e][b] = max(0, S[t][b] . Wg[t][:, e]) in fp32; counts of active rows per
 // (t, e, 64-row chunk).  Grid (chunks, T), 256 threads: wave w handles rows 16 w .. 16 w + 15
-// of the chunk, one row at a time, each lane taking 8-element pieces of the row.  Wg[t] is
-// staged in LDS transposed to [E][D] so that each lane reads 32 contiguous bytes per expert.
+// of the chunk, 8 rows at a time, each row split over 8 lanes (lane = 8 r + s takes the
+// 8-element pieces s, s + 8, ... of row r: the 8 lanes of a row read 128 contiguous bytes).
+// Wg[t] is staged in LDS as fp32, element (d, e) at (d / 8) * GATE_BLK + (d % 8) * EP + e with
+// EP = E rounded up to 4 (zero padded) and GATE_BLK = 8 EP + 4, so that the 8 pieces read
+// in one step fall in distinct banks.  Partial sums meet over the 8 lanes of a row by
+// butterfly exchange, in a fixed order.
+__host__ __device__ constexpr int gate_ep(int E) { return (E + 3) & ~3; }
+__host__ __device__ constexpr int gate_blk(int E) { return 8 * gate_ep(E) + 4; }
+
+template <int EP>
 __global__ __launch_bounds__(256) void moe_gate_kernel(MoeArgs a) {
-  __shared__ __attribute__((aligned(16))) float wg[MOE_MAX_GATE_WEIGHTS];
+  extern __shared__ __attribute__((aligned(16))) float wg[];
   __shared__ int wave_cnt[4][MOE_MAX_E];
   const int t = blockIdx.y, chunk = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int D = a.D, E = a.E, B = a.B, T = a.T;
+  constexpr int BLK = 8 * EP + 4;
   const bf16_t* Wg = static_cast<const bf16_t*>(a.Wg) + size_t(t) * D * E;
-  for (int i = threadIdx.x; i < D * E; i += blockDim.x) {
-    const int d = i / E, e = i - d * E;
-    wg[e * D + d] = load1(Wg + i);
+  for (int i = threadIdx.x; i < D * EP; i += blockDim.x) {
+    const int d = i / EP, e = i - d * EP;
+    wg[(d >> 3) * BLK + (d & 7) * EP + e] = e < E ? load1(Wg + d * E + e) : 0.f;
   }
   __syncthreads();
-  int my_cnt = 0;  // lane e (< E) counts the active rows of expert e in this wave
-  for (int rr = 0; rr < 16; ++rr) {
-    const int b = chunk * 64 + wave * 16 + rr;
-    if (b >= B) break;  // uniform within the wave
-    const bf16_t* s = static_cast<const bf16_t*>(a.S) + (size_t(t) * B + b) * D;
-    float acc[MOE_MAX_E];
+  const int r = lane >> 3, sl = lane & 7;
+  const int nch = D / 8;
+  int my_cnt[MOE_MAX_E];  // active rows of expert e in this wave (uniform)
 #pragma unroll
-    for (int e = 0; e < MOE_MAX_E; ++e) acc[e] = 0.f;
-    for (int c = lane; c < D / 8; c += 64) {
-      float v[8];
-      load8(s + c * 8, v);
+  for (int e = 0; e < MOE_MAX_E; ++e) my_cnt[e] = 0;
+  for (int grp = 0; grp < 2; ++grp) {
+    const int b = chunk * 64 + wave * 16 + grp * 8 + r;
+    const bool in = b < B;
+    float acc[EP];
 #pragma unroll
-      for (int e = 0; e < MOE_MAX_E; ++e) {
-        if (e < E) {
-          const float4 w0 = *reinterpret_cast<const float4*>(wg + e * D + c * 8);
-          const float4 w1 = *reinterpret_cast<const float4*>(wg + e * D + c * 8 + 4);
-          float r = acc[e];
-          r = fmaf(v[0], w0.x, r); r = fmaf(v[1], w0.y, r); r = fmaf(v[2], w0.z, r); r = fmaf(v[3], w0.w, r);
-          r = fmaf(v[4], w1.x, r); r = fmaf(v[5], w1.y, r); r = fmaf(v[6], w1.z, r); r = fmaf(v[7], w1.w, r);
-          acc[e] = r;
+    for (int e = 0; e < EP; ++e) acc[e] = 0.f;
+    if (in) {
+      const bf16_t* srow = static_cast<const bf16_t*>(a.S) + (size_t(t) * B + b) * D;
+      for (int c = sl; c < nch; c += 8) {
+        float v[8];
+        load8(srow + c * 8, v);
+        const float* wb = wg + c * BLK;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+#pragma unroll
+          for (int e4 = 0; e4 < EP; e4 += 4) {
+            const float4 w = *reinterpret_cast<const float4*>(wb + u * EP + e4);
+            acc[e4 + 0] = fmaf(v[u], w.x, acc[e4 + 0]);
+            acc[e4 + 1] = fmaf(v[u], w.y, acc[e4 + 1]);
+            acc[e4 + 2] = fmaf(v[u], w.z, acc[e4 + 2]);
+            acc[e4 + 3] = fmaf(v[u], w.w, acc[e4 + 3]);
+          }
         }
       }
     }
-    float mine = 0.f;
+    // sum over the 8 lanes of the row (every lane ends with all totals)
 #pragma unroll
-    for (int e = 0; e < MOE_MAX_E; ++e) {
-      if (e < E) {
-        const float tot = wave_sum(acc[e]);
-        if (lane == e) mine = tot;
-      }
+    for (int e = 0; e < EP; ++e) {
+      float x = acc[e];
+      x += __shfl_xor(x, 1, 64);
+      x += __shfl_xor(x, 2, 64);
+      x += __shfl_xor(x, 4, 64);
+      acc[e] = x;
     }
-    if (lane < E) {
-      const float gv = mine > 0.f ? mine : 0.f;
-      a.g[(size_t(t) * E + lane) * B + b] = gv;
-      if (a.gate_out) a.gate_out[(size_t(b) * T + t) * E + lane] = gv;
-      my_cnt += gv > 0.f ? 1 : 0;
+    // lane s of the row writes experts s and s + 8
+#pragma unroll
+    for (int h = 0; h < (EP + 7) / 8; ++h) {
+      const int e = sl + 8 * h;
+      float tot = 0.f;
+#pragma unroll
+      for (int k = 0; k < EP; ++k)
+        if (k == e) tot = acc[k];
+      const float gv = tot > 0.f ? tot : 0.f;
+      const bool act = in && e < E && gv > 0.f;
+      if (in && e < E) {
+        a.g[(size_t(t) * E + e) * B + b] = gv;
+        if (a.gate_out) a.gate_out[(size_t(b) * T + t) * E + e] = gv;
+      }
+      const uint64_t m = __ballot(act);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (8 * h + k < MOE_MAX_E) my_cnt[8 * h + k] += __popcll(m & (0x0101010101010101ull << k));
     }
   }
-  if (lane < E) wave_cnt[wave][lane] = my_cnt;
+  if (lane == 0)
+#pragma unroll
+    for (int e = 0; e < MOE_MAX_E; ++e)
+      if (e < E) wave_cnt[wave][e] = my_cnt[e];
   __syncthreads();
   if (threadIdx.x < E) {
     const int e = threadIdx.x;
@@ -171,8 +204,33 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
 
 }  // namespace
 
+size_t moe_gate_lds_bytes(int D, int E) { return size_t(D / 8) * gate_blk(E) * sizeof(float); }
+
+hipError_t moe_init() {
+  const int bytes = int(MOE_MAX_GATE_LDS);
+  hipError_t e;
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gate_kernel<4>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes)) != hipSuccess)
+    return e;
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gate_kernel<8>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes)) != hipSuccess)
+    return e;
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gate_kernel<12>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes)) != hipSuccess)
+    return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gate_kernel<16>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
 hipError_t launch_moe_route(const MoeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(moe_gate_kernel, dim3(a.nchunk, a.T), dim3(256), 0, stream, a);
+  const size_t lds = moe_gate_lds_bytes(a.D, a.E);
+  const dim3 grid(a.nchunk, a.T);
+  switch (gate_ep(a.E)) {
+    case 4: hipLaunchKernelGGL((moe_gate_kernel<4>), grid, dim3(256), lds, stream, a); break;
+    case 8: hipLaunchKernelGGL((moe_gate_kernel<8>), grid, dim3(256), lds, stream, a); break;
+    case 12: hipLaunchKernelGGL((moe_gate_kernel<12>), grid, dim3(256), lds, stream, a); break;
+    default: hipLaunchKernelGGL((moe_gate_kernel<16>), grid, dim3(256), lds, stream, a); break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, stream, a);

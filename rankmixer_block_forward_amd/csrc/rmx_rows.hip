@@ -37,14 +37,14 @@ __device__ __forceinline__ void storew(T* p, const float* v) {
   }
 }
 
-// LayerNorm of one row held as v[MAXC][W] by the 64 lanes of a wave (chunk c = lane + 64 i),
+// LayerNorm of one row held as v[NC][W] by the 64 lanes of a wave (chunk c = lane + 64 i),
 // in place: v = gamma * (v - mu) / sqrt(var + eps) + beta.
-template <int W, int MAXC, typename T>
-__device__ __forceinline__ void wave_layernorm(float (&v)[MAXC][W], int lane, int nchunks, int D,
+template <int W, int NC, typename T>
+__device__ __forceinline__ void wave_layernorm(float (&v)[NC][W], int lane, int nchunks, int D,
                                                const T* gamma, const T* beta, float eps) {
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
+  for (int i = 0; i < NC; ++i) {
     const int c = lane + 64 * i;
     if (c < nchunks) {
 #pragma unroll
@@ -54,7 +54,7 @@ __device__ __forceinline__ void wave_layernorm(float (&v)[MAXC][W], int lane, in
   const float mu = wave_sum(s) / float(D);
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
+  for (int i = 0; i < NC; ++i) {
     const int c = lane + 64 * i;
     if (c < nchunks) {
 #pragma unroll
@@ -67,7 +67,7 @@ __device__ __forceinline__ void wave_layernorm(float (&v)[MAXC][W], int lane, in
   const float var = wave_sum(ss) / float(D);
   const float rstd = 1.0f / sqrtf(var + eps);
 #pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
+  for (int i = 0; i < NC; ++i) {
     const int c = lane + 64 * i;
     if (c < nchunks) {
       float g[W], bt[W];
@@ -79,10 +79,41 @@ __device__ __forceinline__ void wave_layernorm(float (&v)[MAXC][W], int lane, in
   }
 }
 
-template <typename T, int W, int MODE>
-__global__ __launch_bounds__(512) void rows_kernel(RowsArgs a) {
+// One block input row (token t of sample b) into registers: X0[b, t] (first block) or the
+// previous block's pre-LN2 row Y[t, b] (fp32).
+template <typename T, int W, int NC, int MODE>
+__device__ __forceinline__ void load_row(const RowsArgs& a, int b, int t, int lane, int nchunks,
+                                         float (&v)[NC][W]) {
+  if constexpr (MODE == ROWS_FIRST) {
+    const T* src = static_cast<const T*>(a.in) + (size_t(b) * a.T + t) * a.D;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunks) loadw<W>(src + c * W, v[i]);
+    }
+  } else {
+    const float* src = static_cast<const float*>(a.in) + (size_t(t) * a.B + b) * a.D;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunks) loadw<W>(src + c * W, v[i]);
+    }
+  }
+}
+
+// NC = chunks of W columns per lane (ceil(D / (64 W))).  Up to rows_max_waves waves per
+// sample; each
+// wave walks its tokens with the next row's loads in flight while the current one is
+// normalized.
+// Waves per sample: 16, or 8 where the registers of a wide row (or the pool's partial sums)
+// need the room.
+constexpr int rows_max_waves(int NC, int MODE) {
+  return MODE == ROWS_FINAL ? (NC > 4 ? 4 : 8) : (NC > 3 ? 8 : 16);
+}
+
+template <typename T, int W, int NC, int MODE>
+__global__ __launch_bounds__(64 * rows_max_waves(NC, MODE)) void rows_kernel(RowsArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  constexpr int MAXC = (W == 8) ? ROWS_MAX_D / (64 * 8) : ROWS_MAX_D_SCALAR / 64;
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -92,36 +123,33 @@ __global__ __launch_bounds__(512) void rows_kernel(RowsArgs a) {
   const int nchunks = D / W;
   T* xs = reinterpret_cast<T*>(smem_raw);  // [T][D] rows of sample b (FIRST / MID)
 
-  float pacc[MAXC][W];
+  float pacc[MODE == ROWS_FINAL ? NC : 1][W];
 #pragma unroll
-  for (int i = 0; i < MAXC; ++i)
+  for (int i = 0; i < (MODE == ROWS_FINAL ? NC : 1); ++i)
 #pragma unroll
     for (int e = 0; e < W; ++e) pacc[i][e] = 0.f;
 
   // Phase A: the block input rows X[b, t, :] for t = wave, wave + nw, ...
+  float nxt[NC][W];
+  if (wave < Tn) load_row<T, W, NC, MODE>(a, b, wave, lane, nchunks, nxt);
   for (int t = wave; t < Tn; t += nw) {
-    float v[MAXC][W];
-    if constexpr (MODE == ROWS_FIRST) {
-      const T* src = static_cast<const T*>(a.in) + (size_t(b) * Tn + t) * D;
+    float v[NC][W];
 #pragma unroll
-      for (int i = 0; i < MAXC; ++i) {
+    for (int i = 0; i < NC; ++i)
+#pragma unroll
+      for (int e = 0; e < W; ++e) v[i][e] = nxt[i][e];
+    if (t + nw < Tn) load_row<T, W, NC, MODE>(a, b, t + nw, lane, nchunks, nxt);
+    if constexpr (MODE == ROWS_FIRST) {
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
         const int c = lane + 64 * i;
-        if (c < nchunks) {
-          loadw<W>(src + c * W, v[i]);
-          storew<W>(xs + t * D + c * W, v[i]);
-        }
+        if (c < nchunks) storew<W>(xs + t * D + c * W, v[i]);
       }
     } else {
-      const float* src = static_cast<const float*>(a.in) + (size_t(t) * B + b) * D;
+      wave_layernorm<W, NC>(v, lane, nchunks, D, static_cast<const T*>(a.ln2_g),
+                            static_cast<const T*>(a.ln2_b), a.eps);
 #pragma unroll
-      for (int i = 0; i < MAXC; ++i) {
-        const int c = lane + 64 * i;
-        if (c < nchunks) loadw<W>(src + c * W, v[i]);
-      }
-      wave_layernorm<W, MAXC>(v, lane, nchunks, D, static_cast<const T*>(a.ln2_g),
-                              static_cast<const T*>(a.ln2_b), a.eps);
-#pragma unroll
-      for (int i = 0; i < MAXC; ++i) {
+      for (int i = 0; i < NC; ++i) {
         const int c = lane + 64 * i;
         if (c < nchunks) {
           if constexpr (MODE == ROWS_MID) {
@@ -140,7 +168,7 @@ __global__ __launch_bounds__(512) void rows_kernel(RowsArgs a) {
     // Mean pool: per-wave partial sums meet in LDS, then sum over waves in wave order.
     float* red = reinterpret_cast<float*>(smem_raw);  // [nw][D]
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
+    for (int i = 0; i < NC; ++i) {
       const int c = lane + 64 * i;
       if (c < nchunks)
 #pragma unroll
@@ -158,9 +186,9 @@ __global__ __launch_bounds__(512) void rows_kernel(RowsArgs a) {
   __syncthreads();
   // Phase B: output rows h = wave, wave + nw, ...:  S[h] = LN1(X[h] + mix(X)[h]).
   for (int h = wave; h < Tn; h += nw) {
-    float r[MAXC][W];
+    float r[NC][W];
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
+    for (int i = 0; i < NC; ++i) {
       const int c = lane + 64 * i;
       if (c < nchunks) {
         const int col = c * W;
@@ -173,11 +201,11 @@ __global__ __launch_bounds__(512) void rows_kernel(RowsArgs a) {
         for (int e = 0; e < W; ++e) r[i][e] = own[e] + mixed[e];
       }
     }
-    wave_layernorm<W, MAXC>(r, lane, nchunks, D, static_cast<const T*>(a.ln1_g),
-                            static_cast<const T*>(a.ln1_b), a.eps);
+    wave_layernorm<W, NC>(r, lane, nchunks, D, static_cast<const T*>(a.ln1_g),
+                          static_cast<const T*>(a.ln1_b), a.eps);
     T* dst = static_cast<T*>(a.S) + (size_t(h) * B + b) * D;
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
+    for (int i = 0; i < NC; ++i) {
       const int c = lane + 64 * i;
       if (c < nchunks) storew<W>(dst + c * W, r[i]);
     }
@@ -209,9 +237,10 @@ __global__ __launch_bounds__(256) void token_mix_kernel(const T* __restrict__ X,
   }
 }
 
-template <typename T, int W>
-hipError_t launch_rows_t(int mode, const RowsArgs& a, hipStream_t stream) {
-  int nw = a.T < 8 ? a.T : 8;
+template <typename T, int W, int NC>
+hipError_t launch_rows_nc(int mode, const RowsArgs& a, hipStream_t stream) {
+  const int maxw = rows_max_waves(NC, mode);
+  int nw = a.T < maxw ? a.T : maxw;
   size_t lds;
   if (mode == ROWS_FINAL) {
     while (nw > 1 && size_t(nw) * a.D * 4 > 64 * 1024) --nw;
@@ -222,29 +251,62 @@ hipError_t launch_rows_t(int mode, const RowsArgs& a, hipStream_t stream) {
   dim3 grid(a.B), block(64 * nw);
   switch (mode) {
     case ROWS_FIRST:
-      hipLaunchKernelGGL((rows_kernel<T, W, ROWS_FIRST>), grid, block, lds, stream, a);
+      hipLaunchKernelGGL((rows_kernel<T, W, NC, ROWS_FIRST>), grid, block, lds, stream, a);
       break;
     case ROWS_MID:
-      hipLaunchKernelGGL((rows_kernel<T, W, ROWS_MID>), grid, block, lds, stream, a);
+      hipLaunchKernelGGL((rows_kernel<T, W, NC, ROWS_MID>), grid, block, lds, stream, a);
       break;
     default:
-      hipLaunchKernelGGL((rows_kernel<T, W, ROWS_FINAL>), grid, block, lds, stream, a);
+      hipLaunchKernelGGL((rows_kernel<T, W, NC, ROWS_FINAL>), grid, block, lds, stream, a);
       break;
   }
   return hipGetLastError();
 }
 
+// chunks per lane: ceil(D / (64 W)); the scalar path (small D) always takes 8
 template <typename T, int W>
-hipError_t set_rows_lds_limit() {
+hipError_t launch_rows_t(int mode, const RowsArgs& a, hipStream_t stream) {
+  if constexpr (W == 1) {
+    return launch_rows_nc<T, 1, ROWS_MAX_D_SCALAR / 64>(mode, a, stream);
+  } else {
+    switch ((a.D / W + 63) / 64) {
+      case 1: return launch_rows_nc<T, W, 1>(mode, a, stream);
+      case 2: return launch_rows_nc<T, W, 2>(mode, a, stream);
+      case 3: return launch_rows_nc<T, W, 3>(mode, a, stream);
+      case 4: return launch_rows_nc<T, W, 4>(mode, a, stream);
+      case 5: return launch_rows_nc<T, W, 5>(mode, a, stream);
+      case 6: return launch_rows_nc<T, W, 6>(mode, a, stream);
+      case 7: return launch_rows_nc<T, W, 7>(mode, a, stream);
+      default: return launch_rows_nc<T, W, 8>(mode, a, stream);
+    }
+  }
+}
+
+template <typename T, int W, int NC>
+hipError_t set_rows_lds_limit_nc() {
   const int bytes = int(ROWS_MAX_LDS);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_kernel<T, W, ROWS_FIRST>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_kernel<T, W, NC, ROWS_FIRST>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_kernel<T, W, ROWS_MID>),
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_kernel<T, W, NC, ROWS_MID>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_kernel<T, W, ROWS_FINAL>),
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_kernel<T, W, NC, ROWS_FINAL>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <typename T>
+hipError_t set_rows_lds_limit() {
+  hipError_t e;
+  if ((e = set_rows_lds_limit_nc<T, 1, ROWS_MAX_D_SCALAR / 64>()) != hipSuccess) return e;
+  if ((e = set_rows_lds_limit_nc<T, 8, 1>()) != hipSuccess) return e;
+  if ((e = set_rows_lds_limit_nc<T, 8, 2>()) != hipSuccess) return e;
+  if ((e = set_rows_lds_limit_nc<T, 8, 3>()) != hipSuccess) return e;
+  if ((e = set_rows_lds_limit_nc<T, 8, 4>()) != hipSuccess) return e;
+  if ((e = set_rows_lds_limit_nc<T, 8, 5>()) != hipSuccess) return e;
+  if ((e = set_rows_lds_limit_nc<T, 8, 6>()) != hipSuccess) return e;
+  if ((e = set_rows_lds_limit_nc<T, 8, 7>()) != hipSuccess) return e;
+  return set_rows_lds_limit_nc<T, 8, 8>();
 }
 
 }  // namespace
@@ -254,11 +316,9 @@ bool rows_vectorized(int T, int D) { return D % 8 == 0 && (D / T) % 8 == 0; }
 size_t rows_lds_bytes(int dtype, int T, int D) { return size_t(T) * D * dtype_size(dtype); }
 
 hipError_t rows_init() {
-  hipError_t e;
-  if ((e = set_rows_lds_limit<float, 8>()) != hipSuccess) return e;
-  if ((e = set_rows_lds_limit<float, 1>()) != hipSuccess) return e;
-  if ((e = set_rows_lds_limit<bf16_t, 8>()) != hipSuccess) return e;
-  return set_rows_lds_limit<bf16_t, 1>();
+  hipError_t e = set_rows_lds_limit<float>();
+  if (e != hipSuccess) return e;
+  return set_rows_lds_limit<bf16_t>();
 }
 
 hipError_t launch_rows(int dtype, int mode, const RowsArgs& a, hipStream_t stream) {
