@@ -50,6 +50,7 @@ constexpr int STAGE_BYTES = A_STAGE_BYTES + BK * BN * 2;   // + 16 KB, rows of 5
 constexpr int MFMA_THREADS = 256;
 constexpr int EPI_LD = 132;        // fp32 row stride of the epilogue staging tile
 constexpr int NUM_XCD = 8;         // MI355X: 8 accelerator complex dies, each with its own L2
+constexpr int TILE_BAND = 8;       // row tiles per band of the dense tile order
 
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
@@ -60,8 +61,9 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 // Workgroups are dealt to the XCDs round-robin.  Remap so that each XCD receives a
-// contiguous range of tile indices, and order tiles M-fastest within a token so that the
-// tiles resident on one XCD at a time share their weight panels and A rows in its L2.
+// contiguous range of tile indices, and order tiles M-fastest within bands of row tiles of
+// a token so that the tiles resident on one XCD at a time share their weight panels and A
+// rows in its L2.
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   const int xcd = bid % NUM_XCD, pos = bid / NUM_XCD;
   const int base = nblocks / NUM_XCD, extra = nblocks % NUM_XCD;
@@ -320,7 +322,13 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int g = id / (nMt * nNt);
   const int rem = id - g * nMt * nNt;
-  const int nt = rem / nMt, mt = rem - nt * nMt;
+  // Within a token, tiles run over bands of TILE_BAND row tiles: M-fastest inside a band,
+  // then N, then the next band, so the tiles resident on one XCD at a time form a compact
+  // block whatever the batch size.
+  const int band = rem / (TILE_BAND * nNt);
+  const int in_band = rem - band * TILE_BAND * nNt;
+  const int bm = min(TILE_BAND, nMt - band * TILE_BAND);
+  const int nt = in_band / bm, mt = band * TILE_BAND + (in_band - (in_band / bm) * bm);
   const int m0 = mt * BM, n0 = nt * BN;
 
   // Slices are < 2^31 bytes (checked at launch); an offset equal to the slice size is out
