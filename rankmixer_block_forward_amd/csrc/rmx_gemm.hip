@@ -80,13 +80,17 @@ struct Frags {
   u32x2_t b[8];  // W columns of the 4 column blocks: k 0..3 and 4..7, 4 bf16 each
 };
 
-// MFMA 32x32x16 operand layout: lane l supplies row (l % 32) of A and column (l % 32) of
-// B, each with the 8 consecutive k at 8 (l / 32) of the 16-k sub-step.
+// MFMA 32x32x16 operand layout: lane l supplies row (l % 32) of the first operand and
+// column (l % 32) of the second, each with the 8 consecutive k at 8 (l / 32) of the 16-k
+// sub-step; lane l, register r of the result holds row 8 (r / 4) + 4 (l / 32) + r % 4,
+// column l % 32.  The W fragment goes first, so each block holds the transposed product:
+// lane l owns output row l % 32 of the block and, in registers 4 g .. 4 g + 3, the four
+// consecutive output columns 8 g + 4 (l / 32) .. + 3.
 __device__ __forceinline__ void mfma_block(f32x16_t (&acc)[4][4], const Frags& f, int i, int j) {
   const bf16x8_t a = __builtin_bit_cast(bf16x8_t, f.a[i]);
   u32x2_t both[2] = {f.b[2 * j], f.b[2 * j + 1]};
   const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(both);
-  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i][j], 0, 0, 0);
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc[i][j], 0, 0, 0);
 }
 
 // Buffer descriptor over [base, base + bytes), built from wave-uniform values so that it
@@ -243,10 +247,11 @@ __device__ __forceinline__ void mfma_tile(f32x16_t (&acc)[4][4], const TileSrc& 
   __syncthreads();
 }
 
-// Epilogue of one tile.  Accumulator layout of a 32 x 32 block: lane l, register r holds
-// row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.  Each wave stages 32 rows x 128
-// columns at a time through LDS so that every lane then owns 8 consecutive columns of one
-// row: 16-byte global stores, and coalesced bias / residual loads.  `out_row(m)` is the
+// Epilogue of one tile.  Accumulator layout of a 32 x 32 block (transposed product): lane
+// l holds row l % 32 and, in register 4 g + e, column 8 g + 4 (l / 32) + e.  Each wave
+// stages 32 rows x 128 columns at a time through LDS (16-byte writes) so that every lane
+// then owns 8 consecutive columns of one row: 16-byte global stores, and coalesced bias /
+// residual loads.  `out_row(m)` is the
 // output row of tile row m, or -1 if it does not exist.
 template <int EPI, typename OutRow>
 __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[4][4], float* smem_f, const GemmArgs& p,
@@ -268,9 +273,10 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[4][4], float
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        st[row * EPI_LD + j * 32 + (lane & 31)] = acc[i][j][r];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 v = make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                                     acc[i][j][4 * g4 + 3]);
+        *reinterpret_cast<float4*>(st + (lane & 31) * EPI_LD + j * 32 + 8 * g4 + 4 * (lane >> 5)) = v;
       }
     // the staging rows are private to this wave, whose LDS operations complete in order
     asm volatile("" ::: "memory");
