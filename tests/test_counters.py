@@ -1,0 +1,51 @@
+"""Host logic of the HBM traffic record (rankmixer_block_forward_amd/counters.py): the
+calibration scale comes from the copy dispatches and is applied per kernel."""
+import csv
+import json
+
+from rankmixer_block_forward_amd import counters
+
+
+def _write(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (k, c, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+
+
+def test_record_scales_by_copy_calibration(tmp_path):
+    g1 = "void rmx::(anonymous namespace)::gemm_bf16_mfma<0>(rmx::GemmArgs)"
+    g2 = "void rmx::(anonymous namespace)::gemm_bf16_mfma<1>(rmx::GemmArgs)"
+    cp = "void rmx::(anonymous namespace)::token_mix_kernel<rmx::bf16_t, 8>(rmx::bf16_t const*, ...)"
+    other = "void at::native::vectorized_elementwise_kernel<4>(...)"
+    copy_bytes = 1 << 30
+    # the fetch counter reads 5/6 of the copy, the write counter all of it
+    _write(tmp_path / "f.csv", [(cp, "FETCH_SIZE", copy_bytes / 1024 * 5 / 6)] * 3 +
+           [(g1, "FETCH_SIZE", 1000.0), (g1, "FETCH_SIZE", 3000.0), (g2, "FETCH_SIZE", 600.0),
+            (other, "FETCH_SIZE", 1e9)])
+    _write(tmp_path / "w.csv", [(cp, "WRITE_SIZE", copy_bytes / 1024)] * 3 +
+           [(g1, "WRITE_SIZE", 500.0), (g1, "WRITE_SIZE", 500.0), (g2, "WRITE_SIZE", 100.0)])
+    rec = counters.build_record(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "w B=1", copy_bytes)
+    assert abs(rec["calibration"]["fetch_scale"] - 1.2) < 1e-4
+    assert abs(rec["calibration"]["write_scale"] - 1.0) < 1e-9
+    k1 = rec["kernels"]["gemm1_gelu"]
+    assert k1["fetch_bytes"] == round(2000.0 * 1024 * 1.2)      # mean of the two dispatches, scaled
+    assert k1["write_bytes"] == 500 * 1024
+    assert k1["bytes_per_launch"] == k1["fetch_bytes"] + k1["write_bytes"]
+    assert rec["kernels"]["gemm2_residual"]["fetch_bytes"] == round(600.0 * 1024 * 1.2)
+    assert set(rec["kernels"]) == {"gemm1_gelu", "gemm2_residual"}
+    assert rec["gemm_source_sha256_16"] == counters.gemm_hash()
+    json.dumps(rec)
+
+
+def test_committed_record_is_well_formed():
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles",
+                        "traffic_counters.json")
+    with open(path) as f:
+        rec = json.load(f)
+    assert rec["calibration"]["copy_bytes_each_way"] > 0
+    for k, e in rec["kernels"].items():
+        assert e["bytes_per_launch"] == e["fetch_bytes"] + e["write_bytes"] or \
+            abs(e["bytes_per_launch"] - e["fetch_bytes"] - e["write_bytes"]) <= 1
