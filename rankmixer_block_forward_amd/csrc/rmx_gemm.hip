@@ -48,9 +48,9 @@ constexpr int BM = 256, BN = 256, BK = 32, NS = 4;
 constexpr int A_STAGE_BYTES = BM * BK * 2;                 // 16 KB, rows of 64 B
 constexpr int STAGE_BYTES = A_STAGE_BYTES + BK * BN * 2;   // + 16 KB, rows of 512 B
 constexpr int MFMA_THREADS = 256;
-constexpr int EPI_LD = 132;        // fp32 row stride of the epilogue staging tile
 constexpr int NUM_XCD = 8;         // MI355X: 8 accelerator complex dies, each with its own L2
 constexpr int TILE_BAND = 8;       // row tiles per band of the dense tile order
+
 
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
@@ -247,21 +247,25 @@ __device__ __forceinline__ void mfma_tile(f32x16_t (&acc)[4][4], const TileSrc& 
   __syncthreads();
 }
 
-// Epilogue of one tile.  Accumulator layout of a 32 x 32 block (transposed product): lane
-// l holds row l % 32 and, in register 4 g + e, column 8 g + 4 (l / 32) + e.  Each wave
-// stages 32 rows x 128 columns at a time through LDS (16-byte writes) so that every lane
-// then owns 8 consecutive columns of one row: 16-byte global stores, and coalesced bias /
-// residual loads.  `out_row(m)` is the
-// output row of tile row m, or -1 if it does not exist.
-template <int EPI, typename OutRow>
-__device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[4][4], float* smem_f, const GemmArgs& p,
-                                              const bf16_t* bias_g, int n0, int wave, int lane, OutRow out_row) {
+// Epilogue of one tile: the wave's NI x NJ blocks of 32 x 32, whose top-left element is
+// tile row wrow0, tile column wcol0 (n0 + wcol0 in the output).  Accumulator layout of a
+// block (transposed product): lane l holds row l % 32 and, in register 4 g + e, column
+// 8 g + 4 (l / 32) + e.  Each wave stages 32 rows x 32 NJ columns at a time through LDS
+// (16-byte writes) so that every lane then owns 8 consecutive columns of one row: 16-byte
+// global stores, and coalesced bias / residual loads.  `out_row(m)` is the output row of
+// tile row m, or -1 if it does not exist.
+template <int EPI, int NI, int NJ, typename OutRow>
+__device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], float* smem_f, const GemmArgs& p,
+                                              const bf16_t* bias_g, int n0, int wrow0, int wcol0, int wave,
+                                              int lane, OutRow out_row) {
+  constexpr int LD = NJ * 32 + 4;     // fp32 row stride of the staging rows
+  constexpr int LPR = NJ * 4;         // lanes per staged row (8 columns each)
+  constexpr int RPP = 64 / LPR;       // rows per pass
   const int N = p.N;
-  const int wm = wave >> 1, wn = wave & 1;
-  float* st = smem_f + wave * 32 * EPI_LD;
-  const int col8 = (lane & 15) * 8;
-  const int rsub = lane >> 4;
-  const int n = n0 + wn * 128 + col8;
+  float* st = smem_f + wave * 32 * LD;
+  const int col8 = (lane % LPR) * 8;
+  const int rsub = lane / LPR;
+  const int n = n0 + wcol0 + col8;
   const bool n_ok = n < N;
   float bias[8];
 #pragma unroll
@@ -269,24 +273,24 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[4][4], float
   if (bias_g && n_ok) load8(bias_g + n, bias);
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const float4 v = make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
                                      acc[i][j][4 * g4 + 3]);
-        *reinterpret_cast<float4*>(st + (lane & 31) * EPI_LD + j * 32 + 8 * g4 + 4 * (lane >> 5)) = v;
+        *reinterpret_cast<float4*>(st + (lane & 31) * LD + j * 32 + 8 * g4 + 4 * (lane >> 5)) = v;
       }
     // the staging rows are private to this wave, whose LDS operations complete in order
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int pass = 0; pass < 8; ++pass) {
-      const int row = pass * 4 + rsub;
-      const int orow = out_row(wm * 128 + i * 32 + row);
+    for (int pass = 0; pass < 32 / RPP; ++pass) {
+      const int row = pass * RPP + rsub;
+      const int orow = out_row(wrow0 + i * 32 + row);
       float v[8];
-      const float4 x0 = *reinterpret_cast<const float4*>(st + row * EPI_LD + col8);
-      const float4 x1 = *reinterpret_cast<const float4*>(st + row * EPI_LD + col8 + 4);
+      const float4 x0 = *reinterpret_cast<const float4*>(st + row * LD + col8);
+      const float4 x1 = *reinterpret_cast<const float4*>(st + row * LD + col8 + 4);
       v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
       v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
       if (orow >= 0 && n_ok) {
@@ -351,8 +355,8 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
   f32x16_t acc[4][4];
   mfma_tile(acc, ts, smem, lds0, K, N, wave, lane);
   const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
-  tile_epilogue<EPI>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, wave, lane,
-                     [&](int m) { return m0 + m < M ? g * M + m0 + m : -1; });
+  tile_epilogue<EPI, 4, 4>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, (wave >> 1) * 128,
+                           (wave & 1) * 128, wave, lane, [&](int m) { return m0 + m < M ? g * M + m0 + m : -1; });
 }
 
 // Sparse-MoE grouped GEMM.  Group g has rows group_start[g] .. group_start[g+1]-1 of the
@@ -415,9 +419,151 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_moe(GemmArgs p) {
     f32x16_t acc[4][4];
     mfma_tile(acc, ts, smem, lds0, K, N, wave, lane);
     const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
-    tile_epilogue<EPI>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, wave, lane,
-                       [&](int m) { return m0 + m < rows ? row0 + m0 + m : -1; });
+    tile_epilogue<EPI, 4, 4>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, (wave >> 1) * 128,
+                             (wave & 1) * 128, wave, lane, [&](int m) { return m0 + m < rows ? row0 + m0 + m : -1; });
   }
+}
+
+// ----------------------------------------------------------- small-batch kernel
+// Tiles of 64 rows x 256 columns for few rows per token (serving batches): the weight
+// panel dominates the bytes, and a 256-row tile would spend three quarters of its MFMA
+// work on rows that do not exist.  4 waves side by side, each 64 x 64 (2 x 2 blocks);
+// K steps of 32 through a 4-stage ring of 20 KB (A 64 x 32, W 32 x 256), so two workgroups
+// share a CU and their copy streams overlap.  Same copy, swizzle and wait scheme as the
+// 256 x 256 kernel: 5 loads per wave per K step (1 of A, 4 of W).
+constexpr int SM_BM = 64;
+constexpr int SM_A_BYTES = SM_BM * BK * 2;                 // 4 KB, rows of 64 B
+constexpr int SM_STAGE_BYTES = SM_A_BYTES + BK * BN * 2;   // + 16 KB
+constexpr int SM_COPIES = 5;
+
+template <int EPI>
+__global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[NS * SM_STAGE_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_g;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nMt = (M + SM_BM - 1) / SM_BM, nNt = (N + BN - 1) / BN;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = id / (nMt * nNt);
+  const int rem = id - g * nMt * nNt;
+  const int nt = rem / nMt, mt = rem - nt * nMt;
+  const int m0 = mt * SM_BM, n0 = nt * BN;
+
+  const uint32_t bytesA = uint32_t(M) * uint32_t(K) * 2u, bytesW = uint32_t(K) * uint32_t(N) * 2u;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(g) * M * K, bytesA);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * K * N, bytesW);
+  // copy 0: A rows 16 w .. 16 w + 15 (lane q takes chunk q % 4 of row q / 4, swizzled);
+  // copies 1..4: W k rows 8 w + 2 (c - 1) and +1, as in the 256 x 256 kernel
+  uint32_t offA, offW[4];
+  {
+    const int r = 16 * wave + (lane >> 2);
+    const int c = (lane & 3) ^ swz_a(r);
+    offA = (m0 + r < M) ? uint32_t(m0 + r) * uint32_t(K) * 2u + uint32_t(c * 16) : bytesA;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int kr = 8 * wave + 2 * a + (lane >> 5);
+      const int col = n0 + (((lane & 31) ^ swz_w(kr)) * 8);
+      offW[a] = col < N ? (uint32_t(kr) * uint32_t(N) + uint32_t(col)) * 2u : bytesW;
+    }
+  }
+  const int nk = K / BK;
+  auto copy = [&](int kt, int stage, int q) {
+    kt = kt < nk ? kt : nk - 1;
+    const uint32_t sbase = lds0 + uint32_t(stage) * SM_STAGE_BYTES;
+    if (q == 0) {
+      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + uint32_t(16 * wave) * 64u), offA, rA, kt * BK * 2);
+    } else {
+      const uint32_t dst =
+          __builtin_amdgcn_readfirstlane(sbase + SM_A_BYTES + uint32_t(8 * wave + 2 * (q - 1)) * 512u);
+      copy_to_lds(dst, offW[q - 1], rW, kt * BK * N * 2);
+    }
+  };
+
+  uint32_t aoff[2][2], boff[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = i * 32 + (lane & 31);
+      const int c = kk * 2 + (lane >> 5);
+      aoff[kk][i] = uint32_t(m * 64 + ((c ^ swz_a(m)) << 4));
+    }
+  {
+    const int kb = 8 * (lane >> 5) + ((lane & 15) >> 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = wave * 64 + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      boff[j] = uint32_t(SM_A_BYTES + kb * 512 + (((n >> 3) ^ swz_w(kb)) << 4) + (n & 7) * 2);
+    }
+  }
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  struct SmFrags {
+    u32x4_t a[2];
+    u32x2_t b[4];
+  };
+  auto read_frags = [&](SmFrags& f, const lds_u8* sp, int kk) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f.a[i] = *reinterpret_cast<const lds_u32x4*>(sp + aoff[kk][i]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const lds_u8* q = sp + boff[j] + kk * 16 * 512;
+      f.b[2 * j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)q));
+      f.b[2 * j + 1] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * 512)));
+    }
+  };
+  f32x16_t acc[2][2];
+  auto mfma4 = [&](const SmFrags& f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x2_t both[2] = {f.b[2 * j], f.b[2 * j + 1]};
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(both),
+                                                            __builtin_bit_cast(bf16x8_t, f.a[i]), acc[i][j], 0, 0, 0);
+      }
+  };
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Prologue: K steps 0..NS-1; wait for step 0 (SM_COPIES loads per step).
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+#pragma unroll
+    for (int q = 0; q < SM_COPIES; ++q) copy(st, st, q);
+  asm volatile("s_waitcnt vmcnt(15)\n\ts_barrier" ::: "memory");
+  SmFrags f0, f1;
+  read_frags(f0, smem, 0);
+  int stage = 0;
+  for (int it = 0; it < nk; ++it) {
+    const lds_u8* sp = smem + stage * SM_STAGE_BYTES;
+    const int nstage = stage + 1 == NS ? 0 : stage + 1;
+    read_frags(f1, sp, 1);
+    mfma4(f0);
+    // step it+1 visible (the loads of the two steps after it may be outstanding); this
+    // stage free for step it+NS
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(f0, smem + nstage * SM_STAGE_BYTES, 0);
+    mfma4(f1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < SM_COPIES; ++q) copy(it + NS, stage, q);
+    __builtin_amdgcn_sched_barrier(0);
+    stage = nstage;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
+  tile_epilogue<EPI, 2, 2>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, 0, wave * 64, wave, lane,
+                           [&](int m) { return m0 + m < M ? g * M + m0 + m : -1; });
 }
 
 // --------------------------------------------------------------- generic kernel
@@ -511,6 +657,14 @@ hipError_t launch_gemm_moe(int epi, const GemmArgs& a, hipStream_t stream) {
 
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t stream) {
   if (a.G == 0 || a.M == 0 || a.N == 0) return hipSuccess;
+  if (gemm_uses_mfma(dtype, a.M, a.N, a.K) && a.M <= GEMM_SMALL_M) {
+    const int tiles = a.G * ((a.M + SM_BM - 1) / SM_BM) * ((a.N + BN - 1) / BN);
+    if (epi == EPI_GELU)
+      hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_GELU>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_RESID>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+    return hipGetLastError();
+  }
   if (gemm_uses_mfma(dtype, a.M, a.N, a.K)) {
     const int tiles = a.G * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (epi == EPI_GELU)

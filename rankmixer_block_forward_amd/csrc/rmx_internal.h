@@ -103,6 +103,8 @@ struct GemmArgs {
   const float* row_gate;
   int a_rows;  // EPI_MOE1: rows of A (T * B)
 };
+// Rows per token up to which the dense launch uses 64-row tiles.
+constexpr int GEMM_SMALL_M = 64;
 
 // True when the bf16 MFMA kernel handles this shape (else the generic kernel runs).
 bool gemm_uses_mfma(int dtype, int M, int N, int K);

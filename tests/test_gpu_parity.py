@@ -82,8 +82,11 @@ def test_zero_token_rows_fp32():
 @pytest.mark.parametrize("B,T,D,k,L", [
     (300, 4, 256, 4, 2),   # MFMA path: 2 M tiles (ragged), 4 N tiles in GEMM1
     (77, 5, 320, 2, 1),    # MFMA path, ragged N tiles (640 = 2.5 x 256, 320 = 1.25 x 256)
-    (50, 4, 96, 2, 2),     # K = 96 not a multiple of 64: generic kernel in bf16
-    (1, 16, 768, 4, 2),    # one sample at the 100M width
+    (50, 4, 96, 2, 2),     # 64-row tiles, odd K-step count (K = 96)
+    (50, 5, 40, 2, 2),     # K = 40 not a multiple of 32: generic kernel in bf16
+    (1, 16, 768, 4, 2),    # one sample at the 100M width (64-row tiles)
+    (64, 8, 512, 4, 1),    # largest batch on the 64-row tiles
+    (65, 8, 512, 4, 1),    # smallest batch on the 256-row tiles
     (513, 16, 768, 4, 1),  # one row past a tile boundary
 ])
 def test_bf16_shapes(B, T, D, k, L):
@@ -112,6 +115,18 @@ def test_bf16_deterministic():
 
 
 # ------------------------------------------------------- full-size workloads
+
+def test_small_batch_deterministic():
+    """Few rows per token (64-row tiles): two runs agree bit for bit, and match the oracle."""
+    cfg = synth.Config("small", B=33, T=8, D=256, k=4, L=2, dtype="bf16", bias_std=0.05)
+    inp = synth.make_inputs(cfg, seed=21)
+    o1, xl1 = run_gpu(cfg, inp)
+    o2, xl2 = run_gpu(cfg, inp)
+    assert np.array_equal(o1, o2) and np.array_equal(xl1, xl2)
+    rows = sample_rows(cfg.B, 33)
+    o_ref, xl_ref = run_oracle(cfg, inp, rows)
+    check(cfg, o1[rows], xl1[rows], o_ref, xl_ref, "bf16 B=33")
+
 
 def test_rankmixer_100m_full_size():
     cfg = synth.M100
