@@ -39,6 +39,10 @@ def parse():
     p.add_argument("--sweep", action="store_true", help="one line per serving batch size")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-samples", type=int, default=384)
+    p.add_argument("--library-reference", action="store_true",
+                   help="time the vendor library's bf16 GEMM (torch.mm / torch.bmm on contiguous "
+                        "operands) at reference shapes and at the two grouped-GEMM shapes, one JSON "
+                        "line each, for scale; no RankMixer work")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="after the timed region, run the library's token-mixing kernel (a pure "
                         "permutation copy of the input, bytes known) three times: the reference "
@@ -198,6 +202,40 @@ def cpu_baseline(cfg, n):
                       f"fp64 NumPy, {el:.1f} s"}
 
 
+def library_reference():
+    """The platform library's bf16 GEMM at a few shapes (contiguous operands only)."""
+    import torch
+    torch.manual_seed(0)
+
+    def timeit(f, n=10):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for n in (4096, 8192, 16384):
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        b = (torch.randn(n, n, device="cuda") / n ** 0.5).to(torch.bfloat16)
+        ms = timeit(lambda: torch.mm(a, b))
+        print(json.dumps({"library_gemm": f"mm {n}x{n}x{n}", "ms": round(ms, 4),
+                          "tflops": round(2.0 * n ** 3 / ms / 1e9, 1)}), flush=True)
+        del a, b
+    G, M, D, kD = 32, 2048, 1536, 6144
+    for name, (k, n) in (("GEMM1 shape", (D, kD)), ("GEMM2 shape", (kD, D))):
+        # activations ~ N(0, 1), weights ~ N(0, 1/K): the workload's value ranges
+        a = torch.randn(G, M, k, device="cuda", dtype=torch.bfloat16)
+        b = (torch.randn(G, k, n, device="cuda") / k ** 0.5).to(torch.bfloat16).contiguous()
+        ms = timeit(lambda: torch.bmm(a, b))
+        print(json.dumps({"library_gemm": f"bmm {G}x({M}x{k})x({k}x{n}) {name}", "ms": round(ms, 4),
+                          "tflops": round(2.0 * G * M * k * n / ms / 1e9, 1)}), flush=True)
+        del a, b
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -207,6 +245,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.library_reference:
+        library_reference()
+        return
     from rankmixer_block_forward_amd import synth
     cfg = synth.CONFIGS[args.workload]
     batches = list(synth.SWEEP_BATCHES) if args.sweep else [args.batch or cfg.B]
