@@ -3,5 +3,5 @@
 Imported only by the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU
 baseline; the GPU library never imports it and shares no code with it.
 """
-from .rmx_oracle import (token_mix, layer_norm, gelu, pffn, moe_gates, moe_pffn,  # noqa: F401
+from .rmx_oracle import (tokenize, token_mix, layer_norm, gelu, pffn, moe_gates, moe_pffn,  # noqa: F401
                          block, forward)

@@ -89,3 +89,17 @@ def forward_sample(x, layers, eps=1e-5):
         gates_all.append(gates if gates else None)
     o = [sum(x[t][j] for t in range(T)) / T for j in range(D)]
     return o, x, gates_all
+
+
+def tokenize_sample(e, Wp, bp):
+    """One sample's concatenated embedding e[T*d] -> tokens x[T][D] with scalar loops:
+    token t projects coordinates t*d .. t*d + d - 1 with its own Wp[t][d][D], bp[t][D]."""
+    e = [float(v) for v in _tolist(e)]
+    Wp, bp = _tolist(Wp), _tolist(bp)
+    T = len(Wp)
+    d = len(Wp[0])
+    out = []
+    for t in range(T):
+        piece = e[t * d:(t + 1) * d]
+        out.append(_linear(piece, Wp[t], bp[t]))
+    return out

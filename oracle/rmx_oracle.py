@@ -13,7 +13,7 @@ Pages cited (by title):
   [exp1]   "RankMixer 详解（1）：特征分组与完整计算流程" (jackknifer.me),
            sections 3.1, 3.3, 4.1, 5.1, 6.
   [uni]    "UniMixer: A Unified Architecture for Scaling Laws in Recommendation
-           Systems" (Chinese translation, juejin.cn), eq (10), Appendix A.
+           Systems" (Chinese translation, juejin.cn), eq (9), eq (10), Appendix A.
 
 Readings taken where the pages leave a step open (each is listed in the design doc):
   * H = T, and D must be divisible by T ([paper] 3.3.1; [exp1] 3.1).
@@ -25,6 +25,10 @@ Readings taken where the pages leave a step open (each is listed in the design doc):
   * Sparse-MoE: gate g = ReLU(s W_g) with no bias and no renormalisation, an expert
     is a Linear-GELU-Linear of the eq (6)-(7) form, V = sum_e g_e * expert_e(s)
     summed in expert order ([paper] 3.4 eq (10)).
+  * Tokenisation: token i projects its own slice of the concatenated embedding with
+    its own linear layer ([uni] eq (9) makes the layer token-specific; [paper] 3.2
+    eq (2) and [exp1] 2 leave the sharing open), in the row-vector convention of the
+    FFN: x_t = e[t*d:(t+1)*d] Wp[t] + bp[t], Wp[t] of shape d x D.
 
 Pinned by tests/test_oracle_pins.py against the pages' worked examples, closed forms,
 invariants, library special cases and brute force (tests/golden/ holds the pages'
@@ -35,12 +39,31 @@ from __future__ import annotations
 import numpy as np
 from scipy.special import erf
 
-__all__ = ["token_mix", "layer_norm", "gelu", "pffn", "moe_gates", "moe_pffn",
+__all__ = ["tokenize", "token_mix", "layer_norm", "gelu", "pffn", "moe_gates", "moe_pffn",
            "block", "forward"]
 
 
 def _f64(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float64)
+
+
+def tokenize(E: np.ndarray, Wp, bp) -> np.ndarray:
+    """Tokenisation projection ([paper] 3.2 eq (2); [exp1] 2; [uni] eq (9)).
+
+    E[B, T*d] is the concatenated feature embedding; token t takes the half-open slice
+    E[:, t*d:(t+1)*d] (the first d coordinates go to the first token) and projects it to
+    D dimensions with its own layer: X[:, t, :] = E[:, t*d:(t+1)*d] Wp[t] + bp[t],
+    Wp[t] of shape d x D.  Returns X[B, T, D].
+    """
+    E = _f64(E)
+    T, d, D = np.shape(Wp)
+    B = E.shape[0]
+    if E.shape[1] != T * d:
+        raise ValueError(f"E has {E.shape[1]} columns, expected T*d = {T * d}")
+    X = np.empty((B, T, D), dtype=np.float64)
+    for t in range(T):
+        X[:, t, :] = E[:, t * d:(t + 1) * d] @ _f64(Wp[t]) + _f64(bp[t])
+    return X
 
 
 def token_mix(X: np.ndarray) -> np.ndarray:

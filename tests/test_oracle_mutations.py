@@ -11,7 +11,7 @@ import oracle
 import oracle.rmx_oracle as ro
 from tests import test_oracle_pins as pins
 
-ORIG = {name: getattr(ro, name) for name in ("token_mix", "layer_norm", "gelu", "pffn", "moe_gates")}
+ORIG = {name: getattr(ro, name) for name in ("token_mix", "layer_norm", "gelu", "pffn", "moe_gates", "tokenize")}
 
 
 def _mix_identity(X):
@@ -88,7 +88,30 @@ def _gates_no_relu(S, Wg):
     return np.stack([S[:, t] @ np.asarray(Wg[t]) for t in range(S.shape[1])], axis=1)
 
 
+def _tok_transposed_slices(E, Wp, bp):
+    # takes token t's coordinates strided by T instead of contiguous
+    E = np.asarray(E, dtype=np.float64)
+    T, d, D = np.shape(Wp)
+    B = E.shape[0]
+    Et = E.reshape(B, d, T).transpose(0, 2, 1).reshape(B, T * d)
+    return ORIG["tokenize"](Et, Wp, bp)
+
+
+def _tok_first_layer_shared(E, Wp, bp):
+    T = np.shape(Wp)[0]
+    return ORIG["tokenize"](E, [Wp[0]] * T, [bp[0]] * T)
+
+
+def _tok_slice_shifted(E, Wp, bp):
+    # off by one: token t starts at coordinate t*d + 1 (wrapping the last coordinate)
+    E = np.roll(np.asarray(E, dtype=np.float64), -1, axis=1)
+    return ORIG["tokenize"](E, Wp, bp)
+
+
 MUTATIONS = {
+    "tokenize_strided_slices": ("tokenize", _tok_transposed_slices),
+    "tokenize_shared_first_layer": ("tokenize", _tok_first_layer_shared),
+    "tokenize_slice_off_by_one": ("tokenize", _tok_slice_shifted),
     "mix_identity": ("token_mix", _mix_identity),
     "mix_reversed_within_head": ("token_mix", _mix_reversed_heads),
     "mix_tokens_reversed": ("token_mix", _mix_tokens_reversed),

@@ -332,3 +332,60 @@ def test_moe_equal_experts_scale_one_mlp():
     for t in range(T):
         y = _torch_mlp(S[:, t], p["We1"][t, 0], p["be1"][t, 0], p["We2"][t, 0], p["be2"][t, 0])
         np.testing.assert_allclose(V[:, t], G[:, t].sum(-1)[:, None] * y, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------- tokenisation
+
+def test_tokenize_identity_projection_takes_half_open_slices():
+    """d = D, Wp[t] = I, bp = 0: token t is exactly coordinates t*d .. t*d + d - 1 of the
+    concatenated embedding, the first d going to the first token ([exp1] 2: half-open
+    slices, first slice the first d coordinates)."""
+    T, d, B = 3, 4, 2
+    E = np.arange(B * T * d, dtype=np.float64).reshape(B, T * d)
+    X = oracle.tokenize(E, np.stack([np.eye(d)] * T), np.zeros((T, d)))
+    assert X.shape == (B, T, d)
+    assert X[0, 0].tolist() == [0.0, 1.0, 2.0, 3.0]
+    assert X[0, 2].tolist() == [8.0, 9.0, 10.0, 11.0]
+    assert X[1, 1].tolist() == [16.0, 17.0, 18.0, 19.0]
+
+
+def test_tokenize_shared_weights_is_one_linear_layer():
+    """All tokens given the same layer: one torch Linear over the [B, T, d] view."""
+    rng = np.random.default_rng(11)
+    T, d, D, B = 4, 5, 7, 6
+    W = rng.standard_normal((d, D))
+    b = rng.standard_normal(D)
+    E = rng.standard_normal((B, T * d))
+    X = oracle.tokenize(E, np.stack([W] * T), np.stack([b] * T))
+    ref = F.linear(torch.tensor(E).view(B, T, d), torch.tensor(W).T, torch.tensor(b)).numpy()
+    np.testing.assert_allclose(X, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_tokenize_token_specific_is_block_diagonal_linear():
+    """Token-specific layers ([uni] eq (9)) = one Linear over the whole embedding with a
+    block-diagonal weight whose t-th block is Wp[t]."""
+    rng = np.random.default_rng(12)
+    T, d, D, B = 3, 4, 6, 5
+    Wp = rng.standard_normal((T, d, D))
+    bp = rng.standard_normal((T, D))
+    E = rng.standard_normal((B, T * d))
+    X = oracle.tokenize(E, Wp, bp)
+    bd = torch.block_diag(*[torch.tensor(w) for w in Wp])            # [T*d, T*D]
+    ref = F.linear(torch.tensor(E), bd.T, torch.tensor(bp.reshape(-1))).numpy().reshape(B, T, D)
+    np.testing.assert_allclose(X, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_tokenize_matches_scalar_brute_force():
+    rng = np.random.default_rng(13)
+    T, d, D, B = 3, 5, 4, 4
+    Wp = rng.standard_normal((T, d, D))
+    bp = rng.standard_normal((T, D))
+    E = rng.standard_normal((B, T * d))
+    X = oracle.tokenize(E, Wp, bp)
+    for b in range(B):
+        np.testing.assert_allclose(X[b], np.array(brute.tokenize_sample(E[b], Wp, bp)), rtol=1e-13, atol=1e-13)
+
+
+def test_tokenize_rejects_wrong_width():
+    with pytest.raises(ValueError):
+        oracle.tokenize(np.zeros((2, 7)), np.zeros((2, 4, 3)), np.zeros((2, 3)))
