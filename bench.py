@@ -39,6 +39,9 @@ def parse():
     p.add_argument("--sweep", action="store_true", help="one line per serving batch size")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-samples", type=int, default=384)
+    p.add_argument("--tokenize", action="store_true",
+                   help="time the tokenisation projection (rmx_tokenize) at the 1B input shape "
+                        "(B x [T*d] -> B x T x D, d = 512) and print its line instead")
     p.add_argument("--library-reference", action="store_true",
                    help="time the vendor library's bf16 GEMM (torch.mm / torch.bmm on contiguous "
                         "operands) at reference shapes and at the two grouped-GEMM shapes, one JSON "
@@ -236,6 +239,51 @@ def library_reference():
         del a, b
 
 
+def bench_tokenize(B, steps, warmup):
+    """The tokenisation projection at the 1B input: E [B, T*d] -> X [B, T, D]."""
+    import torch
+    import rankmixer_block_forward_amd as rmx
+    from rankmixer_block_forward_amd import synth
+    T, D, d = synth.B1.T, synth.B1.D, synth.TOKENIZE_D
+    ti = synth.make_tokenize_inputs(B, T, d, D, "bf16", seed=0)
+
+    def dev(a):
+        return torch.from_numpy(a).to("cuda").to(torch.bfloat16).contiguous()
+    E, Wp, bp = dev(ti.E), dev(ti.Wp), dev(ti.bp)
+    X = torch.empty((B, T, D), dtype=torch.bfloat16, device="cuda")
+    for _ in range(warmup):
+        rmx.tokenize(E, Wp, bp, X=X)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        rmx.tokenize(E, Wp, bp, X=X)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert torch.isfinite(X.float()).all().item()
+    flops = 2.0 * B * T * d * D
+    nbytes = 2.0 * (B * T * d + T * d * D + T * D + B * T * D)
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops / nbytes > ridge:
+        ach = flops / (ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    else:
+        ach = nbytes / (ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof.update(traffic=None, kernel="tokenize", avg_launch_ms=round(ms, 4),
+                algorithmic_flops_per_launch=flops, algorithmic_bytes_per_launch=nbytes)
+    print(json.dumps({
+        "metric": "tokenisation projection: samples/s (concatenated embedding -> T tokens of D)",
+        "value": round(B / (ms / 1e3), 1), "unit": "samples/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded Gaussian embedding and random-init projections)",
+        "config": {"workload": "rankmixer-1b-tokenize", "B": B, "T": T, "d": d, "D": D},
+        "tflops": round(flops / (ms / 1e3) / 1e12, 2), "roofline": roof}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -247,6 +295,9 @@ def main():
         sys.exit(1)
     if args.library_reference:
         library_reference()
+        return
+    if args.tokenize:
+        bench_tokenize(args.batch or 2048, args.steps, args.warmup)
         return
     from rankmixer_block_forward_amd import synth
     cfg = synth.CONFIGS[args.workload]

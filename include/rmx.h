@@ -136,6 +136,19 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
 rmx_status rmx_token_mix(const void* X, void* Y, int64_t B, int32_t T, int32_t D,
                          int32_t dtype, void* stream);
 
+/* Tokenisation projection, the step before the first block: the concatenated feature
+ * embedding E [B, T*d] (device, dtype) is cut into T half-open slices of d coordinates and
+ * slice t is projected by token t's own layer,
+ *     X[b, t, :] = E[b, t*d : (t+1)*d] Wp[t] + bp[t],
+ * Wp [T, d, D] (device, dtype, row-vector convention), bp [T, D] (device, dtype, or NULL =
+ * zeros), X [B, T, D] (device, dtype): the input of rmx_block_forward.  E and X must not
+ * overlap.  fp32 or bf16; the products accumulate in fp32 and X is rounded to dtype.
+ * T, d, D >= 1, B >= 0 (B == 0 enqueues nothing).  Stateless: no handle.
+ * ("RankMixer" paper translation, section 3.2 eq (2); "RankMixer 详解（1）", section 2;
+ * "UniMixer" translation, eq (9) for the token-specific layers.) */
+rmx_status rmx_tokenize(const void* E, const void* Wp, const void* bp, void* X, int64_t B, int32_t T,
+                        int32_t d, int32_t D, int32_t dtype, void* stream);
+
 /* Kernel-level timing.  While enabled, every kernel the handle launches is bracketed by
  * a pair of HIP events recorded on the caller's stream; rmx_profile_read() waits for the
  * recorded events and returns, per kernel kind, the summed duration in ms and the
@@ -163,7 +176,8 @@ const char* rmx_kernel_name(int32_t kind);
 const char* rmx_status_string(rmx_status s);
 
 /* Detail of the last failure: of this handle's last call when h != NULL, else of the
- * calling thread's last call (rmx_create, rmx_token_mix).  Never NULL; "" if none. */
+ * calling thread's last call (rmx_create, rmx_token_mix, rmx_tokenize).  Never NULL; "" if
+ * none. */
 const char* rmx_last_error(const rmx_handle* h);
 
 /* RMX_ABI_VERSION of the built library. */

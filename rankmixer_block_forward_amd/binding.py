@@ -21,6 +21,7 @@ KERNEL_COUNT = 8
 # Every symbol include/rmx.h declares.
 EXPORTS = (
     "rmx_create", "rmx_destroy", "rmx_block_forward", "rmx_block_forward_ex", "rmx_token_mix",
+    "rmx_tokenize",
     "rmx_profile_enable", "rmx_profile_read", "rmx_profile_reset", "rmx_kernel_name",
     "rmx_status_string", "rmx_last_error", "rmx_abi_version",
 )
@@ -65,6 +66,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rmx_block_forward_ex.argtypes = [vp, vp, i64, ctypes.POINTER(rmx_weights), i32, i32, vp,
                                          vp, vp, vp]
     lib.rmx_token_mix.argtypes = [vp, vp, i64, i32, i32, i32, vp]
+    lib.rmx_tokenize.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, vp]
     lib.rmx_profile_enable.argtypes = [vp, i32]
     lib.rmx_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
                                      ctypes.POINTER(i64)]
@@ -221,6 +223,26 @@ def token_mix(X, Y=None, stream=None):
     _ptr(Y, "Y", X.dtype, X.shape)
     _check(lib.rmx_token_mix(_ptr(X, "X"), _ptr(Y, "Y"), B, T, D, code, _stream(stream)))
     return Y
+
+
+def tokenize(E, Wp, bp=None, X=None, stream=None):
+    """X[b, t] = E[b, t*d:(t+1)*d] @ Wp[t] + bp[t] on the GPU (the library's tokenisation
+    projection); E [B, T*d], Wp [T, d, D], bp [T, D] or None; returns X [B, T, D]."""
+    import torch
+    lib = load_library()
+    T, d, D = Wp.shape
+    B = E.shape[0]
+    code = _dtype_code(E.dtype)
+    _ptr(E, "E", E.dtype, (B, T * d))
+    _ptr(Wp, "Wp", E.dtype)
+    if bp is not None:
+        _ptr(bp, "bp", E.dtype, (T, D))
+    if X is None:
+        X = torch.empty((B, T, D), dtype=E.dtype, device=E.device)
+    _ptr(X, "X", E.dtype, (B, T, D))
+    _check(lib.rmx_tokenize(_ptr(E, "E"), _ptr(Wp, "Wp"), _ptr(bp, "bp"), _ptr(X, "X"), B, T, d, D, code,
+                            _stream(stream)))
+    return X
 
 
 def upload(inputs, device="cuda"):

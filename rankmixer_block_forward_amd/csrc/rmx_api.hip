@@ -560,6 +560,44 @@ rmx_status rmx_token_mix(const void* X, void* Y, int64_t B, int32_t T, int32_t D
   return RMX_OK;
 }
 
+rmx_status rmx_tokenize(const void* E, const void* Wp, const void* bp, void* X, int64_t B, int32_t T,
+                        int32_t d, int32_t D, int32_t dtype, void* stream) {
+  clear_error(nullptr);
+  if (T < 1 || d < 1 || D < 1 || B < 0) return fail(nullptr, RMX_ERR_INVALID_ARG, "T, d, D must be >= 1 and B >= 0");
+  if (dtype != RMX_FP32 && dtype != RMX_BF16) return fail(nullptr, RMX_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (B > INT32_MAX) return fail(nullptr, RMX_ERR_UNSUPPORTED, "B must be < 2^31");
+  if (B == 0) return RMX_OK;
+  int dev = -1;
+  rmx_status st = check_device_arch(nullptr, &dev);
+  if (st != RMX_OK) return st;
+  const size_t esz = dtype_size(dtype);
+  const size_t bytesE = size_t(B) * T * d * esz, bytesX = size_t(B) * T * D * esz;
+  if ((st = check_dev(nullptr, E, bytesE, dev, "E")) != RMX_OK) return st;
+  if ((st = check_dev(nullptr, Wp, size_t(T) * d * D * esz, dev, "Wp")) != RMX_OK) return st;
+  if ((st = check_dev_opt(nullptr, bp, size_t(T) * D * esz, dev, "bp")) != RMX_OK) return st;
+  if ((st = check_dev(nullptr, X, bytesX, dev, "X")) != RMX_OK) return st;
+  const uintptr_t e = reinterpret_cast<uintptr_t>(E), x = reinterpret_cast<uintptr_t>(X);
+  if (e < x + bytesX && x < e + bytesE) return fail(nullptr, RMX_ERR_INVALID_ARG, "E and X overlap");
+  // token t is group t: A = E with rows T*d apart and groups d apart, C = X with rows T*D
+  // apart and groups D apart
+  GemmArgs g{};
+  g.A = E;
+  g.W = Wp;
+  g.bias = bp;
+  g.C = X;
+  g.G = T;
+  g.M = int(B);
+  g.N = D;
+  g.K = d;
+  g.lda = int64_t(T) * d;
+  g.sa = d;
+  g.ldc = int64_t(T) * D;
+  g.sc = D;
+  hipError_t err = launch_gemm(dtype, EPI_BIAS, g, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(nullptr, RMX_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return RMX_OK;
+}
+
 rmx_status rmx_profile_enable(rmx_handle* h, int32_t enable) {
   if (!h) return fail(nullptr, RMX_ERR_INVALID_ARG, "handle is NULL");
   h->prof = enable != 0;

@@ -252,12 +252,12 @@ __device__ __forceinline__ void mfma_tile(f32x16_t (&acc)[4][4], const TileSrc& 
 // block (transposed product): lane l holds row l % 32 and, in register 4 g + e, column
 // 8 g + 4 (l / 32) + e.  Each wave stages 32 rows x 32 NJ columns at a time through LDS
 // (16-byte writes) so that every lane then owns 8 consecutive columns of one row: 16-byte
-// global stores, and coalesced bias / residual loads.  `out_row(m)` is the output row of
-// tile row m, or -1 if it does not exist.
-template <int EPI, int NI, int NJ, typename OutRow>
+// global stores, and coalesced bias / residual loads.  `out_off(m)` is the element offset
+// of the output row of tile row m in C (and R), or -1 if the row does not exist.
+template <int EPI, int NI, int NJ, typename OutOff>
 __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], float* smem_f, const GemmArgs& p,
                                               const bf16_t* bias_g, int n0, int wrow0, int wcol0, int wave,
-                                              int lane, OutRow out_row) {
+                                              int lane, OutOff out_off) {
   constexpr int LD = NJ * 32 + 4;     // fp32 row stride of the staging rows
   constexpr int LPR = NJ * 4;         // lanes per staged row (8 columns each)
   constexpr int RPP = 64 / LPR;       // rows per pass
@@ -287,17 +287,21 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], flo
 #pragma unroll
     for (int pass = 0; pass < 32 / RPP; ++pass) {
       const int row = pass * RPP + rsub;
-      const int orow = out_row(wrow0 + i * 32 + row);
+      const int64_t ooff = out_off(wrow0 + i * 32 + row);
       float v[8];
       const float4 x0 = *reinterpret_cast<const float4*>(st + row * LD + col8);
       const float4 x1 = *reinterpret_cast<const float4*>(st + row * LD + col8 + 4);
       v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
       v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-      if (orow >= 0 && n_ok) {
-        const size_t off = size_t(orow) * N + n;
+      if (ooff >= 0 && n_ok) {
+        const size_t off = size_t(ooff) + n;
         if constexpr (EPI == EPI_GELU || EPI == EPI_MOE1) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[e]);
+          store8(static_cast<bf16_t*>(p.C) + off, v);
+        } else if constexpr (EPI == EPI_BIAS) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += bias[e];
           store8(static_cast<bf16_t*>(p.C) + off, v);
         } else if constexpr (EPI == EPI_RESID) {
           float rr[8];
@@ -306,7 +310,7 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], flo
           for (int e = 0; e < 8; ++e) v[e] = v[e] + bias[e] + rr[e];
           store8(static_cast<float*>(p.C) + off, v);
         } else {
-          const float gv = p.row_gate[orow];
+          const float gv = p.row_gate[ooff / N];
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = gv * (v[e] + bias[e]);
           store8(static_cast<float*>(p.C) + off, v);
@@ -343,20 +347,23 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
 
   // Slices are < 2^31 bytes (checked at launch); an offset equal to the slice size is out
   // of range whether or not the uniform offset takes part in the range check.
-  const uint32_t bytesA = uint32_t(M) * uint32_t(K) * 2u, bytesW = uint32_t(K) * uint32_t(N) * 2u;
+  const uint32_t lda = uint32_t(p.lda);
+  const uint32_t bytesA = (uint32_t(M - 1) * lda + uint32_t(K)) * 2u, bytesW = uint32_t(K) * uint32_t(N) * 2u;
   TileSrc ts;
-  ts.rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(g) * M * K, bytesA);
+  ts.rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(g) * size_t(p.sa), bytesA);
   ts.rW = make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * K * N, bytesW);
   tile_offsets(ts, wave, lane, n0, N,
                [&](int r, int cbytes) {
-                 return (m0 + r < M) ? uint32_t(m0 + r) * uint32_t(K) * 2u + uint32_t(cbytes) : bytesA;
+                 return (m0 + r < M) ? uint32_t(m0 + r) * lda * 2u + uint32_t(cbytes) : bytesA;
                },
                bytesW);
   f32x16_t acc[4][4];
   mfma_tile(acc, ts, smem, lds0, K, N, wave, lane);
   const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
   tile_epilogue<EPI, 4, 4>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, (wave >> 1) * 128,
-                           (wave & 1) * 128, wave, lane, [&](int m) { return m0 + m < M ? g * M + m0 + m : -1; });
+                           (wave & 1) * 128, wave, lane, [&](int m) -> int64_t {
+                             return m0 + m < M ? int64_t(g) * p.sc + int64_t(m0 + m) * p.ldc : -1;
+                           });
 }
 
 // Sparse-MoE grouped GEMM.  Group g has rows group_start[g] .. group_start[g+1]-1 of the
@@ -420,7 +427,9 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_moe(GemmArgs p) {
     mfma_tile(acc, ts, smem, lds0, K, N, wave, lane);
     const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
     tile_epilogue<EPI, 4, 4>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, (wave >> 1) * 128,
-                             (wave & 1) * 128, wave, lane, [&](int m) { return m0 + m < rows ? row0 + m0 + m : -1; });
+                             (wave & 1) * 128, wave, lane, [&](int m) -> int64_t {
+                               return m0 + m < rows ? int64_t(row0 + m0 + m) * N : -1;
+                             });
   }
 }
 
@@ -450,8 +459,9 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
   const int nt = rem / nMt, mt = rem - nt * nMt;
   const int m0 = mt * SM_BM, n0 = nt * BN;
 
-  const uint32_t bytesA = uint32_t(M) * uint32_t(K) * 2u, bytesW = uint32_t(K) * uint32_t(N) * 2u;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(g) * M * K, bytesA);
+  const uint32_t lda = uint32_t(p.lda);
+  const uint32_t bytesA = (uint32_t(M - 1) * lda + uint32_t(K)) * 2u, bytesW = uint32_t(K) * uint32_t(N) * 2u;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(g) * size_t(p.sa), bytesA);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * K * N, bytesW);
   // copy 0: A rows 16 w .. 16 w + 15 (lane q takes chunk q % 4 of row q / 4, swizzled);
   // copies 1..4: W k rows 8 w + 2 (c - 1) and +1, as in the 256 x 256 kernel
@@ -459,7 +469,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
   {
     const int r = 16 * wave + (lane >> 2);
     const int c = (lane & 3) ^ swz_a(r);
-    offA = (m0 + r < M) ? uint32_t(m0 + r) * uint32_t(K) * 2u + uint32_t(c * 16) : bytesA;
+    offA = (m0 + r < M) ? uint32_t(m0 + r) * lda * 2u + uint32_t(c * 16) : bytesA;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int kr = 8 * wave + 2 * a + (lane >> 5);
@@ -563,7 +573,9 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
   __syncthreads();
   const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
   tile_epilogue<EPI, 2, 2>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, 0, wave * 64, wave, lane,
-                           [&](int m) { return m0 + m < M ? g * M + m0 + m : -1; });
+                           [&](int m) -> int64_t {
+                             return m0 + m < M ? int64_t(g) * p.sc + int64_t(m0 + m) * p.ldc : -1;
+                           });
 }
 
 // --------------------------------------------------------------- generic kernel
@@ -577,7 +589,7 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs p) {
   const int M = p.M, N = p.N, K = p.K;
   const int g = blockIdx.z;
   const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
-  const T* A = static_cast<const T*>(p.A) + size_t(g) * M * K;
+  const T* A = static_cast<const T*>(p.A) + size_t(g) * size_t(p.sa);
   const T* W = static_cast<const T*>(p.W) + size_t(g) * K * N;
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
@@ -588,7 +600,7 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs p) {
       const int e = tid + 256 * i;  // 0..1023
       const int am = e / GK, ak = e % GK;
       const int row = m0 + am, kk = k0 + ak;
-      As[ak][am] = (row < M && kk < K) ? load1(A + size_t(row) * K + kk) : 0.f;
+      As[ak][am] = (row < M && kk < K) ? load1(A + size_t(row) * size_t(p.lda) + kk) : 0.f;
       const int bk = e / GT, bn = e % GT;
       const int kr = k0 + bk, col = n0 + bn;
       Bs[bk][bn] = (kr < K && col < N) ? load1(W + size_t(kr) * N + col) : 0.f;
@@ -617,9 +629,11 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs p) {
       const int n = n0 + tx * 4 + j;
       if (n >= N) continue;
       const float bias = p.bias ? load1(static_cast<const T*>(p.bias) + size_t(g) * N + n) : 0.f;
-      const size_t off = (size_t(g) * M + m) * N + n;
+      const size_t off = size_t(g) * size_t(p.sc) + size_t(m) * size_t(p.ldc) + n;
       if constexpr (EPI == EPI_GELU) {
         store1(static_cast<T*>(p.C) + off, gelu_erf(acc[i][j] + bias));
+      } else if constexpr (EPI == EPI_BIAS) {
+        store1(static_cast<T*>(p.C) + off, acc[i][j] + bias);
       } else {
         static_cast<float*>(p.C)[off] = acc[i][j] + bias + load1(static_cast<const T*>(p.R) + off);
       }
@@ -629,9 +643,11 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs p) {
 
 }  // namespace
 
-bool gemm_uses_mfma(int dtype, int M, int N, int K) {
+bool gemm_uses_mfma(int dtype, int M, int N, int K, int64_t lda) {
   const uint64_t lim = uint64_t(1) << 31;
-  return dtype == DT_BF16 && K % BK == 0 && N % 8 == 0 && uint64_t(M) * K * 2 < lim && uint64_t(K) * N * 2 < lim;
+  const uint64_t ld = lda > 0 ? uint64_t(lda) : uint64_t(K);
+  const uint64_t spanA = M > 0 ? (uint64_t(M - 1) * ld + uint64_t(K)) * 2 : 0;
+  return dtype == DT_BF16 && K % BK == 0 && N % 8 == 0 && ld % 8 == 0 && spanA < lim && uint64_t(K) * N * 2 < lim;
 }
 
 hipError_t gemm_init() { return hipSuccess; }
@@ -655,20 +671,30 @@ hipError_t launch_gemm_moe(int epi, const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t stream) {
-  if (a.G == 0 || a.M == 0 || a.N == 0) return hipSuccess;
-  if (gemm_uses_mfma(dtype, a.M, a.N, a.K) && a.M <= GEMM_SMALL_M) {
+hipError_t launch_gemm(int dtype, int epi, const GemmArgs& args, hipStream_t stream) {
+  if (args.G == 0 || args.M == 0 || args.N == 0) return hipSuccess;
+  GemmArgs a = args;
+  if (a.lda == 0) a.lda = a.K;
+  if (a.ldc == 0) a.ldc = a.N;
+  if (a.sa == 0) a.sa = int64_t(a.M) * a.lda;
+  if (a.sc == 0) a.sc = int64_t(a.M) * a.ldc;
+  const bool mfma = gemm_uses_mfma(dtype, a.M, a.N, a.K, a.lda) && (a.sa % 8) == 0;
+  if (mfma && a.M <= GEMM_SMALL_M) {
     const int tiles = a.G * ((a.M + SM_BM - 1) / SM_BM) * ((a.N + BN - 1) / BN);
     if (epi == EPI_GELU)
       hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_GELU>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+    else if (epi == EPI_BIAS)
+      hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_BIAS>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
     else
       hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_RESID>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
     return hipGetLastError();
   }
-  if (gemm_uses_mfma(dtype, a.M, a.N, a.K)) {
+  if (mfma) {
     const int tiles = a.G * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (epi == EPI_GELU)
       hipLaunchKernelGGL((gemm_bf16_mfma<EPI_GELU>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+    else if (epi == EPI_BIAS)
+      hipLaunchKernelGGL((gemm_bf16_mfma<EPI_BIAS>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
     else
       hipLaunchKernelGGL((gemm_bf16_mfma<EPI_RESID>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
     return hipGetLastError();
@@ -677,11 +703,15 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t stream
   if (dtype == DT_BF16) {
     if (epi == EPI_GELU)
       hipLaunchKernelGGL((gemm_generic<bf16_t, EPI_GELU>), grid, dim3(256), 0, stream, a);
+    else if (epi == EPI_BIAS)
+      hipLaunchKernelGGL((gemm_generic<bf16_t, EPI_BIAS>), grid, dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((gemm_generic<bf16_t, EPI_RESID>), grid, dim3(256), 0, stream, a);
   } else {
     if (epi == EPI_GELU)
       hipLaunchKernelGGL((gemm_generic<float, EPI_GELU>), grid, dim3(256), 0, stream, a);
+    else if (epi == EPI_BIAS)
+      hipLaunchKernelGGL((gemm_generic<float, EPI_BIAS>), grid, dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((gemm_generic<float, EPI_RESID>), grid, dim3(256), 0, stream, a);
   }

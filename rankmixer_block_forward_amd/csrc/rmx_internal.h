@@ -88,7 +88,8 @@ hipError_t launch_moe_combine(const MoeArgs& a, hipStream_t stream);
 //   EPI_MOE1:  C [rows, N] (bf16) = GELU(A[src_row] W_g + bias_g), A = S [T * B, K]
 //   EPI_MOE2:  C [rows, N] (fp32) = row_gate * (A W_g + bias_g),   A = C of EPI_MOE1
 //   group g owns compacted rows group_start[g] .. group_start[g + 1] - 1.
-enum Epilogue { EPI_GELU = 0, EPI_RESID = 1, EPI_MOE1 = 2, EPI_MOE2 = 3 };
+//   EPI_BIAS:  C [G, M, N] (dtype) = A W + bias
+enum Epilogue { EPI_GELU = 0, EPI_RESID = 1, EPI_MOE1 = 2, EPI_MOE2 = 3, EPI_BIAS = 4 };
 
 struct GemmArgs {
   const void* A;
@@ -102,12 +103,16 @@ struct GemmArgs {
   const int* src_row;
   const float* row_gate;
   int a_rows;  // EPI_MOE1: rows of A (T * B)
+  // Dense kernels only (0 = contiguous): elements between rows of A, between rows of C
+  // (and R), between groups of A, between groups of C (and R).
+  int64_t lda, ldc, sa, sc;
 };
 // Rows per token up to which the dense launch uses 64-row tiles.
 constexpr int GEMM_SMALL_M = 64;
 
-// True when the bf16 MFMA kernel handles this shape (else the generic kernel runs).
-bool gemm_uses_mfma(int dtype, int M, int N, int K);
+// True when the bf16 MFMA kernel handles this shape (else the generic kernel runs);
+// lda = 0 means K.
+bool gemm_uses_mfma(int dtype, int M, int N, int K, int64_t lda = 0);
 // Sparse-MoE grouped GEMM launch (bf16 MFMA only); `max_rows` bounds every group's rows.
 hipError_t launch_gemm_moe(int epi, const GemmArgs& a, hipStream_t stream);
 bool gemm_moe_supported(int N, int K, int64_t a_rows);

@@ -29,6 +29,7 @@ KIND_X, KIND_MASK = 1, 2
 KIND_W1, KIND_B1, KIND_W2, KIND_B2 = 10, 11, 12, 13
 KIND_G1, KIND_BE1, KIND_G2, KIND_BE2 = 20, 21, 22, 23
 KIND_WG, KIND_WE1, KIND_BEXP1, KIND_WE2, KIND_BEXP2 = 30, 31, 32, 33, 34
+KIND_E, KIND_WP, KIND_BP = 40, 41, 42
 
 X_BLOCK = 64
 
@@ -222,3 +223,39 @@ def _expert_bias(cfg, seed, kind, shape):
         return np.zeros((L, T, E) + shape, dtype=np.float32)
     return _stacked_expert(cfg, seed, kind, shape, cfg.bias_std)
 
+
+
+# Tokenisation projection workload: the concatenated embedding of the 1B shape's input.
+# The pages give no per-token slice width d for it; 512 is taken (a 16,384-wide
+# concatenated embedding), d = D is covered by the tests.
+TOKENIZE_D = 512
+
+
+@dataclass
+class TokenizeInputs:
+    """Host copies of one tokenisation workload: E [B, T*d], Wp [T, d, D], bp [T, D]."""
+    E: np.ndarray
+    Wp: np.ndarray
+    bp: np.ndarray
+
+
+def make_tokenize_inputs(B: int, T: int, d: int, D: int, dtype: str = "bf16", seed: int = 0,
+                         bias_std: float = 0.0) -> TokenizeInputs:
+    """E ~ N(0, 1) drawn in blocks of 64 samples; Wp[t] ~ N(0, 1/d) (std = 1/sqrt(fan_in));
+    bp[t] ~ N(0, bias_std^2) or zero.  Same per-slice substreams as make_inputs."""
+    E = np.empty((B, T * d), dtype=np.float32)
+    nblk = (B + X_BLOCK - 1) // X_BLOCK
+
+    def one(i):
+        lo, hi = i * X_BLOCK, min(B, (i + 1) * X_BLOCK)
+        v = _normal(seed, (KIND_E, i), (hi - lo, T * d), 1.0)
+        E[lo:hi] = round_bf16(v) if dtype == "bf16" else v
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(nblk)))
+    Wp = np.empty((T, d, D), dtype=np.float32)
+    _fill_slices(Wp, lambda key: _normal(seed, key, (d, D), 1.0 / np.sqrt(d)), [(KIND_WP, t) for t in range(T)],
+                 dtype)
+    bp = np.zeros((T, D), dtype=np.float32)
+    if bias_std > 0.0:
+        _fill_slices(bp, lambda key: _normal(seed, key, (D,), bias_std), [(KIND_BP, t) for t in range(T)], dtype)
+    return TokenizeInputs(E=E, Wp=Wp, bp=bp)

@@ -76,3 +76,14 @@ def test_null_arguments():
     assert lib.rmx_token_mix(None, None, 1, 3, 8, 0, None) == binding.RMX_ERR_INVALID_ARG
     assert "divisible" in lib.rmx_last_error(None).decode()
     assert lib.rmx_token_mix(None, None, 0, 4, 8, 0, None) == binding.RMX_OK  # B = 0: nothing to do
+
+
+def test_tokenize_host_side_rejections():
+    """Argument errors of rmx_tokenize are caught on the host before any GPU work."""
+    lib = rmx.load_library()
+    assert lib.rmx_tokenize(None, None, None, None, 1, 0, 4, 8, 0, None) == binding.RMX_ERR_INVALID_ARG
+    assert ">= 1" in lib.rmx_last_error(None).decode()
+    assert lib.rmx_tokenize(None, None, None, None, 1, 2, 4, 8, 7, None) == binding.RMX_ERR_INVALID_ARG
+    assert "dtype" in lib.rmx_last_error(None).decode()
+    assert lib.rmx_tokenize(None, None, None, None, 0, 2, 4, 8, 1, None) == binding.RMX_OK  # B = 0
+    assert lib.rmx_tokenize(None, None, None, None, -1, 2, 4, 8, 1, None) == binding.RMX_ERR_INVALID_ARG
