@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RMX_ABI_VERSION 1
+#define RMX_ABI_VERSION 2
 
 typedef struct rmx_handle rmx_handle; /* opaque, owned by the library */
 
@@ -90,7 +90,11 @@ typedef struct {
  * Sparse-MoE only (else NULL; W1/b1/W2/b2 are then unused and may be NULL):
  *   Wg  [L, T, D, E]              router weights, no bias
  *   We1 [L, T, E, D, h]  be1 [L, T, E, h]   (be1 may be NULL)
- *   We2 [L, T, E, h, D]  be2 [L, T, E, D]   (be2 may be NULL)                        */
+ *   We2 [L, T, E, h, D]  be2 [L, T, E, D]   (be2 may be NULL)
+ * packed: NULL, or W1 and W2 of all blocks prepared by rmx_pack_weights for this handle
+ *   (dense bf16 handles whose D and k*D are multiples of 32).  When set, the forward reads
+ *   the weights from it (W1 and W2 are then unused and may be NULL); the result is the
+ *   same bit for bit.                                                                   */
 typedef struct {
   const void* W1;
   const void* b1;
@@ -105,6 +109,7 @@ typedef struct {
   const void* be1;
   const void* We2;
   const void* be2;
+  const void* packed;
 } rmx_weights;
 
 /* Validates cfg, checks that the current HIP device is gfx950, and allocates the
@@ -135,6 +140,18 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
  * (Paper section 3.3.1 eq (3)-(4); "RankMixer 详解（1）", section 3.1.) */
 rmx_status rmx_token_mix(const void* X, void* Y, int64_t B, int32_t T, int32_t D,
                          int32_t dtype, void* stream);
+
+/* Weights prepared once for the matrix cores.  rmx_packed_weights_bytes gives the size of
+ * the prepared copy of W1 and W2 of all L blocks for this handle, or 0 when the handle has
+ * no such path (fp32, Sparse-MoE, or D or k*D not a multiple of 32).  rmx_pack_weights
+ * reads w->W1 and w->W2 (device, [L, T, D, kD] and [L, T, kD, D]) and writes the copy to
+ * `packed` (device, `bytes` >= rmx_packed_weights_bytes(h), 16-byte aligned), enqueued on
+ * `stream`: each token's W^T in blocks of 256 rows x 32 columns, so that a K step of a
+ * 256-column weight tile is one contiguous 16 KB.  Pass it as rmx_weights.packed.  The
+ * caller owns the buffer; it stays valid while W1 and W2 are unchanged. */
+size_t rmx_packed_weights_bytes(const rmx_handle* h);
+rmx_status rmx_pack_weights(rmx_handle* h, const rmx_weights* w, int32_t L, void* packed, size_t bytes,
+                            void* stream);
 
 /* Tokenisation projection, the step before the first block: the concatenated feature
  * embedding E [B, T*d] (device, dtype) is cut into T half-open slices of d coordinates and

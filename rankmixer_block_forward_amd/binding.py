@@ -21,7 +21,7 @@ KERNEL_COUNT = 8
 # Every symbol include/rmx.h declares.
 EXPORTS = (
     "rmx_create", "rmx_destroy", "rmx_block_forward", "rmx_block_forward_ex", "rmx_token_mix",
-    "rmx_tokenize",
+    "rmx_tokenize", "rmx_packed_weights_bytes", "rmx_pack_weights",
     "rmx_profile_enable", "rmx_profile_read", "rmx_profile_reset", "rmx_kernel_name",
     "rmx_status_string", "rmx_last_error", "rmx_abi_version",
 )
@@ -41,7 +41,7 @@ class rmx_config(ctypes.Structure):
 
 
 WEIGHT_NAMES = ("W1", "b1", "W2", "b2", "ln1_g", "ln1_b", "ln2_g", "ln2_b",
-                "Wg", "We1", "be1", "We2", "be2")
+                "Wg", "We1", "be1", "We2", "be2", "packed")
 
 
 class rmx_weights(ctypes.Structure):
@@ -67,6 +67,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          vp, vp, vp]
     lib.rmx_token_mix.argtypes = [vp, vp, i64, i32, i32, i32, vp]
     lib.rmx_tokenize.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, vp]
+    lib.rmx_packed_weights_bytes.argtypes = [vp]
+    lib.rmx_packed_weights_bytes.restype = ctypes.c_size_t
+    lib.rmx_pack_weights.argtypes = [vp, ctypes.POINTER(rmx_weights), i32, vp, ctypes.c_size_t, vp]
     lib.rmx_profile_enable.argtypes = [vp, i32]
     lib.rmx_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
                                      ctypes.POINTER(i64)]
@@ -79,7 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rmx_last_error.restype = ctypes.c_char_p
     lib.rmx_abi_version.restype = i32
     for name in EXPORTS:
-        if name not in ("rmx_kernel_name", "rmx_status_string", "rmx_last_error", "rmx_abi_version"):
+        if name not in ("rmx_kernel_name", "rmx_status_string", "rmx_last_error", "rmx_abi_version",
+                        "rmx_packed_weights_bytes"):
             getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -169,6 +173,23 @@ class Handle:
             t = w.get(n)
             setattr(s, n, _ptr(t, n, self.dtype))
         return s
+
+    def packed_weights_bytes(self) -> int:
+        """Bytes of the prepared copy of W1 and W2 (0 when this handle has no such path)."""
+        return int(self._lib.rmx_packed_weights_bytes(self._h))
+
+    def pack_weights(self, weights: dict, stream=None):
+        """W1 and W2 of all blocks prepared for the matrix cores (rmx_pack_weights): a device
+        tensor to pass as weights["packed"]; the forward then reads the weights from it."""
+        import torch
+        nbytes = self.packed_weights_bytes()
+        if nbytes == 0:
+            raise RmxError(RMX_ERR_UNSUPPORTED, "this handle has no prepared-weights path")
+        packed = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+        ws = self._weights({"W1": weights["W1"], "W2": weights["W2"]})
+        _check(self._lib.rmx_pack_weights(self._h, ctypes.byref(ws), self.cfg.L, _ptr(packed, "packed"), nbytes,
+                                          _stream(stream)), self._h)
+        return packed
 
     def forward(self, X, weights: dict, out=None, xl_out=None, gate_out=None, stream=None,
                 L: int | None = None, k: int | None = None):

@@ -26,8 +26,8 @@ GEMM_SOURCE = os.path.join(PKG, "csrc", "rmx_gemm.hip")
 
 # kernel-name patterns -> the names the library's profiling uses
 KERNELS = [
-    (re.compile(r"gemm_bf16_mfma<0>"), "gemm1_gelu"),
-    (re.compile(r"gemm_bf16_mfma<1>"), "gemm2_residual"),
+    (re.compile(r"gemm_bf16_mfma<0[,>]"), "gemm1_gelu"),
+    (re.compile(r"gemm_bf16_mfma<1[,>]"), "gemm2_residual"),
     (re.compile(r"gemm_bf16_moe<2>"), "moe_ffn1"),
     (re.compile(r"gemm_bf16_moe<3>"), "moe_ffn2"),
     (re.compile(r"token_mix_kernel"), "copy"),

@@ -45,6 +45,9 @@ struct rmx_handle {
   void* S = nullptr;   // [T, max_batch, D]   dtype
   void* H = nullptr;   // [T, max_batch, kD]  dtype
   float* Y = nullptr;  // [T, max_batch, D]   fp32
+  // Dense bf16 handles with D and kD multiples of 32 can run on prepared weights; S and H
+  // then take the packed operand layout and are sized for pk_rows(max_batch) rows.
+  bool pk_capable = false;
   // Sparse-MoE workspace (moe_experts > 0); G = T * E groups, R = G * max_batch rows
   float* moe_g = nullptr;        // [G, max_batch]
   int* moe_cnt = nullptr;        // [G, nchunk]
@@ -317,11 +320,14 @@ rmx_status rmx_create(const rmx_config* cfg, rmx_handle** out_handle) {
     *ptr = static_cast<std::remove_pointer_t<std::remove_reference_t<decltype(*ptr)>>*>(q);
     total += bytes;
   };
+  h->pk_capable = cfg->moe_experts == 0 && cfg->dtype == RMX_BF16 && cfg->D % 32 == 0 &&
+                  (int64_t(cfg->k) * cfg->D) % 32 == 0;
+  const size_t prow = h->pk_capable ? size_t(cfg->T) * size_t(pk_rows(cfg->max_batch)) : rows;
   if (rows > 0) {
-    alloc(&h->S, nS * esz);
+    alloc(&h->S, prow * cfg->D * esz);
     alloc(&h->Y, nS * sizeof(float));
     if (cfg->moe_experts == 0) {
-      alloc(&h->H, nH * esz);
+      alloc(&h->H, prow * size_t(cfg->k) * cfg->D * esz);
     } else {
       const size_t G = size_t(cfg->T) * cfg->moe_experts, mb = size_t(cfg->max_batch);
       const size_t nchunk = (mb + 63) / 64, R = G * mb;
@@ -390,15 +396,22 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
   if ((st = check_dev_opt(h, xl_out, size_t(B) * T * D * esz, dev, "xl_out")) != RMX_OK) return st;
   const size_t E = size_t(c.moe_experts), hid = size_t(c.moe_hidden);
   if (moe) {
+    if (w->packed) return fail(h, RMX_ERR_UNSUPPORTED, "prepared weights are for dense handles");
     if ((st = check_dev(h, w->Wg, Ls * T * D * E * esz, dev, "Wg")) != RMX_OK) return st;
     if ((st = check_dev(h, w->We1, Ls * T * E * D * hid * esz, dev, "We1")) != RMX_OK) return st;
     if ((st = check_dev(h, w->We2, Ls * T * E * hid * D * esz, dev, "We2")) != RMX_OK) return st;
     if ((st = check_dev_opt(h, w->be1, Ls * T * E * hid * esz, dev, "be1")) != RMX_OK) return st;
     if ((st = check_dev_opt(h, w->be2, Ls * T * E * D * esz, dev, "be2")) != RMX_OK) return st;
     if ((st = check_dev_opt(h, gate_out, Ls * size_t(B) * T * E * 4, dev, "gate_out")) != RMX_OK) return st;
+  } else if (w->packed) {
+    if (!h->pk_capable)
+      return fail(h, RMX_ERR_UNSUPPORTED, "prepared weights need a dense bf16 handle with D and k*D multiples of 32");
+    if ((st = check_dev(h, w->packed, rmx_packed_weights_bytes(h), dev, "packed")) != RMX_OK) return st;
   } else {
     if ((st = check_dev(h, w->W1, Ls * T * D * kD * esz, dev, "W1")) != RMX_OK) return st;
     if ((st = check_dev(h, w->W2, Ls * T * kD * D * esz, dev, "W2")) != RMX_OK) return st;
+  }
+  if (!moe) {
     if ((st = check_dev_opt(h, w->b1, Ls * T * kD * esz, dev, "b1")) != RMX_OK) return st;
     if ((st = check_dev_opt(h, w->b2, Ls * T * D * esz, dev, "b2")) != RMX_OK) return st;
     if (w->Wg || w->We1 || w->We2 || w->be1 || w->be2)
@@ -427,6 +440,9 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
   };
   hipError_t e = hipSuccess;
   const int Bi = int(B);
+  const bool pk = !moe && w->packed != nullptr;
+  // prepared weights of block n: W1^T then W2^T, packed (elements)
+  const size_t pk_w1 = T * size_t(pk_rows(int64_t(kD))) * D, pk_w2 = T * size_t(pk_rows(int64_t(D))) * kD;
   for (int n = 0; n < c.L && e == hipSuccess; ++n) {
     RowsArgs ra{};
     ra.in = n == 0 ? X : static_cast<const void*>(h->Y);
@@ -439,6 +455,7 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
     ra.T = c.T;
     ra.D = c.D;
     ra.eps = c.ln_eps;
+    ra.s_packed = pk ? 1 : 0;
     e = run_rows(h, s, n == 0 ? ROWS_FIRST : ROWS_MID, ra);
     if (e != hipSuccess) break;
 
@@ -496,7 +513,8 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
 
     GemmArgs g1{};
     g1.A = h->S;
-    g1.W = at(w->W1, size_t(n) * T * D * kD);
+    g1.W = pk ? at(w->packed, size_t(n) * (pk_w1 + pk_w2)) : at(w->W1, size_t(n) * T * D * kD);
+    g1.packed = pk ? 1 : 0;
     g1.bias = at(w->b1, size_t(n) * T * kD);
     g1.C = h->H;
     g1.G = c.T;
@@ -508,7 +526,8 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
 
     GemmArgs g2{};
     g2.A = h->H;
-    g2.W = at(w->W2, size_t(n) * T * kD * D);
+    g2.W = pk ? at(w->packed, size_t(n) * (pk_w1 + pk_w2) + pk_w1) : at(w->W2, size_t(n) * T * kD * D);
+    g2.packed = pk ? 1 : 0;
     g2.bias = at(w->b2, size_t(n) * T * D);
     g2.R = h->S;
     g2.C = h->Y;
@@ -532,6 +551,53 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
     e = run_rows(h, s, ROWS_FINAL, ra);
   }
   if (e != hipSuccess) return fail(h, RMX_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return RMX_OK;
+}
+
+size_t rmx_packed_weights_bytes(const rmx_handle* h) {
+  if (!h || !h->pk_capable) return 0;
+  const rmx_config& c = h->cfg;
+  const size_t T = c.T, D = c.D, kD = size_t(c.k) * c.D;
+  const size_t per_layer = T * size_t(pk_rows(int64_t(kD))) * D + T * size_t(pk_rows(int64_t(D))) * kD;
+  return size_t(c.L) * per_layer * 2;
+}
+
+rmx_status rmx_pack_weights(rmx_handle* h, const rmx_weights* w, int32_t L, void* packed, size_t bytes,
+                            void* stream) {
+  if (!h) return fail(nullptr, RMX_ERR_INVALID_ARG, "handle is NULL");
+  clear_error(h);
+  const rmx_config& c = h->cfg;
+  if (!w) return fail(h, RMX_ERR_INVALID_ARG, "weights is NULL");
+  if (L != c.L) return fail(h, RMX_ERR_INVALID_ARG, "L=%d but the handle was created with L=%d", L, c.L);
+  if (!h->pk_capable)
+    return fail(h, RMX_ERR_UNSUPPORTED, "prepared weights need a dense bf16 handle with D and k*D multiples of 32");
+  const size_t need = rmx_packed_weights_bytes(h);
+  if (bytes < need) return fail(h, RMX_ERR_INVALID_ARG, "packed buffer of %zu bytes, %zu needed", bytes, need);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
+    (void)hipGetLastError();
+    return fail(h, RMX_ERR_INVALID_ARG, "current device %d is not the handle's device %d", dev, h->device);
+  }
+  const size_t T = c.T, D = c.D, kD = size_t(c.k) * c.D, Ls = c.L;
+  rmx_status st;
+  if ((st = check_dev(h, w->W1, Ls * T * D * kD * 2, dev, "W1")) != RMX_OK) return st;
+  if ((st = check_dev(h, w->W2, Ls * T * kD * D * 2, dev, "W2")) != RMX_OK) return st;
+  if ((st = check_dev(h, packed, need, dev, "packed")) != RMX_OK) return st;
+  const uintptr_t pb = reinterpret_cast<uintptr_t>(packed);
+  for (const void* src : {w->W1, w->W2}) {
+    const uintptr_t sb = reinterpret_cast<uintptr_t>(src);
+    if (pb < sb + Ls * T * D * kD * 2 && sb < pb + need)
+      return fail(h, RMX_ERR_INVALID_ARG, "packed overlaps W1 or W2");
+  }
+  const size_t pk_w1 = T * size_t(pk_rows(int64_t(kD))) * D, pk_w2 = T * size_t(pk_rows(int64_t(D))) * kD;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (size_t n = 0; n < Ls; ++n) {
+    uint16_t* dst = static_cast<uint16_t*>(packed) + n * (pk_w1 + pk_w2);
+    hipError_t e = launch_pack_weights(static_cast<const uint16_t*>(w->W1) + n * T * D * kD, dst, c.T, c.D, int(kD), s);
+    if (e == hipSuccess)
+      e = launch_pack_weights(static_cast<const uint16_t*>(w->W2) + n * T * kD * D, dst + pk_w1, c.T, int(kD), c.D, s);
+    if (e != hipSuccess) return fail(h, RMX_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
   return RMX_OK;
 }
 

@@ -63,6 +63,18 @@ __device__ __forceinline__ float load1(const bf16_t* p) { return bf16_to_f32(p->
 __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store1(bf16_t* p, float v) { p->bits = f32_to_bf16(v); }
 
+// ---- Packed operand layout of a bf16 matrix [rows, K], K % 32 == 0: blocks of 256 rows x
+// 32 columns (16 KB), ordered [row block][K step]; inside a block row r holds its four
+// 16-byte chunks, chunk c at position c ^ pk_swz(r).  A K step of a 256-row block is then
+// one contiguous 16 KB that lands in LDS as is, already swizzled for conflict-free 16-byte
+// fragment reads.  Rows are padded to a multiple of 256 (pk_rows, rmx_internal.h).
+__device__ __forceinline__ int pk_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+// element offset of (row, col) with col % 8 == 0: the start of a 16-byte chunk
+__device__ __forceinline__ size_t pk_off(int row, int col, int K) {
+  const int rb = row >> 8, r = row & 255, kt = col >> 5, c = (col >> 3) & 3;
+  return ((size_t(rb) * size_t(K >> 5) + size_t(kt)) << 13) + size_t(r << 5) + size_t((c ^ pk_swz(r)) << 3);
+}
+
 // ---- Token Mixing index map (H = T).  Output row h, column c takes head h of token
 // t = c / q at position r = c % q:  M[h, c] = X[t, h*q + r].  Returns the source column
 // in token t's row; *t_out receives t.  (RankMixer paper translation, section 3.3.1

@@ -252,12 +252,14 @@ __device__ __forceinline__ void mfma_tile(f32x16_t (&acc)[4][4], const TileSrc& 
 // block (transposed product): lane l holds row l % 32 and, in register 4 g + e, column
 // 8 g + 4 (l / 32) + e.  Each wave stages 32 rows x 32 NJ columns at a time through LDS
 // (16-byte writes) so that every lane then owns 8 consecutive columns of one row: 16-byte
-// global stores, and coalesced bias / residual loads.  `out_off(m)` is the element offset
-// of the output row of tile row m in C (and R), or -1 if the row does not exist.
-template <int EPI, int NI, int NJ, typename OutOff>
+// global stores, and coalesced bias / residual loads.  `row_of(m)` is the output row (in
+// group g) of tile row m, or -1 if the row does not exist; C (and R) rows are p.ldc apart
+// and groups p.sc apart, except that with PK the GELU output and the residual are in the
+// packed operand layout.
+template <int EPI, int NI, int NJ, bool PK, typename RowOf>
 __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], float* smem_f, const GemmArgs& p,
                                               const bf16_t* bias_g, int n0, int wrow0, int wcol0, int wave,
-                                              int lane, OutOff out_off) {
+                                              int lane, int g, RowOf row_of) {
   constexpr int LD = NJ * 32 + 4;     // fp32 row stride of the staging rows
   constexpr int LPR = NJ * 4;         // lanes per staged row (8 columns each)
   constexpr int RPP = 64 / LPR;       // rows per pass
@@ -287,30 +289,32 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], flo
 #pragma unroll
     for (int pass = 0; pass < 32 / RPP; ++pass) {
       const int row = pass * RPP + rsub;
-      const int64_t ooff = out_off(wrow0 + i * 32 + row);
+      const int orow = row_of(wrow0 + i * 32 + row);
       float v[8];
       const float4 x0 = *reinterpret_cast<const float4*>(st + row * LD + col8);
       const float4 x1 = *reinterpret_cast<const float4*>(st + row * LD + col8 + 4);
       v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
       v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-      if (ooff >= 0 && n_ok) {
-        const size_t off = size_t(ooff) + n;
+      if (orow >= 0 && n_ok) {
+        const size_t off = size_t(g) * size_t(p.sc) + size_t(orow) * size_t(p.ldc) + n;
+        size_t pko = 0;
+        if constexpr (PK) pko = size_t(g) * size_t(pk_rows(p.M)) * N + pk_off(orow, n, N);
         if constexpr (EPI == EPI_GELU || EPI == EPI_MOE1) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[e]);
-          store8(static_cast<bf16_t*>(p.C) + off, v);
+          store8(static_cast<bf16_t*>(p.C) + (PK ? pko : off), v);
         } else if constexpr (EPI == EPI_BIAS) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] += bias[e];
           store8(static_cast<bf16_t*>(p.C) + off, v);
         } else if constexpr (EPI == EPI_RESID) {
           float rr[8];
-          load8(static_cast<const bf16_t*>(p.R) + off, rr);
+          load8(static_cast<const bf16_t*>(p.R) + (PK ? pko : off), rr);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = v[e] + bias[e] + rr[e];
           store8(static_cast<float*>(p.C) + off, v);
         } else {
-          const float gv = p.row_gate[ooff / N];
+          const float gv = p.row_gate[orow];
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = gv * (v[e] + bias[e]);
           store8(static_cast<float*>(p.C) + off, v);
@@ -323,8 +327,102 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], flo
   __syncthreads();
 }
 
-// Dense per-token GEMM: one workgroup per tile, G * ceil(M/256) * ceil(N/256) tiles.
-template <int EPI>
+// K loop of one 256 x 256 tile over packed operands: K steps of 32 through a 3-stage ring;
+// a stage is the tile's 16 KB A block and 16 KB W^T block of that step, each copied as 16
+// contiguous 1 KB pieces (4 per wave); both fragments are plain 16-byte LDS reads.
+constexpr int PK_NS = 3;
+__device__ __forceinline__ void mfma_tile_pk(f32x16_t (&acc)[4][4], __amdgpu_buffer_rsrc_t rA,
+                                             __amdgpu_buffer_rsrc_t rW, lds_u8* smem, uint32_t lds0, int K,
+                                             int wave, int lane) {
+  const int nk = K / BK;
+  auto copy = [&](int kt, int stage, int q) {
+    kt = kt < nk ? kt : nk - 1;
+    const uint32_t sbase = lds0 + uint32_t(stage) * STAGE_BYTES;
+    const uint32_t piece = uint32_t(4 * wave + (q & 3));
+    const uint32_t voff = piece * 1024u + uint32_t(lane) * 16u;
+    if (q < 4) copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), voff, rA, kt * 16384);
+    else copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + A_STAGE_BYTES + piece * 1024u), voff, rW, kt * 16384);
+  };
+  const int wm = wave >> 1, wn = wave & 1;
+  uint32_t aoff[2][4], boff[2][4];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = kk * 2 + (lane >> 5);
+      const int m = wm * 128 + i * 32 + (lane & 31);
+      aoff[kk][i] = uint32_t(m * 64 + ((c ^ pk_swz(m)) << 4));
+      const int n = wn * 128 + i * 32 + (lane & 31);
+      boff[kk][i] = uint32_t(A_STAGE_BYTES + n * 64 + ((c ^ pk_swz(n)) << 4));
+    }
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  struct PkFrags {
+    u32x4_t a[4];  // A rows of the 4 row blocks: 8 bf16 each
+    u32x4_t b[4];  // W^T rows (output columns) of the 4 column blocks: 8 bf16 each
+  };
+  auto read_frags = [&](PkFrags& f, const lds_u8* sp, int kk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const lds_u32x4*>(sp + aoff[kk][i]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const lds_u32x4*>(sp + boff[kk][j]);
+  };
+  auto mm = [&](const PkFrags& f, int i, int j) {
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.b[j]),
+                                                        __builtin_bit_cast(bf16x8_t, f.a[i]), acc[i][j], 0, 0, 0);
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // prologue: steps 0..PK_NS-1; wait for step 0 (8 loads per step)
+#pragma unroll
+  for (int st = 0; st < PK_NS; ++st)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) copy(st, st, q);
+  asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  PkFrags f0, f1;
+  read_frags(f0, smem, 0);
+  int stage = 0;
+  for (int it = 0; it < nk; ++it) {
+    const lds_u8* sp = smem + stage * STAGE_BYTES;
+    const int nstage = stage + 1 == PK_NS ? 0 : stage + 1;
+    read_frags(f1, sp, 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mm(f0, i, j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
+    // every read of this stage has returned; after the barrier step it+1 is visible (the 8
+    // loads of the step after it may be outstanding) and this stage takes step it+PK_NS
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(f0, smem + nstage * STAGE_BYTES, 0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      mm(f1, q >> 1, (q & 1) * 2);
+      mm(f1, q >> 1, (q & 1) * 2 + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      copy(it + PK_NS, stage, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    stage = nstage;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// Dense per-token GEMM: one workgroup per tile, G * ceil(M/256) * ceil(N/256) tiles; PK:
+// operands in the packed layout.
+template <int EPI, bool PK>
 __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem_g[NS * STAGE_BYTES];
   lds_u8* const smem = (lds_u8*)smem_g;  // the generic pointer of a __shared__ array is in LDS
@@ -345,25 +443,33 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
   const int nt = in_band / bm, mt = band * TILE_BAND + (in_band - (in_band / bm) * bm);
   const int m0 = mt * BM, n0 = nt * BN;
 
-  // Slices are < 2^31 bytes (checked at launch); an offset equal to the slice size is out
-  // of range whether or not the uniform offset takes part in the range check.
-  const uint32_t lda = uint32_t(p.lda);
-  const uint32_t bytesA = (uint32_t(M - 1) * lda + uint32_t(K)) * 2u, bytesW = uint32_t(K) * uint32_t(N) * 2u;
-  TileSrc ts;
-  ts.rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(g) * size_t(p.sa), bytesA);
-  ts.rW = make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * K * N, bytesW);
-  tile_offsets(ts, wave, lane, n0, N,
-               [&](int r, int cbytes) {
-                 return (m0 + r < M) ? uint32_t(m0 + r) * lda * 2u + uint32_t(cbytes) : bytesA;
-               },
-               bytesW);
   f32x16_t acc[4][4];
-  mfma_tile(acc, ts, smem, lds0, K, N, wave, lane);
+  if constexpr (PK) {
+    // the tile's A blocks (row block mt) and W^T blocks (row block nt): K/32 x 16 KB each
+    const uint32_t blk = uint32_t(K / BK) * 16384u;
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(static_cast<const uint16_t*>(p.A) + (size_t(g) * nMt + mt) * (size_t(blk) / 2), blk);
+    const __amdgpu_buffer_rsrc_t rW =
+        make_rsrc(static_cast<const uint16_t*>(p.W) + (size_t(g) * nNt + nt) * (size_t(blk) / 2), blk);
+    mfma_tile_pk(acc, rA, rW, smem, lds0, K, wave, lane);
+  } else {
+    // Slices are < 2^31 bytes (checked at launch); an offset equal to the slice size is out
+    // of range whether or not the uniform offset takes part in the range check.
+    const uint32_t lda = uint32_t(p.lda);
+    const uint32_t bytesA = (uint32_t(M - 1) * lda + uint32_t(K)) * 2u, bytesW = uint32_t(K) * uint32_t(N) * 2u;
+    TileSrc ts;
+    ts.rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(g) * size_t(p.sa), bytesA);
+    ts.rW = make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * K * N, bytesW);
+    tile_offsets(ts, wave, lane, n0, N,
+                 [&](int r, int cbytes) {
+                   return (m0 + r < M) ? uint32_t(m0 + r) * lda * 2u + uint32_t(cbytes) : bytesA;
+                 },
+                 bytesW);
+    mfma_tile(acc, ts, smem, lds0, K, N, wave, lane);
+  }
   const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
-  tile_epilogue<EPI, 4, 4>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, (wave >> 1) * 128,
-                           (wave & 1) * 128, wave, lane, [&](int m) -> int64_t {
-                             return m0 + m < M ? int64_t(g) * p.sc + int64_t(m0 + m) * p.ldc : -1;
-                           });
+  tile_epilogue<EPI, 4, 4, PK>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, (wave >> 1) * 128,
+                               (wave & 1) * 128, wave, lane, g, [&](int m) { return m0 + m < M ? m0 + m : -1; });
 }
 
 // Sparse-MoE grouped GEMM.  Group g has rows group_start[g] .. group_start[g+1]-1 of the
@@ -426,10 +532,9 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_moe(GemmArgs p) {
     f32x16_t acc[4][4];
     mfma_tile(acc, ts, smem, lds0, K, N, wave, lane);
     const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
-    tile_epilogue<EPI, 4, 4>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, (wave >> 1) * 128,
-                             (wave & 1) * 128, wave, lane, [&](int m) -> int64_t {
-                               return m0 + m < rows ? int64_t(row0 + m0 + m) * N : -1;
-                             });
+    tile_epilogue<EPI, 4, 4, false>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, (wave >> 1) * 128,
+                                    (wave & 1) * 128, wave, lane, 0,
+                                    [&](int m) { return m0 + m < rows ? row0 + m0 + m : -1; });
   }
 }
 
@@ -445,7 +550,7 @@ constexpr int SM_A_BYTES = SM_BM * BK * 2;                 // 4 KB, rows of 64 B
 constexpr int SM_STAGE_BYTES = SM_A_BYTES + BK * BN * 2;   // + 16 KB
 constexpr int SM_COPIES = 5;
 
-template <int EPI>
+template <int EPI, bool PK>
 __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem_g[NS * SM_STAGE_BYTES];
   lds_u8* const smem = (lds_u8*)smem_g;
@@ -458,15 +563,27 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
   const int rem = id - g * nMt * nNt;
   const int nt = rem / nMt, mt = rem - nt * nMt;
   const int m0 = mt * SM_BM, n0 = nt * BN;
+  const int nk = K / BK;
 
-  const uint32_t lda = uint32_t(p.lda);
-  const uint32_t bytesA = (uint32_t(M - 1) * lda + uint32_t(K)) * 2u, bytesW = uint32_t(K) * uint32_t(N) * 2u;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(g) * size_t(p.sa), bytesA);
-  const __amdgpu_buffer_rsrc_t rW = make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * K * N, bytesW);
-  // copy 0: A rows 16 w .. 16 w + 15 (lane q takes chunk q % 4 of row q / 4, swizzled);
-  // copies 1..4: W k rows 8 w + 2 (c - 1) and +1, as in the 256 x 256 kernel
+  __amdgpu_buffer_rsrc_t rA, rW;
+  // row-major operands: copy 0 takes A rows 16 w .. 16 w + 15 (lane q takes chunk q % 4 of
+  // row q / 4, swizzled), copies 1..4 W k rows 8 w + 2 (c - 1) and +1, as in the 256 x 256
+  // kernel.  Packed operands: copy 0 is piece w of the 4 KB of the tile's 64 A rows in the
+  // step's 16 KB block, copies 1..4 pieces 4 w .. 4 w + 3 of the 16 KB W^T block.
   uint32_t offA, offW[4];
-  {
+  if constexpr (PK) {
+    const uint32_t blk = uint32_t(nk) * 16384u;
+    const int64_t row_blocks = pk_rows(M) / 256;
+    rA = make_rsrc(static_cast<const uint16_t*>(p.A) + (size_t(g) * row_blocks + m0 / 256) * (size_t(blk) / 2), blk);
+    rW = make_rsrc(static_cast<const uint16_t*>(p.W) + (size_t(g) * nNt + nt) * (size_t(blk) / 2), blk);
+    offA = uint32_t(m0 % 256) * 64u + uint32_t(wave) * 1024u + uint32_t(lane) * 16u;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) offW[a] = uint32_t(4 * wave + a) * 1024u + uint32_t(lane) * 16u;
+  } else {
+    const uint32_t lda = uint32_t(p.lda);
+    const uint32_t bytesA = (uint32_t(M - 1) * lda + uint32_t(K)) * 2u, bytesW = uint32_t(K) * uint32_t(N) * 2u;
+    rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(g) * size_t(p.sa), bytesA);
+    rW = make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * K * N, bytesW);
     const int r = 16 * wave + (lane >> 2);
     const int c = (lane & 3) ^ swz_a(r);
     offA = (m0 + r < M) ? uint32_t(m0 + r) * lda * 2u + uint32_t(c * 16) : bytesA;
@@ -477,20 +594,28 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
       offW[a] = col < N ? (uint32_t(kr) * uint32_t(N) + uint32_t(col)) * 2u : bytesW;
     }
   }
-  const int nk = K / BK;
   auto copy = [&](int kt, int stage, int q) {
     kt = kt < nk ? kt : nk - 1;
     const uint32_t sbase = lds0 + uint32_t(stage) * SM_STAGE_BYTES;
-    if (q == 0) {
-      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + uint32_t(16 * wave) * 64u), offA, rA, kt * BK * 2);
+    if constexpr (PK) {
+      if (q == 0) {
+        copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + uint32_t(wave) * 1024u), offA, rA, kt * 16384);
+      } else {
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(sbase + SM_A_BYTES + uint32_t(4 * wave + q - 1) * 1024u);
+        copy_to_lds(dst, offW[q - 1], rW, kt * 16384);
+      }
     } else {
-      const uint32_t dst =
-          __builtin_amdgcn_readfirstlane(sbase + SM_A_BYTES + uint32_t(8 * wave + 2 * (q - 1)) * 512u);
-      copy_to_lds(dst, offW[q - 1], rW, kt * BK * N * 2);
+      if (q == 0) {
+        copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + uint32_t(16 * wave) * 64u), offA, rA, kt * BK * 2);
+      } else {
+        const uint32_t dst =
+            __builtin_amdgcn_readfirstlane(sbase + SM_A_BYTES + uint32_t(8 * wave + 2 * (q - 1)) * 512u);
+        copy_to_lds(dst, offW[q - 1], rW, kt * BK * N * 2);
+      }
     }
   };
 
-  uint32_t aoff[2][2], boff[2];
+  uint32_t aoff[2][2], boff[2][2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -498,29 +623,34 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
       const int m = i * 32 + (lane & 31);
       const int c = kk * 2 + (lane >> 5);
       aoff[kk][i] = uint32_t(m * 64 + ((c ^ swz_a(m)) << 4));
+      if constexpr (PK) {
+        const int n = wave * 64 + i * 32 + (lane & 31);
+        boff[kk][i] = uint32_t(SM_A_BYTES + n * 64 + ((c ^ pk_swz(n)) << 4));
+      } else {
+        const int kb = 8 * (lane >> 5) + ((lane & 15) >> 2);
+        const int n = wave * 64 + i * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        boff[kk][i] = uint32_t(SM_A_BYTES + kb * 512 + (((n >> 3) ^ swz_w(kb)) << 4) + (n & 7) * 2);
+      }
     }
-  {
-    const int kb = 8 * (lane >> 5) + ((lane & 15) >> 2);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = wave * 64 + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      boff[j] = uint32_t(SM_A_BYTES + kb * 512 + (((n >> 3) ^ swz_w(kb)) << 4) + (n & 7) * 2);
-    }
-  }
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
   typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
   struct SmFrags {
     u32x4_t a[2];
-    u32x2_t b[4];
+    u32x4_t b[2];  // W columns of the 2 column blocks: 8 bf16 each
   };
   auto read_frags = [&](SmFrags& f, const lds_u8* sp, int kk) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) f.a[i] = *reinterpret_cast<const lds_u32x4*>(sp + aoff[kk][i]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const lds_u8* q = sp + boff[j] + kk * 16 * 512;
-      f.b[2 * j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)q));
-      f.b[2 * j + 1] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * 512)));
+      if constexpr (PK) {
+        f.b[j] = *reinterpret_cast<const lds_u32x4*>(sp + boff[kk][j]);
+      } else {
+        const lds_u8* q = sp + boff[0][j] + kk * 16 * 512;
+        const u32x2_t lo = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)q));
+        const u32x2_t hi = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * 512)));
+        f.b[j] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+      }
     }
   };
   f32x16_t acc[2][2];
@@ -528,11 +658,9 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        u32x2_t both[2] = {f.b[2 * j], f.b[2 * j + 1]};
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(both),
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.b[j]),
                                                             __builtin_bit_cast(bf16x8_t, f.a[i]), acc[i][j], 0, 0, 0);
-      }
   };
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -572,10 +700,8 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
-  tile_epilogue<EPI, 2, 2>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, 0, wave * 64, wave, lane,
-                           [&](int m) -> int64_t {
-                             return m0 + m < M ? int64_t(g) * p.sc + int64_t(m0 + m) * p.ldc : -1;
-                           });
+  tile_epilogue<EPI, 2, 2, PK>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, 0, wave * 64, wave, lane, g,
+                               [&](int m) { return m0 + m < M ? m0 + m : -1; });
 }
 
 // --------------------------------------------------------------- generic kernel
@@ -658,8 +784,12 @@ bool gemm_moe_supported(int N, int K, int64_t a_rows) {
          uint64_t(a_rows) * N * 2 < lim;
 }
 
-hipError_t launch_gemm_moe(int epi, const GemmArgs& a, hipStream_t stream) {
-  if (a.G == 0) return hipSuccess;
+hipError_t launch_gemm_moe(int epi, const GemmArgs& args, hipStream_t stream) {
+  if (args.G == 0) return hipSuccess;
+  GemmArgs a = args;  // outputs are the compacted rows [rows, N]
+  a.ldc = a.N;
+  a.sc = 0;
+  a.packed = 0;
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -671,6 +801,59 @@ hipError_t launch_gemm_moe(int epi, const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+namespace {
+
+template <bool PK>
+hipError_t launch_dense_mfma(int epi, const GemmArgs& a, hipStream_t stream) {
+  if (a.M <= GEMM_SMALL_M) {
+    const int tiles = a.G * ((a.M + SM_BM - 1) / SM_BM) * ((a.N + BN - 1) / BN);
+    if (epi == EPI_GELU)
+      hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_GELU, PK>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+    else if (epi == EPI_BIAS && !PK)
+      hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_BIAS, false>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_RESID, PK>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+    return hipGetLastError();
+  }
+  const int tiles = a.G * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  if (epi == EPI_GELU)
+    hipLaunchKernelGGL((gemm_bf16_mfma<EPI_GELU, PK>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+  else if (epi == EPI_BIAS && !PK)
+    hipLaunchKernelGGL((gemm_bf16_mfma<EPI_BIAS, false>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_bf16_mfma<EPI_RESID, PK>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+// W [G][K][N] -> W^T packed [G][pk_rows(N) x K]: one thread per 16-byte chunk of the output
+// (8 consecutive k of one output row n), padding rows zero.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const bf16_t* __restrict__ W, bf16_t* __restrict__ out,
+                                                           int G, int K, int N) {
+  const int64_t rows = pk_rows(N);
+  const int64_t chunks = int64_t(G) * rows * (K / 8);
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < chunks; i += int64_t(gridDim.x) * blockDim.x) {
+    const int kc = int(i % (K / 8));
+    const int64_t gr = i / (K / 8);
+    const int n = int(gr % rows);
+    const int g = int(gr / rows);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = n < N ? load1(W + (size_t(g) * K + size_t(kc) * 8 + e) * N + n) : 0.f;
+    store8(out + size_t(g) * size_t(rows) * K + pk_off(n, kc * 8, K), v);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack_weights(const void* W, void* out, int G, int K, int N, hipStream_t stream) {
+  if (G == 0 || N == 0) return hipSuccess;
+  const int64_t chunks = int64_t(G) * pk_rows(N) * (K / 8);
+  const int64_t want = (chunks + 255) / 256;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(unsigned(want < 65536 ? want : 65536)), dim3(256), 0, stream,
+                     static_cast<const bf16_t*>(W), static_cast<bf16_t*>(out), G, K, N);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& args, hipStream_t stream) {
   if (args.G == 0 || args.M == 0 || args.N == 0) return hipSuccess;
   GemmArgs a = args;
@@ -678,27 +861,12 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& args, hipStream_t str
   if (a.ldc == 0) a.ldc = a.N;
   if (a.sa == 0) a.sa = int64_t(a.M) * a.lda;
   if (a.sc == 0) a.sc = int64_t(a.M) * a.ldc;
-  const bool mfma = gemm_uses_mfma(dtype, a.M, a.N, a.K, a.lda) && (a.sa % 8) == 0;
-  if (mfma && a.M <= GEMM_SMALL_M) {
-    const int tiles = a.G * ((a.M + SM_BM - 1) / SM_BM) * ((a.N + BN - 1) / BN);
-    if (epi == EPI_GELU)
-      hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_GELU>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
-    else if (epi == EPI_BIAS)
-      hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_BIAS>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_RESID>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
-    return hipGetLastError();
+  if (a.packed) {
+    // packed operands exist only for the MFMA kernels, and not for the bias-only epilogue
+    if (!gemm_uses_mfma(dtype, a.M, a.N, a.K) || epi == EPI_BIAS) return hipErrorInvalidValue;
+    return launch_dense_mfma<true>(epi, a, stream);
   }
-  if (mfma) {
-    const int tiles = a.G * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    if (epi == EPI_GELU)
-      hipLaunchKernelGGL((gemm_bf16_mfma<EPI_GELU>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
-    else if (epi == EPI_BIAS)
-      hipLaunchKernelGGL((gemm_bf16_mfma<EPI_BIAS>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_bf16_mfma<EPI_RESID>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
-    return hipGetLastError();
-  }
+  if (gemm_uses_mfma(dtype, a.M, a.N, a.K, a.lda) && (a.sa % 8) == 0) return launch_dense_mfma<false>(epi, a, stream);
   dim3 grid((a.N + GT - 1) / GT, (a.M + GT - 1) / GT, a.G);
   if (dtype == DT_BF16) {
     if (epi == EPI_GELU)

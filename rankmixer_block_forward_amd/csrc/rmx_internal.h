@@ -19,6 +19,9 @@ inline int dtype_size(int dt) { return dt == DT_BF16 ? 2 : 4; }
 // S is written token-major [T, B, D] (dtype), the layout the grouped GEMMs read.
 enum RowsMode { ROWS_FIRST = 0, ROWS_MID = 1, ROWS_FINAL = 2 };
 
+// Rows of one group of a matrix in the packed operand layout (blocks of 256 rows).
+__host__ __device__ inline int64_t pk_rows(int64_t rows) { return (rows + 255) / 256 * 256; }
+
 struct RowsArgs {
   const void* in;
   const void* ln2_g;
@@ -30,6 +33,7 @@ struct RowsArgs {
   void* xl;
   int B, T, D;
   float eps;
+  int s_packed;  // S in the packed operand layout, token t at S + t * pk_rows(B) * D
 };
 
 // Largest D the row kernel's per-lane registers hold.
@@ -106,6 +110,10 @@ struct GemmArgs {
   // Dense kernels only (0 = contiguous): elements between rows of A, between rows of C
   // (and R), between groups of A, between groups of C (and R).
   int64_t lda, ldc, sa, sc;
+  // Dense kernels only: A [G][pk_rows(M) x K] and W^T [G][pk_rows(N) x K] in the packed
+  // operand layout; EPI_GELU then writes C packed ([G][pk_rows(M) x N]) and EPI_RESID reads
+  // R packed, C stays row-major.  Strides are ignored.
+  int packed;
 };
 // Rows per token up to which the dense launch uses 64-row tiles.
 constexpr int GEMM_SMALL_M = 64;
@@ -118,5 +126,8 @@ hipError_t launch_gemm_moe(int epi, const GemmArgs& a, hipStream_t stream);
 bool gemm_moe_supported(int N, int K, int64_t a_rows);
 hipError_t gemm_init();
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t stream);
+// W [G][K][N] (bf16, row-major) -> W^T [G][pk_rows(N) x K] in the packed operand layout
+// (padding rows zero); K % 32 == 0.
+hipError_t launch_pack_weights(const void* W, void* out, int G, int K, int N, hipStream_t stream);
 
 }  // namespace rmx

@@ -203,6 +203,17 @@ __global__ __launch_bounds__(64 * rows_max_waves(NC, MODE)) void rows_kernel(Row
     }
     wave_layernorm<W, NC>(r, lane, nchunks, D, static_cast<const T*>(a.ln1_g),
                           static_cast<const T*>(a.ln1_b), a.eps);
+    if constexpr (W == 8) {
+      if (a.s_packed) {
+        T* dst = static_cast<T*>(a.S) + size_t(h) * size_t(pk_rows(B)) * D;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const int c = lane + 64 * i;
+          if (c < nchunks) storew<W>(dst + pk_off(b, c * W, D), r[i]);
+        }
+        continue;
+      }
+    }
     T* dst = static_cast<T*>(a.S) + (size_t(h) * B + b) * D;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {

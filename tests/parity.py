@@ -38,13 +38,17 @@ def sample_rows(B, n, seed=0):
     return np.unique(np.concatenate([[0, B - 1], mid]))
 
 
-def run_gpu(cfg, inp, with_xl=True, handle=None):
-    """Forward of synth inputs through the library; returns (o, X_L) as float32 arrays."""
+def run_gpu(cfg, inp, with_xl=True, handle=None, packed=False):
+    """Forward of synth inputs through the library; returns (o, X_L) as float32 arrays.
+    packed: run on weights prepared with rmx_pack_weights (W1/W2 then not passed)."""
     import torch
     import rankmixer_block_forward_amd as rmx
     X, w = rmx.upload(inp)
     h = handle or rmx.Handle.for_config(cfg, max_batch=X.shape[0])
     try:
+        if packed:
+            w = dict(w, packed=h.pack_weights(w))
+            del w["W1"], w["W2"]
         out = torch.full((X.shape[0], cfg.D), float("nan"), dtype=torch.float32, device=X.device)
         xl = torch.full_like(X, float("nan")) if with_xl else None
         h.forward(X, w, out=out, xl_out=xl)

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = rmx.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.rmx_abi_version() == 1
+    assert lib.rmx_abi_version() == 2
 
 
 def test_status_strings_and_kernel_names():
@@ -87,3 +87,9 @@ def test_tokenize_host_side_rejections():
     assert "dtype" in lib.rmx_last_error(None).decode()
     assert lib.rmx_tokenize(None, None, None, None, 0, 2, 4, 8, 1, None) == binding.RMX_OK  # B = 0
     assert lib.rmx_tokenize(None, None, None, None, -1, 2, 4, 8, 1, None) == binding.RMX_ERR_INVALID_ARG
+
+
+def test_packed_weights_host_side():
+    lib = rmx.load_library()
+    assert lib.rmx_packed_weights_bytes(None) == 0
+    assert lib.rmx_pack_weights(None, None, 1, None, 0, None) == binding.RMX_ERR_INVALID_ARG

@@ -128,6 +128,48 @@ def test_small_batch_deterministic():
     check(cfg, o1[rows], xl1[rows], o_ref, xl_ref, "bf16 B=33")
 
 
+@pytest.mark.parametrize("B,T,D,k,L", [
+    (300, 4, 256, 4, 2),   # 256-row tiles, ragged rows
+    (77, 5, 320, 2, 1),    # ragged column tiles (kD = 640, D = 320)
+    (33, 8, 256, 4, 2),    # 64-row tiles
+    (64, 8, 512, 4, 1),    # largest batch on the 64-row tiles
+    (65, 8, 512, 4, 1),    # smallest batch on the 256-row tiles
+    (1, 16, 768, 4, 2),    # one sample
+])
+def test_prepared_weights_bit_identical(B, T, D, k, L):
+    """Weights prepared by rmx_pack_weights (and the packed S and H they bring) give the
+    same bits as the row-major path, and match the oracle."""
+    cfg = synth.Config("pk", B=B, T=T, D=D, k=k, L=L, dtype="bf16", bias_std=0.02)
+    inp = synth.make_inputs(cfg, seed=B + 3 * D)
+    o1, xl1 = run_gpu(cfg, inp)
+    o2, xl2 = run_gpu(cfg, inp, packed=True)
+    assert np.array_equal(o1, o2) and np.array_equal(xl1, xl2)
+    rows = sample_rows(B, 32)
+    o_ref, xl_ref = run_oracle(cfg, inp, rows)
+    check(cfg, o2[rows], xl2[rows], o_ref, xl_ref, f"prepared {B}x{T}x{D} k{k} L{L}")
+
+
+def test_prepared_weights_1b_full_size():
+    cfg = synth.B1
+    inp = synth.make_inputs(cfg, seed=0)
+    o1, _ = run_gpu(cfg, inp, with_xl=False)
+    o2, xl2 = run_gpu(cfg, inp, packed=True)
+    assert np.array_equal(o1, o2)
+    rows = sample_rows(cfg.B, 4)
+    o_ref, xl_ref = run_oracle(cfg, inp, rows)
+    check(cfg, o2[rows], xl2[rows], o_ref, xl_ref, "prepared 1B B=2048")
+
+
+def test_prepared_weights_rejected_where_unsupported():
+    rmx = _rmx()
+    from rankmixer_block_forward_amd import binding
+    for cfg in (synth.TINY, synth.Config("moe", B=8, T=4, D=64, k=2, L=1, dtype="bf16", E=2, moe_hidden=64)):
+        with rmx.Handle.for_config(cfg, max_batch=8) as h:
+            assert h.packed_weights_bytes() == 0
+            with pytest.raises(binding.RmxError):
+                h.pack_weights({"W1": None, "W2": None})
+
+
 def test_rankmixer_100m_full_size():
     cfg = synth.M100
     inp = synth.make_inputs(cfg, seed=0)
