@@ -1,7 +1,9 @@
-"""fp64 CPU oracle of the RankMixer block forward (test infrastructure only).
+"""fp64 CPU oracle of the RankMixer block forward and backward (test infrastructure only).
 
 Imported only by the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU
 baseline; the GPU library never imports it and shares no code with it.
 """
 from .rmx_oracle import (tokenize, token_mix, layer_norm, gelu, pffn, moe_gates, moe_pffn,  # noqa: F401
                          block, forward)
+from .rmx_backward import (gelu_grad, layer_norm_backward, token_mix_backward,  # noqa: F401
+                           pffn_backward, block_backward, backward, bce_logit_head)
