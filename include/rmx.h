@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RMX_ABI_VERSION 2
+#define RMX_ABI_VERSION 3
 
 typedef struct rmx_handle rmx_handle; /* opaque, owned by the library */
 
@@ -166,6 +166,53 @@ rmx_status rmx_pack_weights(rmx_handle* h, const rmx_weights* w, int32_t L, void
 rmx_status rmx_tokenize(const void* E, const void* Wp, const void* bp, void* X, int64_t B, int32_t T,
                         int32_t d, int32_t D, int32_t dtype, void* stream);
 
+/* Training: the forward pass that keeps the activations the backward pass needs, and the
+ * backward pass ("RankMixer 详解（1）：特征分组与完整计算流程", section 5.2).  Dense handles
+ * (moe_experts == 0) only; the weights are read from W1 and W2 (w->packed must be NULL).
+ *
+ * rmx_saved_bytes: bytes of the saved activations for B samples (0 for a Sparse-MoE handle,
+ * a NULL handle or B < 0).  Per block: S [T, B, D] (dtype), the pre-activations
+ * U = S W1 + b1 and the hidden H = GELU(U) [T, B, kD] (dtype), the pre-LN2 rows
+ * [T, B, D] (fp32), each padded to 256 bytes.
+ *
+ * rmx_block_forward_train: rmx_block_forward (same out, bit for bit) that also writes the
+ * saved activations to `saved` (device, `saved_bytes` >= rmx_saved_bytes(h, B)).
+ *
+ * rmx_block_backward: given g_out [B, D] (device, fp32), the gradient of a loss with respect
+ * to out, writes the gradient of that loss with respect to X, dX [B, T, D] (device, fp32),
+ * and with respect to every parameter, summed over the B samples (scale g_out by 1/B for a
+ * mean loss), into `grads` (device, fp32, all required, shaped like the weights):
+ *   dW1 [L, T, D, kD]  db1 [L, T, kD]  dW2 [L, T, kD, D]  db2 [L, T, D]
+ *   dln1_g, dln1_b, dln2_g, dln2_b [L, D]
+ * X, B, w and `saved` must be those of the rmx_block_forward_train call that filled
+ * `saved`, which stays unchanged.  The gradients of the pooled output pass through the
+ * mean pool, then for each block from the last: LayerNorm backward, the per-token FFN
+ * backward (GELU'(u) = Phi(u) + u phi(u)), the second residual, LayerNorm backward, and
+ * the first residual with the mixing transpose, dX = (P^T + I) g.  Products run on the
+ * matrix cores for bf16 (operands rounded to bf16: the gradients of the pre-LN2 rows and of
+ * the pre-activations), accumulate in fp32; everything else is fp32.
+ * The first backward call on a handle allocates its backward workspace (for max_batch
+ * samples; RMX_ERR_OUT_OF_MEMORY if that fails).  Outputs must not overlap the inputs
+ * or each other.  Limits: D <= 2048 when D % 8 == 0 and (D/T) % 8 == 0, else D <= 512;
+ * T*D*sizeof(dtype) <= 96 KiB.  B == 0 enqueues nothing. */
+typedef struct {
+  float* dW1;
+  float* db1;
+  float* dW2;
+  float* db2;
+  float* dln1_g;
+  float* dln1_b;
+  float* dln2_g;
+  float* dln2_b;
+} rmx_grads;
+
+size_t rmx_saved_bytes(const rmx_handle* h, int64_t B);
+rmx_status rmx_block_forward_train(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w, int32_t L,
+                                   int32_t k, float* out, void* saved, size_t saved_bytes, void* stream);
+rmx_status rmx_block_backward(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w, int32_t L,
+                              int32_t k, const void* saved, size_t saved_bytes, const float* g_out, float* dX,
+                              const rmx_grads* grads, void* stream);
+
 /* Kernel-level timing.  While enabled, every kernel the handle launches is bracketed by
  * a pair of HIP events recorded on the caller's stream; rmx_profile_read() waits for the
  * recorded events and returns, per kernel kind, the summed duration in ms and the
@@ -180,7 +227,13 @@ typedef enum {
   RMX_KERNEL_MOE_FFN1 = 5, /* expert first layer (gathered rows) + GELU */
   RMX_KERNEL_MOE_FFN2 = 6, /* expert second layer, gate-weighted */
   RMX_KERNEL_MOE_COMBINE = 7, /* sum of expert outputs + S -> pre-LN2 rows */
-  RMX_KERNEL_COUNT = 8
+  RMX_KERNEL_BWD_ROWS = 8, /* backward: LayerNorm backward, mixing transpose, residuals */
+  RMX_KERNEL_BWD_DU = 9,   /* backward: per-token gY W2^T * GELU'(U) -> gU */
+  RMX_KERNEL_BWD_DS = 10,  /* backward: per-token gU W1^T + gY -> gradient of S */
+  RMX_KERNEL_BWD_DW1 = 11, /* backward: per-token S^T gU -> dW1 */
+  RMX_KERNEL_BWD_DW2 = 12, /* backward: per-token H^T gY -> dW2 */
+  RMX_KERNEL_BWD_SUMS = 13, /* backward: batch sums of the bias and LayerNorm gradients */
+  RMX_KERNEL_COUNT = 14
 } rmx_kernel_kind;
 
 rmx_status rmx_profile_enable(rmx_handle* h, int32_t enable);

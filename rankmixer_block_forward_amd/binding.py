@@ -16,12 +16,13 @@ LIB_PATH = os.path.join(PKG, "librmx.so")
 
 RMX_OK, RMX_ERR_INVALID_ARG, RMX_ERR_UNSUPPORTED, RMX_ERR_OUT_OF_MEMORY, RMX_ERR_HIP = range(5)
 RMX_FP32, RMX_BF16 = 0, 1
-KERNEL_COUNT = 8
+KERNEL_COUNT = 14
 
 # Every symbol include/rmx.h declares.
 EXPORTS = (
     "rmx_create", "rmx_destroy", "rmx_block_forward", "rmx_block_forward_ex", "rmx_token_mix",
     "rmx_tokenize", "rmx_packed_weights_bytes", "rmx_pack_weights",
+    "rmx_saved_bytes", "rmx_block_forward_train", "rmx_block_backward",
     "rmx_profile_enable", "rmx_profile_read", "rmx_profile_reset", "rmx_kernel_name",
     "rmx_status_string", "rmx_last_error", "rmx_abi_version",
 )
@@ -48,6 +49,13 @@ class rmx_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
 
 
+GRAD_NAMES = ("W1", "b1", "W2", "b2", "ln1_g", "ln1_b", "ln2_g", "ln2_b")
+
+
+class rmx_grads(ctypes.Structure):
+    _fields_ = [("d" + n, ctypes.c_void_p) for n in GRAD_NAMES]
+
+
 _lib = None
 
 
@@ -70,6 +78,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rmx_packed_weights_bytes.argtypes = [vp]
     lib.rmx_packed_weights_bytes.restype = ctypes.c_size_t
     lib.rmx_pack_weights.argtypes = [vp, ctypes.POINTER(rmx_weights), i32, vp, ctypes.c_size_t, vp]
+    lib.rmx_saved_bytes.argtypes = [vp, i64]
+    lib.rmx_saved_bytes.restype = ctypes.c_size_t
+    lib.rmx_block_forward_train.argtypes = [vp, vp, i64, ctypes.POINTER(rmx_weights), i32, i32, vp, vp,
+                                            ctypes.c_size_t, vp]
+    lib.rmx_block_backward.argtypes = [vp, vp, i64, ctypes.POINTER(rmx_weights), i32, i32, vp, ctypes.c_size_t,
+                                       vp, vp, ctypes.POINTER(rmx_grads), vp]
     lib.rmx_profile_enable.argtypes = [vp, i32]
     lib.rmx_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
                                      ctypes.POINTER(i64)]
@@ -83,7 +97,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rmx_abi_version.restype = i32
     for name in EXPORTS:
         if name not in ("rmx_kernel_name", "rmx_status_string", "rmx_last_error", "rmx_abi_version",
-                        "rmx_packed_weights_bytes"):
+                        "rmx_packed_weights_bytes", "rmx_saved_bytes"):
             getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -210,6 +224,59 @@ class Handle:
             _ptr(out, "out"), _ptr(xl_out, "xl_out"), _ptr(gate_out, "gate_out"), _stream(stream))
         _check(st, self._h)
         return out
+
+    # ---- training
+    def saved_bytes(self, B: int) -> int:
+        """Bytes of the activations rmx_block_forward_train keeps for B samples."""
+        return int(self._lib.rmx_saved_bytes(self._h, B))
+
+    def forward_train(self, X, weights: dict, out=None, saved=None, stream=None):
+        """The forward pass that also keeps what the backward needs: returns (out, saved),
+        saved a device byte tensor to hand to backward() unchanged."""
+        import torch
+        c = self.cfg
+        B = X.shape[0]
+        _ptr(X, "X", self.dtype, (B, c.T, c.D))
+        if out is None:
+            out = torch.empty((B, c.D), dtype=torch.float32, device=X.device)
+        _ptr(out, "out", torch.float32, (B, c.D))
+        nbytes = self.saved_bytes(B)
+        if saved is None:
+            saved = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X.device)
+        _ptr(saved, "saved", torch.uint8)
+        ws = self._weights(weights)
+        _check(self._lib.rmx_block_forward_train(self._h, _ptr(X, "X"), B, ctypes.byref(ws), c.L, c.k,
+                                                 _ptr(out, "out"), _ptr(saved, "saved"), saved.numel(),
+                                                 _stream(stream)), self._h)
+        return out, saved
+
+    def backward(self, X, weights: dict, saved, g_out, dX=None, grads: dict | None = None, stream=None):
+        """Gradients of a loss whose gradient with respect to out is g_out [B, D] (fp32):
+        returns (dX [B, T, D] fp32, {"W1": dW1, ..., "ln2_b": dln2_b} fp32, summed over the
+        batch).  X, weights and saved are those of the forward_train call."""
+        import torch
+        c = self.cfg
+        B = X.shape[0]
+        kD = c.k * c.D
+        _ptr(X, "X", self.dtype, (B, c.T, c.D))
+        _ptr(g_out, "g_out", torch.float32, (B, c.D))
+        _ptr(saved, "saved", torch.uint8)
+        shapes = {"W1": (c.L, c.T, c.D, kD), "b1": (c.L, c.T, kD), "W2": (c.L, c.T, kD, c.D),
+                  "b2": (c.L, c.T, c.D), "ln1_g": (c.L, c.D), "ln1_b": (c.L, c.D), "ln2_g": (c.L, c.D),
+                  "ln2_b": (c.L, c.D)}
+        if dX is None:
+            dX = torch.empty((B, c.T, c.D), dtype=torch.float32, device=X.device)
+        _ptr(dX, "dX", torch.float32, (B, c.T, c.D))
+        if grads is None:
+            grads = {n: torch.empty(shp, dtype=torch.float32, device=X.device) for n, shp in shapes.items()}
+        g = rmx_grads()
+        for n in GRAD_NAMES:
+            setattr(g, "d" + n, _ptr(grads[n], "d" + n, torch.float32, shapes[n]))
+        ws = self._weights(weights)
+        _check(self._lib.rmx_block_backward(self._h, _ptr(X, "X"), B, ctypes.byref(ws), c.L, c.k,
+                                            _ptr(saved, "saved"), saved.numel(), _ptr(g_out, "g_out"),
+                                            _ptr(dX, "dX"), ctypes.byref(g), _stream(stream)), self._h)
+        return dX, grads
 
     # ---- kernel timing
     def profile_enable(self, on: bool = True):

@@ -60,6 +60,16 @@ struct rmx_handle {
   int* moe_pos = nullptr;        // [G, max_batch]
   void* moe_hidden = nullptr;    // [R, h]  bf16
   float* moe_out = nullptr;      // [R, D]  fp32
+  // Backward workspace, allocated by the first backward call (all for max_batch samples)
+  bool bwd_ready = false;
+  float* bw_gY32 = nullptr;      // [T, max_batch, D]  fp32  gradient of the pre-LN2 rows
+  void* bw_gY = nullptr;         // [T, max_batch, D]  dtype the same, a GEMM operand
+  void* bw_gU = nullptr;         // [T, max_batch, kD] dtype gradient of the pre-activations
+  float* bw_gS = nullptr;        // [T, max_batch, D]  fp32  gradient of S
+  float* bw_gR = nullptr;        // [max_batch, T, D]  fp32  row-kernel scratch
+  float* bw_part1 = nullptr;     // [2, max_batch, D]  fp32  per-sample LN1 gamma / beta gradients
+  float* bw_part2 = nullptr;     // [2, max_batch, D]  fp32  per-sample LN2 gamma / beta gradients
+  float* bw_sum = nullptr;       // column-sum scratch
   std::vector<void*> allocs;     // everything hipMalloc'd, freed by rmx_destroy
   std::string last_error;
   bool prof = false;
@@ -229,12 +239,46 @@ hipError_t run_rows(rmx_handle* h, hipStream_t s, int mode, const RowsArgs& a) {
   return e;
 }
 
-hipError_t run_gemm(rmx_handle* h, hipStream_t s, int epi, const GemmArgs& a) {
+hipError_t run_gemm(rmx_handle* h, hipStream_t s, int epi, const GemmArgs& a, int kind = -1) {
   ProfPair pp;
-  prof_begin(h, s, &pp, epi == EPI_GELU ? RMX_KERNEL_GEMM1 : RMX_KERNEL_GEMM2);
+  if (kind < 0) kind = (epi == EPI_GELU || epi == EPI_GELU_SAVE) ? RMX_KERNEL_GEMM1 : RMX_KERNEL_GEMM2;
+  prof_begin(h, s, &pp, kind);
   hipError_t e = launch_gemm(h->cfg.dtype, epi, a, s);
   prof_end(h, s, &pp);
   return e;
+}
+
+hipError_t run_rows_bwd(rmx_handle* h, hipStream_t s, int mode, const RowsBwdArgs& a) {
+  ProfPair pp;
+  prof_begin(h, s, &pp, RMX_KERNEL_BWD_ROWS);
+  hipError_t e = launch_rows_bwd(h->cfg.dtype, mode, a, s);
+  prof_end(h, s, &pp);
+  return e;
+}
+
+hipError_t run_colsum(rmx_handle* h, hipStream_t s, int dtype, const void* in, float* out, int G, int R, int N) {
+  ProfPair pp;
+  prof_begin(h, s, &pp, RMX_KERNEL_BWD_SUMS);
+  hipError_t e = launch_colsum(dtype, in, out, h->bw_sum, G, R, N, s);
+  prof_end(h, s, &pp);
+  return e;
+}
+
+// Saved activations of one block for B samples (byte offsets, each padded to 256 bytes).
+struct SavedLayout {
+  size_t S, U, H, Y, per_block;
+};
+
+SavedLayout saved_layout(const rmx_config& c, int64_t B) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t esz = dtype_size(c.dtype), rows = size_t(c.T) * size_t(B), kD = size_t(c.k) * c.D;
+  SavedLayout l;
+  l.S = 0;
+  l.U = up(rows * c.D * esz);
+  l.H = l.U + up(rows * kD * esz);
+  l.Y = l.H + up(rows * kD * esz);
+  l.per_block = l.Y + up(rows * c.D * sizeof(float));
+  return l;
 }
 
 hipError_t run_moe_route(rmx_handle* h, hipStream_t s, const MoeArgs& a) {
@@ -281,9 +325,11 @@ const char* rmx_status_string(rmx_status s) {
 const char* rmx_last_error(const rmx_handle* h) { return h ? h->last_error.c_str() : g_thread_error.c_str(); }
 
 const char* rmx_kernel_name(int32_t kind) {
-  static const char* names[RMX_KERNEL_COUNT] = {"rows_ln2_mix_ln1", "gemm1_gelu", "gemm2_residual",
-                                                "rows_ln2_pool",   "moe_gate",   "moe_ffn1",
-                                                "moe_ffn2",        "moe_combine"};
+  static const char* names[RMX_KERNEL_COUNT] = {"rows_ln2_mix_ln1", "gemm1_gelu",   "gemm2_residual",
+                                                "rows_ln2_pool",    "moe_gate",     "moe_ffn1",
+                                                "moe_ffn2",         "moe_combine",  "bwd_rows",
+                                                "bwd_gemm_dU",      "bwd_gemm_dS",  "bwd_gemm_dW1",
+                                                "bwd_gemm_dW2",     "bwd_sums"};
   return (kind >= 0 && kind < RMX_KERNEL_COUNT) ? names[kind] : "unknown";
 }
 
@@ -296,7 +342,8 @@ rmx_status rmx_create(const rmx_config* cfg, rmx_handle** out_handle) {
   int dev = -1;
   if ((st = check_device_arch(nullptr, &dev)) != RMX_OK) return st;
   hipError_t e;
-  if ((e = rows_init()) != hipSuccess || (e = gemm_init()) != hipSuccess || (e = moe_init()) != hipSuccess)
+  if ((e = rows_init()) != hipSuccess || (e = gemm_init()) != hipSuccess || (e = moe_init()) != hipSuccess ||
+      (e = rows_bwd_init()) != hipSuccess)
     return fail(nullptr, RMX_ERR_HIP, "kernel set-up failed: %s", hipGetErrorString(e));
 
   rmx_handle* h = new (std::nothrow) rmx_handle();
@@ -367,9 +414,11 @@ rmx_status rmx_destroy(rmx_handle* h) {
   return RMX_OK;
 }
 
-rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w,
-                                int32_t L, int32_t k, float* out, void* xl_out, float* gate_out,
-                                void* stream) {
+// The forward pass; with `saved` (training) it also keeps S, U, H and the pre-LN2 rows of
+// every block there instead of in the workspace.
+static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w, int32_t L,
+                               int32_t k, float* out, void* xl_out, float* gate_out, void* saved,
+                               size_t saved_bytes, void* stream) {
   if (!h) return fail(nullptr, RMX_ERR_INVALID_ARG, "handle is NULL");
   clear_error(h);
   const rmx_config& c = h->cfg;
@@ -380,7 +429,13 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
     return fail(h, RMX_ERR_INVALID_ARG, "B=%lld outside [0, max_batch=%lld]", (long long)B,
                 (long long)c.max_batch);
   const bool moe = c.moe_experts > 0;
+  const bool train = saved != nullptr;
   if (gate_out && !moe) return fail(h, RMX_ERR_INVALID_ARG, "gate_out must be NULL for a dense handle");
+  if (train && moe) return fail(h, RMX_ERR_UNSUPPORTED, "training needs a dense handle");
+  if (train && w->packed) return fail(h, RMX_ERR_INVALID_ARG, "training reads W1 and W2: packed must be NULL");
+  if (train && saved_bytes < rmx_saved_bytes(h, B))
+    return fail(h, RMX_ERR_INVALID_ARG, "saved buffer of %zu bytes, %zu needed", saved_bytes,
+                rmx_saved_bytes(h, B));
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
     (void)hipGetLastError();
@@ -394,6 +449,7 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
   if ((st = check_dev(h, X, size_t(B) * T * D * esz, dev, "X")) != RMX_OK) return st;
   if ((st = check_dev(h, out, size_t(B) * D * 4, dev, "out")) != RMX_OK) return st;
   if ((st = check_dev_opt(h, xl_out, size_t(B) * T * D * esz, dev, "xl_out")) != RMX_OK) return st;
+  if (train && (st = check_dev(h, saved, rmx_saved_bytes(h, B), dev, "saved")) != RMX_OK) return st;
   const size_t E = size_t(c.moe_experts), hid = size_t(c.moe_hidden);
   if (moe) {
     if (w->packed) return fail(h, RMX_ERR_UNSUPPORTED, "prepared weights are for dense handles");
@@ -430,6 +486,18 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
       (xl_out && overlap(xl_out, size_t(B) * T * D * esz, X, size_t(B) * T * D * esz)) ||
       (xl_out && overlap(xl_out, size_t(B) * T * D * esz, out, size_t(B) * D * 4)))
     return fail(h, RMX_ERR_INVALID_ARG, "out / xl_out overlap X or each other");
+  const SavedLayout lay = saved_layout(c, B);
+  if (train) {
+    const size_t sb = rmx_saved_bytes(h, B);
+    if (overlap(saved, sb, X, size_t(B) * T * D * esz) || overlap(saved, sb, out, size_t(B) * D * 4) ||
+        (xl_out && overlap(saved, sb, xl_out, size_t(B) * T * D * esz)))
+      return fail(h, RMX_ERR_INVALID_ARG, "saved overlaps X, out or xl_out");
+  }
+  // block n's S, hidden and pre-LN2 rows: the saved activations (training) or the workspace
+  auto blk = [&](int n, size_t off) { return static_cast<char*>(saved) + size_t(n) * lay.per_block + off; };
+  auto S_of = [&](int n) -> void* { return train ? blk(n, lay.S) : h->S; };
+  auto H_of = [&](int n) -> void* { return train ? blk(n, lay.H) : h->H; };
+  auto Y_of = [&](int n) -> float* { return train ? reinterpret_cast<float*>(blk(n, lay.Y)) : h->Y; };
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const char* bytes = nullptr;
@@ -445,12 +513,12 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
   const size_t pk_w1 = T * size_t(pk_rows(int64_t(kD))) * D, pk_w2 = T * size_t(pk_rows(int64_t(D))) * kD;
   for (int n = 0; n < c.L && e == hipSuccess; ++n) {
     RowsArgs ra{};
-    ra.in = n == 0 ? X : static_cast<const void*>(h->Y);
+    ra.in = n == 0 ? X : static_cast<const void*>(Y_of(n - 1));
     ra.ln2_g = n == 0 ? nullptr : at(w->ln2_g, size_t(n - 1) * D);
     ra.ln2_b = n == 0 ? nullptr : at(w->ln2_b, size_t(n - 1) * D);
     ra.ln1_g = at(w->ln1_g, size_t(n) * D);
     ra.ln1_b = at(w->ln1_b, size_t(n) * D);
-    ra.S = h->S;
+    ra.S = S_of(n);
     ra.B = Bi;
     ra.T = c.T;
     ra.D = c.D;
@@ -512,25 +580,26 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
     }
 
     GemmArgs g1{};
-    g1.A = h->S;
+    g1.A = S_of(n);
     g1.W = pk ? at(w->packed, size_t(n) * (pk_w1 + pk_w2)) : at(w->W1, size_t(n) * T * D * kD);
     g1.packed = pk ? 1 : 0;
     g1.bias = at(w->b1, size_t(n) * T * kD);
-    g1.C = h->H;
+    g1.C = H_of(n);
+    g1.U = train ? blk(n, lay.U) : nullptr;
     g1.G = c.T;
     g1.M = Bi;
     g1.N = int(kD);
     g1.K = c.D;
-    e = run_gemm(h, s, EPI_GELU, g1);
+    e = run_gemm(h, s, train ? EPI_GELU_SAVE : EPI_GELU, g1);
     if (e != hipSuccess) break;
 
     GemmArgs g2{};
-    g2.A = h->H;
+    g2.A = H_of(n);
     g2.W = pk ? at(w->packed, size_t(n) * (pk_w1 + pk_w2) + pk_w1) : at(w->W2, size_t(n) * T * kD * D);
     g2.packed = pk ? 1 : 0;
     g2.bias = at(w->b2, size_t(n) * T * D);
-    g2.R = h->S;
-    g2.C = h->Y;
+    g2.R = S_of(n);
+    g2.C = Y_of(n);
     g2.G = c.T;
     g2.M = Bi;
     g2.N = c.D;
@@ -539,7 +608,7 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
   }
   if (e == hipSuccess) {
     RowsArgs ra{};
-    ra.in = h->Y;
+    ra.in = Y_of(c.L - 1);
     ra.ln2_g = at(w->ln2_g, size_t(c.L - 1) * D);
     ra.ln2_b = at(w->ln2_b, size_t(c.L - 1) * D);
     ra.pool = out;
@@ -549,6 +618,245 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
     ra.D = c.D;
     ra.eps = c.ln_eps;
     e = run_rows(h, s, ROWS_FINAL, ra);
+  }
+  if (e != hipSuccess) return fail(h, RMX_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return RMX_OK;
+}
+
+rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w,
+                                int32_t L, int32_t k, float* out, void* xl_out, float* gate_out,
+                                void* stream) {
+  return forward_impl(h, X, B, w, L, k, out, xl_out, gate_out, nullptr, 0, stream);
+}
+
+size_t rmx_saved_bytes(const rmx_handle* h, int64_t B) {
+  if (!h || B < 0 || h->cfg.moe_experts > 0) return 0;
+  return size_t(h->cfg.L) * saved_layout(h->cfg, B).per_block;
+}
+
+rmx_status rmx_block_forward_train(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w, int32_t L,
+                                   int32_t k, float* out, void* saved, size_t saved_bytes, void* stream) {
+  if (!saved) {
+    if (h) clear_error(h);
+    return fail(h, RMX_ERR_INVALID_ARG, "saved is NULL");
+  }
+  return forward_impl(h, X, B, w, L, k, out, nullptr, nullptr, saved, saved_bytes, stream);
+}
+
+// The backward workspace, for max_batch samples; allocated once per handle.
+static rmx_status ensure_bwd_workspace(rmx_handle* h) {
+  if (h->bwd_ready) return RMX_OK;
+  const rmx_config& c = h->cfg;
+  const size_t esz = dtype_size(c.dtype), rows = size_t(c.T) * size_t(c.max_batch);
+  const size_t D = c.D, kD = size_t(c.k) * c.D;
+  std::vector<void*> got;
+  bool ok = true;
+  auto alloc = [&](auto** ptr, size_t bytes) {
+    if (!ok) return;
+    void* q = nullptr;
+    if (hipMalloc(&q, bytes ? bytes : 16) != hipSuccess) {
+      (void)hipGetLastError();
+      ok = false;
+      return;
+    }
+    got.push_back(q);
+    *ptr = static_cast<std::remove_pointer_t<std::remove_reference_t<decltype(*ptr)>>*>(q);
+  };
+  alloc(&h->bw_gY32, rows * D * 4);
+  alloc(&h->bw_gY, rows * D * esz);
+  alloc(&h->bw_gU, rows * kD * esz);
+  alloc(&h->bw_gS, rows * D * 4);
+  alloc(&h->bw_gR, rows * D * 4);
+  alloc(&h->bw_part1, 2 * size_t(c.max_batch) * D * 4);
+  alloc(&h->bw_part2, 2 * size_t(c.max_batch) * D * 4);
+  alloc(&h->bw_sum, colsum_scratch_floats(c.T, c.max_batch, int64_t(kD > D ? kD : D)) * 4);
+  if (!ok) {
+    for (void* q : got) (void)hipFree(q);
+    h->bw_gY32 = h->bw_gS = h->bw_gR = h->bw_part1 = h->bw_part2 = h->bw_sum = nullptr;
+    h->bw_gY = h->bw_gU = nullptr;
+    return fail(h, RMX_ERR_OUT_OF_MEMORY, "backward workspace allocation failed");
+  }
+  h->allocs.insert(h->allocs.end(), got.begin(), got.end());
+  h->bwd_ready = true;
+  return RMX_OK;
+}
+
+rmx_status rmx_block_backward(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w, int32_t L,
+                              int32_t k, const void* saved, size_t saved_bytes, const float* g_out, float* dX,
+                              const rmx_grads* grads, void* stream) {
+  if (!h) return fail(nullptr, RMX_ERR_INVALID_ARG, "handle is NULL");
+  clear_error(h);
+  const rmx_config& c = h->cfg;
+  if (!w) return fail(h, RMX_ERR_INVALID_ARG, "weights is NULL");
+  if (!grads) return fail(h, RMX_ERR_INVALID_ARG, "grads is NULL");
+  if (L != c.L) return fail(h, RMX_ERR_INVALID_ARG, "L=%d but the handle was created with L=%d", L, c.L);
+  if (k != c.k) return fail(h, RMX_ERR_INVALID_ARG, "k=%d but the handle was created with k=%d", k, c.k);
+  if (B < 0 || B > c.max_batch)
+    return fail(h, RMX_ERR_INVALID_ARG, "B=%lld outside [0, max_batch=%lld]", (long long)B,
+                (long long)c.max_batch);
+  if (c.moe_experts > 0) return fail(h, RMX_ERR_UNSUPPORTED, "the backward needs a dense handle");
+  if (w->packed) return fail(h, RMX_ERR_INVALID_ARG, "the backward reads W1 and W2: packed must be NULL");
+  if (!rows_bwd_supported(c.dtype, c.T, c.D))
+    return fail(h, RMX_ERR_UNSUPPORTED, "the backward row kernel takes D <= %d (D %% 8 == 0, (D/T) %% 8 == 0) or "
+                "D <= %d, and T*D*sizeof(dtype) within its LDS", ROWS_BWD_MAX_D, ROWS_BWD_MAX_D_SCALAR);
+  const size_t need = rmx_saved_bytes(h, B);
+  if (saved_bytes < need) return fail(h, RMX_ERR_INVALID_ARG, "saved buffer of %zu bytes, %zu needed", saved_bytes, need);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
+    (void)hipGetLastError();
+    return fail(h, RMX_ERR_INVALID_ARG, "current device %d is not the handle's device %d", dev, h->device);
+  }
+  if (B == 0) return RMX_OK;
+
+  const size_t esz = dtype_size(c.dtype);
+  const size_t T = c.T, D = c.D, kD = size_t(c.k) * c.D, Ls = c.L, Bs = size_t(B);
+  struct Span {
+    const void* p;
+    size_t bytes;
+    const char* name;
+  };
+  const Span ins[] = {{X, Bs * T * D * esz, "X"},          {saved, need, "saved"},
+                      {g_out, Bs * D * 4, "g_out"},        {w->W1, Ls * T * D * kD * esz, "W1"},
+                      {w->W2, Ls * T * kD * D * esz, "W2"}, {w->ln1_g, Ls * D * esz, "ln1_g"},
+                      {w->ln2_g, Ls * D * esz, "ln2_g"},    {w->ln2_b, Ls * D * esz, "ln2_b"}};
+  const Span outs[] = {{dX, Bs * T * D * 4, "dX"},
+                       {grads->dW1, Ls * T * D * kD * 4, "dW1"},
+                       {grads->db1, Ls * T * kD * 4, "db1"},
+                       {grads->dW2, Ls * T * kD * D * 4, "dW2"},
+                       {grads->db2, Ls * T * D * 4, "db2"},
+                       {grads->dln1_g, Ls * D * 4, "dln1_g"},
+                       {grads->dln1_b, Ls * D * 4, "dln1_b"},
+                       {grads->dln2_g, Ls * D * 4, "dln2_g"},
+                       {grads->dln2_b, Ls * D * 4, "dln2_b"}};
+  rmx_status st;
+  for (const Span& x : ins)
+    if ((st = check_dev(h, x.p, x.bytes, dev, x.name)) != RMX_OK) return st;
+  for (const Span& x : outs)
+    if ((st = check_dev(h, x.p, x.bytes, dev, x.name)) != RMX_OK) return st;
+  auto overlap = [](const Span& a, const Span& b) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a.p), y = reinterpret_cast<uintptr_t>(b.p);
+    return x < y + b.bytes && y < x + a.bytes;
+  };
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const Span& x : ins)
+      if (overlap(outs[i], x)) return fail(h, RMX_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, x.name);
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(h, RMX_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  if ((st = ensure_bwd_workspace(h)) != RMX_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const SavedLayout lay = saved_layout(c, B);
+  auto blk = [&](int n, size_t off) {
+    return const_cast<char*>(static_cast<const char*>(saved)) + size_t(n) * lay.per_block + off;
+  };
+  auto at = [&](const void* base, size_t off_elems) -> const void* {
+    return static_cast<const char*>(base) + off_elems * esz;
+  };
+  const int Bi = int(B), Ti = c.T, Di = c.D, kDi = int(kD);
+  hipError_t e = hipSuccess;
+  auto ln_sums = [&](const float* part, float* dg, float* db) {
+    if (e == hipSuccess) e = run_colsum(h, s, DT_FP32, part, dg, 1, Bi, Di);
+    if (e == hipSuccess) e = run_colsum(h, s, DT_FP32, part + Bs * D, db, 1, Bi, Di);
+  };
+  for (int n = c.L - 1; n >= 0 && e == hipSuccess; --n) {
+    const size_t nn = size_t(n);
+    void* S_n = blk(n, lay.S);
+    void* U_n = blk(n, lay.U);
+    void* H_n = blk(n, lay.H);
+    if (n == c.L - 1) {
+      // gradient of the last block's pre-LN2 rows from the pooled output's
+      RowsBwdArgs ra{};
+      ra.Y = reinterpret_cast<const float*>(blk(n, lay.Y));
+      ra.ln2_g = at(w->ln2_g, nn * D);
+      ra.g_out = g_out;
+      ra.gY32 = h->bw_gY32;
+      ra.gY = h->bw_gY;
+      ra.part_ln2 = h->bw_part2;
+      ra.B = Bi;
+      ra.T = Ti;
+      ra.D = Di;
+      ra.eps = c.ln_eps;
+      e = run_rows_bwd(h, s, BWD_TOP, ra);
+      ln_sums(h->bw_part2, grads->dln2_g + nn * D, grads->dln2_b + nn * D);
+      if (e != hipSuccess) break;
+    }
+    // db2 = sum over samples of the pre-LN2 row gradients
+    if ((e = run_colsum(h, s, DT_FP32, h->bw_gY32, grads->db2 + nn * T * D, Ti, Bi, Di)) != hipSuccess) break;
+    // gU = (gY W2^T) * GELU'(U)
+    GemmArgs du{};
+    du.A = h->bw_gY;
+    du.W = at(w->W2, nn * T * kD * D);
+    du.bt = 1;
+    du.R = U_n;
+    du.C = h->bw_gU;
+    du.G = Ti;
+    du.M = Bi;
+    du.N = kDi;
+    du.K = Di;
+    if ((e = run_gemm(h, s, EPI_GELU_BWD, du, RMX_KERNEL_BWD_DU)) != hipSuccess) break;
+    if ((e = run_colsum(h, s, c.dtype, h->bw_gU, grads->db1 + nn * T * kD, Ti, Bi, kDi)) != hipSuccess) break;
+    // dW2 = H^T gY
+    GemmArgs dw2{};
+    dw2.A = H_n;
+    dw2.at = 1;
+    dw2.W = h->bw_gY;
+    dw2.C = grads->dW2 + nn * T * kD * D;
+    dw2.G = Ti;
+    dw2.M = kDi;
+    dw2.N = Di;
+    dw2.K = Bi;
+    if ((e = run_gemm(h, s, EPI_STORE32, dw2, RMX_KERNEL_BWD_DW2)) != hipSuccess) break;
+    // dW1 = S^T gU
+    GemmArgs dw1{};
+    dw1.A = S_n;
+    dw1.at = 1;
+    dw1.W = h->bw_gU;
+    dw1.C = grads->dW1 + nn * T * D * kD;
+    dw1.G = Ti;
+    dw1.M = Di;
+    dw1.N = kDi;
+    dw1.K = Bi;
+    if ((e = run_gemm(h, s, EPI_STORE32, dw1, RMX_KERNEL_BWD_DW1)) != hipSuccess) break;
+    // gS = gU W1^T + gY (the second residual)
+    GemmArgs ds{};
+    ds.A = h->bw_gU;
+    ds.W = at(w->W1, nn * T * D * kD);
+    ds.bt = 1;
+    ds.R = h->bw_gY32;
+    ds.C = h->bw_gS;
+    ds.G = Ti;
+    ds.M = Bi;
+    ds.N = Di;
+    ds.K = kDi;
+    if ((e = run_gemm(h, s, EPI_RESID32, ds, RMX_KERNEL_BWD_DS)) != hipSuccess) break;
+    // LN1 backward, mixing transpose and first residual; then LN2 backward of block n - 1
+    RowsBwdArgs ra{};
+    ra.ln1_g = at(w->ln1_g, nn * D);
+    ra.gS = h->bw_gS;
+    ra.gR = h->bw_gR;
+    ra.part_ln1 = h->bw_part1;
+    ra.B = Bi;
+    ra.T = Ti;
+    ra.D = Di;
+    ra.eps = c.ln_eps;
+    if (n > 0) {
+      ra.Y = reinterpret_cast<const float*>(blk(n - 1, lay.Y));
+      ra.ln2_g = at(w->ln2_g, (nn - 1) * D);
+      ra.ln2_b = at(w->ln2_b, (nn - 1) * D);
+      ra.gY32 = h->bw_gY32;
+      ra.gY = h->bw_gY;
+      ra.part_ln2 = h->bw_part2;
+      e = run_rows_bwd(h, s, BWD_MID, ra);
+      ln_sums(h->bw_part1, grads->dln1_g + nn * D, grads->dln1_b + nn * D);
+      ln_sums(h->bw_part2, grads->dln2_g + (nn - 1) * D, grads->dln2_b + (nn - 1) * D);
+    } else {
+      ra.X0 = X;
+      ra.dX = dX;
+      e = run_rows_bwd(h, s, BWD_BOTTOM, ra);
+      ln_sums(h->bw_part1, grads->dln1_g, grads->dln1_b);
+    }
   }
   if (e != hipSuccess) return fail(h, RMX_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return RMX_OK;

@@ -101,15 +101,31 @@ __device__ __forceinline__ float wave_sum(float v) {
 // u >= 0 and q for u < 0, so the left tail keeps its relative accuracy.  The 1 / sqrt 2
 // is folded into p and into the exponent: exp(-x^2) = exp2(-u^2 log2(e) / 2).
 // Branch-free: 13 VALU operations, one reciprocal, one exp2.
-__device__ __forceinline__ float gelu_erf(float u) {
+// normal_tail(u, &e) returns q = (1 - erf(|u| / sqrt 2)) / 2 and sets e = exp(-u^2 / 2).
+__device__ __forceinline__ float normal_tail(float u, float* e) {
   const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, fabsf(u), 1.0f));
   float poly = fmaf(0.5307027145f, t, -0.7265760135f);
   poly = fmaf(poly, t, 0.7107068705f);
   poly = fmaf(poly, t, -0.142248368f);
   poly = fmaf(poly, t, 0.127414796f);
   poly *= t;
-  const float q = poly * __builtin_amdgcn_exp2f((u * -0.72134752044448170f) * u);
+  *e = __builtin_amdgcn_exp2f((u * -0.72134752044448170f) * u);
+  return poly * *e;
+}
+
+__device__ __forceinline__ float gelu_erf(float u) {
+  float e;
+  const float q = normal_tail(u, &e);
   return u * (u >= 0.f ? 1.0f - q : q);
+}
+
+// GELU'(u) = Phi(u) + u phi(u), phi(u) = exp(-u^2 / 2) / sqrt(2 pi) the standard normal
+// density ("RankMixer 详解（1）", section 5.2): the same erf evaluation, its exponential
+// reused for phi.
+__device__ __forceinline__ float gelu_grad_erf(float u) {
+  float e;
+  const float q = normal_tail(u, &e);
+  return fmaf(u * 0.39894228040143268f, e, u >= 0.f ? 1.0f - q : q);
 }
 
 }  // namespace rmx

@@ -114,6 +114,7 @@ __device__ __forceinline__ void copy_to_lds(uint32_t lds_dst, uint32_t voff, __a
 struct TileSrc {
   __amdgpu_buffer_rsrc_t rA, rW;
   uint32_t offA[4], offW[4];  // per-lane byte offsets of this lane's copies (K step 0)
+  uint32_t stepA, stepW;      // transposed A: bytes per K step added to every copy offset
 };
 
 // Per-lane copy offsets.  Copy-in: wave w fills A rows 64w .. 64w+63 (4 loads of 16 rows)
@@ -135,58 +136,134 @@ __device__ __forceinline__ void tile_offsets(TileSrc& ts, int wave, int lane, in
   }
 }
 
+// Operands stored the other way round (the backward products):
+//   AT: A is [K][M] (M contiguous, k rows lda apart): its stage holds 32 k rows x 256 m,
+//       laid out, copied and read like the W tile (transposing fragment reads).  The K
+//       step is folded into each lane's offset (stepA), so that k rows past K fall outside
+//       the buffer range and load zeros: any K works.
+//   BT: W is [N][K] (K contiguous): its stage holds 256 n rows x 32 k, laid out, copied and
+//       read like the A tile (plain fragment reads); K % 32 == 0.
+// With AT the W tile (not transposed) also takes its K step through the lane offsets.
+template <bool AT, bool BT>
+__device__ __forceinline__ void tile_offsets_t(TileSrc& ts, int wave, int lane, int m0, int n0, int M, int N,
+                                               int K, uint32_t lda, uint32_t bytesA, uint32_t bytesW) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    if constexpr (AT) {
+      const int kr = 8 * wave + 2 * a + (lane >> 5);
+      const int m = m0 + (((lane & 31) ^ swz_w(kr)) * 8);
+      ts.offA[a] = m < M ? (uint32_t(kr) * lda + uint32_t(m)) * 2u : bytesA;
+    } else {
+      const int r = 64 * wave + 16 * a + (lane >> 2);
+      const int c = (lane & 3) ^ swz_a(r);
+      ts.offA[a] = m0 + r < M ? (uint32_t(m0 + r) * lda + uint32_t(c * 8)) * 2u : bytesA;
+    }
+    if constexpr (BT) {
+      const int r = 64 * wave + 16 * a + (lane >> 2);
+      const int c = (lane & 3) ^ swz_a(r);
+      ts.offW[a] = n0 + r < N ? (uint32_t(n0 + r) * uint32_t(K) + uint32_t(c * 8)) * 2u : bytesW;
+    } else {
+      const int kr = 8 * wave + 2 * a + (lane >> 5);
+      const int col = n0 + (((lane & 31) ^ swz_w(kr)) * 8);
+      ts.offW[a] = col < N ? (uint32_t(kr) * uint32_t(N) + uint32_t(col)) * 2u : bytesW;
+    }
+  }
+  ts.stepA = uint32_t(BK) * lda * 2u;
+  ts.stepW = uint32_t(BK) * uint32_t(N) * 2u;
+}
+
 // The K loop of one tile: acc (zeroed here) += A_tile (256 x K) * W_tile (K x 256).
 // Ends with every copy drained and the workgroup synchronized, so that the ring memory
-// can be reused by the caller.
+// can be reused by the caller.  AT / BT: operands stored transposed (tile_offsets_t).
+template <bool AT = false, bool BT = false>
 __device__ __forceinline__ void mfma_tile(f32x16_t (&acc)[4][4], const TileSrc& ts, lds_u8* smem, uint32_t lds0,
                                           int K, int N, int wave, int lane) {
-  const int nk = K / BK;
+  const int nk = AT ? (K + BK - 1) / BK : K / BK;
   // Copy q (0..7) of K step kt into ring stage `stage`; steps past the end reload the last
   // step (in bounds, never read) so that every K step issues the same number of loads.
   auto copy = [&](int kt, int stage, int q) {
     kt = kt < nk ? kt : nk - 1;
     const uint32_t sbase = lds0 + uint32_t(stage) * STAGE_BYTES;
     if (q < 4) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(sbase + uint32_t(64 * wave + 16 * q) * 64u);
-      copy_to_lds(dst, ts.offA[q], ts.rA, kt * BK * 2);
+      if constexpr (AT) {
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(sbase + uint32_t(8 * wave + 2 * q) * 512u);
+        copy_to_lds(dst, ts.offA[q] + uint32_t(kt) * ts.stepA, ts.rA, 0);
+      } else {
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(sbase + uint32_t(64 * wave + 16 * q) * 64u);
+        copy_to_lds(dst, ts.offA[q], ts.rA, kt * BK * 2);
+      }
+    } else if constexpr (BT) {
+      const uint32_t dst =
+          __builtin_amdgcn_readfirstlane(sbase + A_STAGE_BYTES + uint32_t(64 * wave + 16 * (q - 4)) * 64u);
+      copy_to_lds(dst, ts.offW[q - 4], ts.rW, kt * BK * 2);
     } else {
       const uint32_t dst =
           __builtin_amdgcn_readfirstlane(sbase + A_STAGE_BYTES + uint32_t(8 * wave + 2 * (q - 4)) * 512u);
-      copy_to_lds(dst, ts.offW[q - 4], ts.rW, kt * BK * N * 2);
+      if constexpr (AT)
+        copy_to_lds(dst, ts.offW[q - 4] + uint32_t(kt) * ts.stepW, ts.rW, 0);
+      else
+        copy_to_lds(dst, ts.offW[q - 4], ts.rW, kt * BK * N * 2);
     }
   };
 
   const int wm = wave >> 1, wn = wave & 1;
-  // Per-lane byte offsets of this wave's fragments within a stage.
-  uint32_t aoff[2][4], boff[4];
+  // Per-lane byte offsets of this wave's fragments within a stage.  Row-tile fragments
+  // (A, or W with BT) are plain 16-byte reads per K sub-step; k-row-tile fragments (W, or
+  // A with AT) are two transposing reads per K sub-step.
+  // transposing read: lane l of each 16-lane group addresses k row kb + (l % 16) / 4 and
+  // 4 consecutive columns at 4 (l % 4); it receives column (l % 16) of that 4 x 16 block
+  const int kb = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  auto row_frag_off = [&](int base, int m, int kk) {
+    const int c = kk * 2 + (lane >> 5);
+    return uint32_t(base + m * 64 + ((c ^ swz_a(m)) << 4));
+  };
+  auto tr_frag_off = [&](int base, int n) {
+    return uint32_t(base + kb * 512 + (((n >> 3) ^ swz_w(kb)) << 4) + (n & 7) * 2);
+  };
+  uint32_t aoff[2][4], boff[4];  // row-tile A per sub-step; k-row-tile W (sub-step 1 at + 16 rows)
+  uint32_t aoff_t[4], boff_r[2][4];  // AT: k-row-tile A; BT: row-tile W
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (AT) {
+      aoff_t[i] = tr_frag_off(0, wm * 128 + i * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = wm * 128 + i * 32 + (lane & 31);
-      const int c = kk * 2 + (lane >> 5);
-      aoff[kk][i] = uint32_t(m * 64 + ((c ^ swz_a(m)) << 4));
+      for (int kk = 0; kk < 2; ++kk) aoff[kk][i] = row_frag_off(0, wm * 128 + i * 32 + (lane & 31), kk);
     }
-  {
-    // transposing read: lane l of each 16-lane group addresses k row kb + (l % 16) / 4 and
-    // 4 consecutive columns at 4 (l % 4); it receives column (l % 16) of that 4 x 16 block
-    const int kb = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    if constexpr (BT) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = wn * 128 + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      boff[j] = uint32_t(A_STAGE_BYTES + kb * 512 + (((n >> 3) ^ swz_w(kb)) << 4) + (n & 7) * 2);
+      for (int kk = 0; kk < 2; ++kk) boff_r[kk][i] = row_frag_off(A_STAGE_BYTES, wn * 128 + i * 32 + (lane & 31), kk);
+    } else {
+      boff[i] = tr_frag_off(A_STAGE_BYTES, wn * 128 + i * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
     }
   }
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
   typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  auto tr_read = [](const lds_u8* q) {
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)q));
+  };
   auto read_frags = [&](Frags& f, const lds_u8* stage_ptr, int kk) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const lds_u32x4*>(stage_ptr + aoff[kk][i]);
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (AT) {
+        const lds_u8* q = stage_ptr + aoff_t[i] + kk * 16 * 512;
+        const u32x2_t lo = tr_read(q), hi = tr_read(q + 4 * 512);
+        f.a[i] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+      } else {
+        f.a[i] = *reinterpret_cast<const lds_u32x4*>(stage_ptr + aoff[kk][i]);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const lds_u8* q = stage_ptr + boff[j] + kk * 16 * 512;
-      f.b[2 * j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)q));
-      f.b[2 * j + 1] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * 512)));
+      if constexpr (BT) {
+        const u32x4_t v = *reinterpret_cast<const lds_u32x4*>(stage_ptr + boff_r[kk][j]);
+        f.b[2 * j] = u32x2_t{v.x, v.y};
+        f.b[2 * j + 1] = u32x2_t{v.z, v.w};
+      } else {
+        const lds_u8* q = stage_ptr + boff[j] + kk * 16 * 512;
+        f.b[2 * j] = tr_read(q);
+        f.b[2 * j + 1] = tr_read(q + 4 * 512);
+      }
     }
   };
 
@@ -303,6 +380,27 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], flo
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[e]);
           store8(static_cast<bf16_t*>(p.C) + (PK ? pko : off), v);
+        } else if constexpr (EPI == EPI_GELU_SAVE) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += bias[e];
+          store8(static_cast<bf16_t*>(p.U) + off, v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
+          store8(static_cast<bf16_t*>(p.C) + off, v);
+        } else if constexpr (EPI == EPI_GELU_BWD) {
+          float u[8];
+          load8(static_cast<const bf16_t*>(p.R) + off, u);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= gelu_grad_erf(u[e]);
+          store8(static_cast<bf16_t*>(p.C) + off, v);
+        } else if constexpr (EPI == EPI_RESID32) {
+          float rr[8];
+          load8(static_cast<const float*>(p.R) + off, rr);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += rr[e];
+          store8(static_cast<float*>(p.C) + off, v);
+        } else if constexpr (EPI == EPI_STORE32) {
+          store8(static_cast<float*>(p.C) + off, v);
         } else if constexpr (EPI == EPI_BIAS) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] += bias[e];
@@ -422,7 +520,7 @@ __device__ __forceinline__ void mfma_tile_pk(f32x16_t (&acc)[4][4], __amdgpu_buf
 
 // Dense per-token GEMM: one workgroup per tile, G * ceil(M/256) * ceil(N/256) tiles; PK:
 // operands in the packed layout.
-template <int EPI, bool PK>
+template <int EPI, bool PK, bool AT = false, bool BT = false>
 __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem_g[NS * STAGE_BYTES];
   lds_u8* const smem = (lds_u8*)smem_g;  // the generic pointer of a __shared__ array is in LDS
@@ -452,6 +550,16 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
     const __amdgpu_buffer_rsrc_t rW =
         make_rsrc(static_cast<const uint16_t*>(p.W) + (size_t(g) * nNt + nt) * (size_t(blk) / 2), blk);
     mfma_tile_pk(acc, rA, rW, smem, lds0, K, wave, lane);
+  } else if constexpr (AT || BT) {
+    // Slices are < 2^31 bytes (checked at launch).
+    const uint32_t lda = uint32_t(p.lda);
+    const uint32_t bytesA = AT ? uint32_t(K) * lda * 2u : (uint32_t(M - 1) * lda + uint32_t(K)) * 2u;
+    const uint32_t bytesW = uint32_t(K) * uint32_t(N) * 2u;
+    TileSrc ts;
+    ts.rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(g) * size_t(p.sa), bytesA);
+    ts.rW = make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * K * N, bytesW);
+    tile_offsets_t<AT, BT>(ts, wave, lane, m0, n0, M, N, K, lda, bytesA, bytesW);
+    mfma_tile<AT, BT>(acc, ts, smem, lds0, K, N, wave, lane);
   } else {
     // Slices are < 2^31 bytes (checked at launch); an offset equal to the slice size is out
     // of range whether or not the uniform offset takes part in the range check.
@@ -726,10 +834,12 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs p) {
       const int e = tid + 256 * i;  // 0..1023
       const int am = e / GK, ak = e % GK;
       const int row = m0 + am, kk = k0 + ak;
-      As[ak][am] = (row < M && kk < K) ? load1(A + size_t(row) * size_t(p.lda) + kk) : 0.f;
+      const size_t a_at = p.at ? size_t(kk) * size_t(p.lda) + row : size_t(row) * size_t(p.lda) + kk;
+      As[ak][am] = (row < M && kk < K) ? load1(A + a_at) : 0.f;
       const int bk = e / GT, bn = e % GT;
       const int kr = k0 + bk, col = n0 + bn;
-      Bs[bk][bn] = (kr < K && col < N) ? load1(W + size_t(kr) * N + col) : 0.f;
+      const size_t w_at = p.bt ? size_t(col) * K + kr : size_t(kr) * N + col;
+      Bs[bk][bn] = (kr < K && col < N) ? load1(W + w_at) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -758,6 +868,15 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs p) {
       const size_t off = size_t(g) * size_t(p.sc) + size_t(m) * size_t(p.ldc) + n;
       if constexpr (EPI == EPI_GELU) {
         store1(static_cast<T*>(p.C) + off, gelu_erf(acc[i][j] + bias));
+      } else if constexpr (EPI == EPI_GELU_SAVE) {
+        store1(static_cast<T*>(p.U) + off, acc[i][j] + bias);
+        store1(static_cast<T*>(p.C) + off, gelu_erf(acc[i][j] + bias));
+      } else if constexpr (EPI == EPI_GELU_BWD) {
+        store1(static_cast<T*>(p.C) + off, acc[i][j] * gelu_grad_erf(load1(static_cast<const T*>(p.R) + off)));
+      } else if constexpr (EPI == EPI_RESID32) {
+        static_cast<float*>(p.C)[off] = acc[i][j] + static_cast<const float*>(p.R)[off];
+      } else if constexpr (EPI == EPI_STORE32) {
+        static_cast<float*>(p.C)[off] = acc[i][j];
       } else if constexpr (EPI == EPI_BIAS) {
         store1(static_cast<T*>(p.C) + off, acc[i][j] + bias);
       } else {
@@ -769,11 +888,18 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs p) {
 
 }  // namespace
 
-bool gemm_uses_mfma(int dtype, int M, int N, int K, int64_t lda) {
+bool gemm_uses_mfma(int dtype, int M, int N, int K, int64_t lda, int at, int bt) {
   const uint64_t lim = uint64_t(1) << 31;
+  if (dtype != DT_BF16 || N % 8 != 0 || uint64_t(K) * N * 2 >= lim) return false;
+  if (at) {
+    // k rows of A are whole 16-byte chunks; the K tail loads zeros; with bt as well the
+    // row-tile W needs K % 32 (no kernel takes both)
+    const uint64_t ld = lda > 0 ? uint64_t(lda) : uint64_t(M);
+    return !bt && M % 8 == 0 && ld % 8 == 0 && ld >= uint64_t(M) && uint64_t(K) * ld * 2 < lim;
+  }
   const uint64_t ld = lda > 0 ? uint64_t(lda) : uint64_t(K);
   const uint64_t spanA = M > 0 ? (uint64_t(M - 1) * ld + uint64_t(K)) * 2 : 0;
-  return dtype == DT_BF16 && K % BK == 0 && N % 8 == 0 && ld % 8 == 0 && spanA < lim && uint64_t(K) * N * 2 < lim;
+  return K % BK == 0 && ld % 8 == 0 && spanA < lim;
 }
 
 hipError_t gemm_init() { return hipSuccess; }
@@ -854,36 +980,71 @@ hipError_t launch_pack_weights(const void* W, void* out, int G, int K, int N, hi
   return hipGetLastError();
 }
 
+namespace {
+
+template <typename T>
+hipError_t launch_generic(int epi, const GemmArgs& a, hipStream_t stream) {
+  const dim3 grid((a.N + GT - 1) / GT, (a.M + GT - 1) / GT, a.G);
+  switch (epi) {
+    case EPI_GELU: hipLaunchKernelGGL((gemm_generic<T, EPI_GELU>), grid, dim3(256), 0, stream, a); break;
+    case EPI_BIAS: hipLaunchKernelGGL((gemm_generic<T, EPI_BIAS>), grid, dim3(256), 0, stream, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_generic<T, EPI_RESID>), grid, dim3(256), 0, stream, a); break;
+    case EPI_GELU_SAVE: hipLaunchKernelGGL((gemm_generic<T, EPI_GELU_SAVE>), grid, dim3(256), 0, stream, a); break;
+    case EPI_GELU_BWD: hipLaunchKernelGGL((gemm_generic<T, EPI_GELU_BWD>), grid, dim3(256), 0, stream, a); break;
+    case EPI_RESID32: hipLaunchKernelGGL((gemm_generic<T, EPI_RESID32>), grid, dim3(256), 0, stream, a); break;
+    case EPI_STORE32: hipLaunchKernelGGL((gemm_generic<T, EPI_STORE32>), grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The backward products and the training forward's GELU epilogue: 256 x 256 tiles only.
+template <bool AT, bool BT>
+hipError_t launch_dense_mfma_t(int epi, const GemmArgs& a, hipStream_t stream) {
+  const dim3 tiles(unsigned(a.G * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN)));
+  switch (epi) {
+    case EPI_GELU_BWD:
+      hipLaunchKernelGGL((gemm_bf16_mfma<EPI_GELU_BWD, false, AT, BT>), tiles, dim3(MFMA_THREADS), 0, stream, a);
+      break;
+    case EPI_RESID32:
+      hipLaunchKernelGGL((gemm_bf16_mfma<EPI_RESID32, false, AT, BT>), tiles, dim3(MFMA_THREADS), 0, stream, a);
+      break;
+    case EPI_STORE32:
+      hipLaunchKernelGGL((gemm_bf16_mfma<EPI_STORE32, false, AT, BT>), tiles, dim3(MFMA_THREADS), 0, stream, a);
+      break;
+    case EPI_GELU_SAVE:
+      if (AT || BT) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_bf16_mfma<EPI_GELU_SAVE, false, false, false>), tiles, dim3(MFMA_THREADS), 0,
+                         stream, a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& args, hipStream_t stream) {
   if (args.G == 0 || args.M == 0 || args.N == 0) return hipSuccess;
   GemmArgs a = args;
-  if (a.lda == 0) a.lda = a.K;
+  if (a.lda == 0) a.lda = a.at ? a.M : a.K;
   if (a.ldc == 0) a.ldc = a.N;
-  if (a.sa == 0) a.sa = int64_t(a.M) * a.lda;
+  if (a.sa == 0) a.sa = a.at ? int64_t(a.K) * a.lda : int64_t(a.M) * a.lda;
   if (a.sc == 0) a.sc = int64_t(a.M) * a.ldc;
+  const bool bwd_epi = epi == EPI_GELU_BWD || epi == EPI_RESID32 || epi == EPI_STORE32;
+  if ((a.at || a.bt) && !bwd_epi) return hipErrorInvalidValue;
   if (a.packed) {
-    // packed operands exist only for the MFMA kernels, and not for the bias-only epilogue
-    if (!gemm_uses_mfma(dtype, a.M, a.N, a.K) || epi == EPI_BIAS) return hipErrorInvalidValue;
+    // packed operands exist only for the MFMA kernels, and only for the inference epilogues
+    if (!gemm_uses_mfma(dtype, a.M, a.N, a.K) || (epi != EPI_GELU && epi != EPI_RESID)) return hipErrorInvalidValue;
     return launch_dense_mfma<true>(epi, a, stream);
   }
-  if (gemm_uses_mfma(dtype, a.M, a.N, a.K, a.lda) && (a.sa % 8) == 0) return launch_dense_mfma<false>(epi, a, stream);
-  dim3 grid((a.N + GT - 1) / GT, (a.M + GT - 1) / GT, a.G);
-  if (dtype == DT_BF16) {
-    if (epi == EPI_GELU)
-      hipLaunchKernelGGL((gemm_generic<bf16_t, EPI_GELU>), grid, dim3(256), 0, stream, a);
-    else if (epi == EPI_BIAS)
-      hipLaunchKernelGGL((gemm_generic<bf16_t, EPI_BIAS>), grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_generic<bf16_t, EPI_RESID>), grid, dim3(256), 0, stream, a);
-  } else {
-    if (epi == EPI_GELU)
-      hipLaunchKernelGGL((gemm_generic<float, EPI_GELU>), grid, dim3(256), 0, stream, a);
-    else if (epi == EPI_BIAS)
-      hipLaunchKernelGGL((gemm_generic<float, EPI_BIAS>), grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_generic<float, EPI_RESID>), grid, dim3(256), 0, stream, a);
+  if (gemm_uses_mfma(dtype, a.M, a.N, a.K, a.lda, a.at, a.bt) && (a.sa % 8) == 0) {
+    if (a.at) return launch_dense_mfma_t<true, false>(epi, a, stream);
+    if (a.bt) return launch_dense_mfma_t<false, true>(epi, a, stream);
+    if (bwd_epi || epi == EPI_GELU_SAVE) return launch_dense_mfma_t<false, false>(epi, a, stream);
+    return launch_dense_mfma<false>(epi, a, stream);
   }
-  return hipGetLastError();
+  return dtype == DT_BF16 ? launch_generic<bf16_t>(epi, a, stream) : launch_generic<float>(epi, a, stream);
 }
 
 }  // namespace rmx

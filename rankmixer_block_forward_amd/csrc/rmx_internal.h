@@ -50,6 +50,53 @@ hipError_t launch_rows(int dtype, int mode, const RowsArgs& a, hipStream_t strea
 hipError_t launch_token_mix(int dtype, const void* X, void* Y, int64_t B, int T, int D,
                             hipStream_t stream);
 
+// ---------------------------------------------------------------- backward row kernel
+// One workgroup per sample ("RankMixer 详解（1）", section 5.2).  Modes:
+//   BWD_TOP     gY = LN2_backward(g_out / T) of the last block (Y = its pre-LN2 rows)
+//   BWD_MID     X = LN2(Y) of block n - 1 recomputed in LDS; gR = LN1_backward(gS) of block
+//               n; gX = gR + P^T gR; gY = LN2_backward(gX) of block n - 1
+//   BWD_BOTTOM  X = X0; gR = LN1_backward(gS) of block 1; dX = gR + P^T gR
+enum RowsBwdMode { BWD_TOP = 0, BWD_MID = 1, BWD_BOTTOM = 2 };
+
+struct RowsBwdArgs {
+  const void* X0;      // BOTTOM: [B, T, D] (dtype), the stack input
+  const float* Y;      // TOP, MID: [T, B, D] pre-LN2 rows (of block L, of block n - 1)
+  const void* ln2_g;   // TOP, MID: LN2 gamma / beta of that block [D] (dtype)
+  const void* ln2_b;
+  const void* ln1_g;   // MID, BOTTOM: LN1 gamma of block n [D] (dtype)
+  const float* gS;     // MID, BOTTOM: [T, B, D] gradient of block n's S (residual included)
+  float* gR;           // MID, BOTTOM: [B, T, D] scratch
+  const float* g_out;  // TOP: [B, D] gradient of the pooled output
+  float* gY32;         // TOP, MID: [T, B, D] gradient of the pre-LN2 rows (fp32)
+  void* gY;            // TOP, MID: the same in dtype (a GEMM operand)
+  float* dX;           // BOTTOM: [B, T, D]
+  float* part_ln1;     // MID, BOTTOM: [2][B][D] per-sample gamma / beta gradients of LN1
+  float* part_ln2;     // TOP, MID: [2][B][D] per-sample gamma / beta gradients of LN2
+  int B, T, D;
+  float eps;
+};
+
+constexpr int ROWS_BWD_MAX_D = 2048;        // vectorized path (D % 8 == 0, (D / T) % 8 == 0)
+constexpr int ROWS_BWD_MAX_D_SCALAR = 512;  // scalar path
+constexpr size_t ROWS_BWD_MAX_LDS = 128 * 1024;
+size_t rows_bwd_lds_bytes(int dtype, int T, int D);
+bool rows_bwd_supported(int dtype, int T, int D);
+// Once per process and device (raises the kernel's LDS limit).
+hipError_t rows_bwd_init();
+hipError_t launch_rows_bwd(int dtype, int mode, const RowsBwdArgs& a, hipStream_t stream);
+
+// out[g, n] = sum over r < R of in[g, r, n] (in: dtype, [G, R, N] contiguous; out fp32),
+// in a fixed order.  scratch: colsum_scratch_floats(G, R, N) floats.
+constexpr int COLSUM_ROWS = 256;
+constexpr int COLSUM_MAX_SPLIT = 64;
+inline size_t colsum_scratch_floats(int64_t G, int64_t R, int64_t N) {
+  int64_t rs = (R + COLSUM_ROWS - 1) / COLSUM_ROWS;
+  if (rs > COLSUM_MAX_SPLIT) rs = COLSUM_MAX_SPLIT;
+  return size_t(rs > 1 ? rs : 0) * size_t(G) * size_t(N);
+}
+hipError_t launch_colsum(int dtype, const void* in, float* out, float* scratch, int G, int R, int N,
+                         hipStream_t stream);
+
 // ---------------------------------------------------------------- Sparse-MoE routing
 // Group gi = t * E + e.  Rows of a group are listed in ascending sample order.
 constexpr int MOE_MAX_E = 16;
@@ -93,7 +140,18 @@ hipError_t launch_moe_combine(const MoeArgs& a, hipStream_t stream);
 //   EPI_MOE2:  C [rows, N] (fp32) = row_gate * (A W_g + bias_g),   A = C of EPI_MOE1
 //   group g owns compacted rows group_start[g] .. group_start[g + 1] - 1.
 //   EPI_BIAS:  C [G, M, N] (dtype) = A W + bias
-enum Epilogue { EPI_GELU = 0, EPI_RESID = 1, EPI_MOE1 = 2, EPI_MOE2 = 3, EPI_BIAS = 4 };
+//   Backward products (no bias):
+//   EPI_GELU_BWD: C [G, M, N] (dtype) = (A W) * GELU'(R),  R [G, M, N] (dtype, the
+//                 pre-activations U, same layout as C)
+//   EPI_RESID32:  C [G, M, N] (fp32)  = A W + R,  R [G, M, N] (fp32)
+//   EPI_STORE32:  C [G, M, N] (fp32)  = A W
+//   Training forward:
+//   EPI_GELU_SAVE: EPI_GELU that also stores the pre-activations A W + bias in U
+//                  ([G, M, N], dtype, C's layout; row-major operands only)
+enum Epilogue {
+  EPI_GELU = 0, EPI_RESID = 1, EPI_MOE1 = 2, EPI_MOE2 = 3, EPI_BIAS = 4,
+  EPI_GELU_BWD = 5, EPI_RESID32 = 6, EPI_STORE32 = 7, EPI_GELU_SAVE = 8
+};
 
 struct GemmArgs {
   const void* A;
@@ -114,13 +172,18 @@ struct GemmArgs {
   // operand layout; EPI_GELU then writes C packed ([G][pk_rows(M) x N]) and EPI_RESID reads
   // R packed, C stays row-major.  Strides are ignored.
   int packed;
+  // Dense kernels only, operands stored transposed (the backward products):
+  //   at: A is [G][K][M], element (m, k) at A + g * sa + k * lda + m (lda = 0: M, sa = 0: K * M)
+  //   bt: W is [G][N][K], element (k, n) at W + g * N * K + n * K + k
+  int at, bt;
+  void* U;  // EPI_GELU_SAVE: the pre-activations
 };
 // Rows per token up to which the dense launch uses 64-row tiles.
 constexpr int GEMM_SMALL_M = 64;
 
 // True when the bf16 MFMA kernel handles this shape (else the generic kernel runs);
-// lda = 0 means K.
-bool gemm_uses_mfma(int dtype, int M, int N, int K, int64_t lda = 0);
+// lda = 0 means K (M with at).
+bool gemm_uses_mfma(int dtype, int M, int N, int K, int64_t lda = 0, int at = 0, int bt = 0);
 // Sparse-MoE grouped GEMM launch (bf16 MFMA only); `max_rows` bounds every group's rows.
 hipError_t launch_gemm_moe(int epi, const GemmArgs& a, hipStream_t stream);
 bool gemm_moe_supported(int N, int K, int64_t a_rows);

@@ -15,69 +15,11 @@
 // over values held in registers, reduced across the 64 lanes of one wavefront.
 #include "rmx_device.h"
 #include "rmx_internal.h"
+#include "rmx_rowops.h"
 
 namespace rmx {
 
 namespace {
-
-template <int W, typename T>
-__device__ __forceinline__ void loadw(const T* p, float* v) {
-  if constexpr (W == 8) {
-    load8(p, v);
-  } else {
-    v[0] = load1(p);
-  }
-}
-template <int W, typename T>
-__device__ __forceinline__ void storew(T* p, const float* v) {
-  if constexpr (W == 8) {
-    store8(p, v);
-  } else {
-    store1(p, v[0]);
-  }
-}
-
-// LayerNorm of one row held as v[NC][W] by the 64 lanes of a wave (chunk c = lane + 64 i),
-// in place: v = gamma * (v - mu) / sqrt(var + eps) + beta.
-template <int W, int NC, typename T>
-__device__ __forceinline__ void wave_layernorm(float (&v)[NC][W], int lane, int nchunks, int D,
-                                               const T* gamma, const T* beta, float eps) {
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nchunks) {
-#pragma unroll
-      for (int e = 0; e < W; ++e) s += v[i][e];
-    }
-  }
-  const float mu = wave_sum(s) / float(D);
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nchunks) {
-#pragma unroll
-      for (int e = 0; e < W; ++e) {
-        const float d = v[i][e] - mu;
-        ss += d * d;
-      }
-    }
-  }
-  const float var = wave_sum(ss) / float(D);
-  const float rstd = 1.0f / sqrtf(var + eps);
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nchunks) {
-      float g[W], bt[W];
-      loadw<W>(gamma + c * W, g);
-      loadw<W>(beta + c * W, bt);
-#pragma unroll
-      for (int e = 0; e < W; ++e) v[i][e] = g[e] * ((v[i][e] - mu) * rstd) + bt[e];
-    }
-  }
-}
 
 // One block input row (token t of sample b) into registers: X0[b, t] (first block) or the
 // previous block's pre-LN2 row Y[t, b] (fp32).

@@ -30,6 +30,7 @@ KIND_W1, KIND_B1, KIND_W2, KIND_B2 = 10, 11, 12, 13
 KIND_G1, KIND_BE1, KIND_G2, KIND_BE2 = 20, 21, 22, 23
 KIND_WG, KIND_WE1, KIND_BEXP1, KIND_WE2, KIND_BEXP2 = 30, 31, 32, 33, 34
 KIND_E, KIND_WP, KIND_BP = 40, 41, 42
+KIND_GOUT = 50
 
 X_BLOCK = 64
 
@@ -259,3 +260,20 @@ def make_tokenize_inputs(B: int, T: int, d: int, D: int, dtype: str = "bf16", se
     if bias_std > 0.0:
         _fill_slices(bp, lambda key: _normal(seed, key, (D,), bias_std), [(KIND_BP, t) for t in range(T)], dtype)
     return TokenizeInputs(E=E, Wp=Wp, bp=bp)
+
+
+def make_grad_out(B: int, D: int, seed: int = 0, rows=None) -> np.ndarray:
+    """Upstream gradient of the pooled output for the backward pass, fp32 [B, D]: N(0, 1)
+    in blocks of 64 samples (per-block substreams, like X).  rows: if given, only those
+    samples keep their gradient, the others are zero."""
+    G = np.empty((B, D), dtype=np.float32)
+    nblk = (B + X_BLOCK - 1) // X_BLOCK
+    for i in range(nblk):
+        lo, hi = i * X_BLOCK, min(B, (i + 1) * X_BLOCK)
+        G[lo:hi] = _normal(seed, (KIND_GOUT, i), (hi - lo, D), 1.0)
+    if rows is not None:
+        keep = np.zeros(B, dtype=bool)
+        keep[np.asarray(rows)] = True
+        G[~keep] = 0.0
+    return G
+

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = rmx.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.rmx_abi_version() == 2
+    assert lib.rmx_abi_version() == 3
 
 
 def test_status_strings_and_kernel_names():
@@ -93,3 +93,21 @@ def test_packed_weights_host_side():
     lib = rmx.load_library()
     assert lib.rmx_packed_weights_bytes(None) == 0
     assert lib.rmx_pack_weights(None, None, 1, None, 0, None) == binding.RMX_ERR_INVALID_ARG
+
+
+def test_training_entry_points_host_side():
+    """Without a handle, the training entry points reject their arguments on the host."""
+    lib = rmx.load_library()
+    assert lib.rmx_saved_bytes(None, 8) == 0
+    assert lib.rmx_block_forward_train(None, None, 1, None, 1, 1, None, None, 0, None) == binding.RMX_ERR_INVALID_ARG
+    assert lib.rmx_block_backward(None, None, 1, None, 1, 1, None, 0, None, None, None, None) == \
+        binding.RMX_ERR_INVALID_ARG
+    assert "handle" in lib.rmx_last_error(None).decode()
+
+
+def test_grads_struct_matches_header():
+    """rmx_grads in the binding lists the header's fields in order."""
+    src = open(os.path.join(ROOT, "include", "rmx.h")).read()
+    body = re.search(r"typedef struct \{([^}]*)\} rmx_grads;", src).group(1)
+    fields = re.findall(r"float\*\s+(\w+);", body)
+    assert fields == [f for f, _ in binding.rmx_grads._fields_]
