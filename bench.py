@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--sweep", action="store_true", help="one line per serving batch size")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-samples", type=int, default=384)
+    p.add_argument("--backward", action="store_true",
+                   help="time one training step's compute instead: forward keeping activations + backward")
     p.add_argument("--tokenize", action="store_true",
                    help="time the tokenisation projection (rmx_tokenize) at the 1B input shape "
                         "(B x [T*d] -> B x T x D, d = 512) and print its line instead")
@@ -189,16 +191,20 @@ def moe_roofline(cfg, B, prof, moe):
             "avg_launch_ms": round(prof[kern]["avg_ms"], 4), "algorithmic_flops_per_launch": flops}
 
 
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(cfg, n):
     """The fp64 oracle, as it stands, on n samples of the same workload."""
     import numpy as np
     import oracle
     from rankmixer_block_forward_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
     inp = synth.make_inputs(cfg.with_(B=n), seed=0)
     t0 = time.perf_counter()
     o, _, _ = oracle.forward(inp.X, inp.layers(), cfg.eps)
@@ -288,6 +294,81 @@ def bench_tokenize(B, steps, warmup):
         "tflops": round(flops / (ms / 1e3) / 1e12, 2), "roofline": roof}), flush=True)
 
 
+def bench_backward(cfg, B, steps, warmup, cpu_samples):
+    """A step = rmx_block_forward_train + rmx_block_backward over one resident batch (the
+    gradients of every parameter and of X for an upstream gradient of the pooled output).
+    FLOPs per step: forward 4 k L T D^2 per sample, backward twice that (gradients of the
+    activations and of the weights, two products each per block)."""
+    import numpy as np
+    import torch
+    import rankmixer_block_forward_amd as rmx
+    from rankmixer_block_forward_amd import synth
+    t0 = time.time()
+    inp = synth.make_inputs(cfg.with_(B=B), seed=0)
+    X, w = rmx.upload(inp)
+    del inp
+    g = torch.from_numpy(synth.make_grad_out(B, cfg.D, seed=0)).cuda()
+    print(f"[bench] inputs {cfg.name} B={B} generated and resident in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+    h = rmx.Handle.for_config(cfg, max_batch=B)
+    out, saved = h.forward_train(X, w)
+    dX, grads = h.backward(X, w, saved, g)
+    for _ in range(warmup):
+        h.forward_train(X, w, out=out, saved=saved)
+        h.backward(X, w, saved, g, dX=dX, grads=grads)
+    torch.cuda.synchronize()
+    h.profile_reset()
+    h.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        h.forward_train(X, w, out=out, saved=saved)
+        h.backward(X, w, saved, g, dX=dX, grads=grads)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    h.profile_enable(False)
+    prof = h.profile_read()
+    assert torch.isfinite(dX).all().item() and torch.isfinite(grads["W1"]).all().item()
+    h.close()
+    ms = elapsed / steps * 1e3
+    fwd_flops = B * 4.0 * cfg.k * cfg.L * cfg.T * cfg.D * cfg.D
+    flops = 3.0 * fwd_flops
+    per_launch = 2.0 * B * cfg.T * cfg.D * cfg.k * cfg.D
+    bwd = ("bwd_gemm_dU", "bwd_gemm_dS", "bwd_gemm_dW1", "bwd_gemm_dW2")
+    kern = max(bwd, key=lambda k: prof.get(k, {}).get("total_ms", 0.0))
+    ach = per_launch / (prof[kern]["avg_ms"] / 1e3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": kern,
+            "avg_launch_ms": round(prof[kern]["avg_ms"], 4), "algorithmic_flops_per_launch": per_launch}
+    line = {
+        "metric": "training step compute (forward keeping activations + backward): samples/s and TFLOP/s",
+        "value": round(B / (ms / 1e3), 1), "unit": "samples/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Gaussian inputs, random-init weights, Gaussian gradient of the pooled output)",
+        "config": {"workload": cfg.name + "-train", "B": B, "T": cfg.T, "H": cfg.T, "D": cfg.D, "k": cfg.k,
+                   "L": cfg.L, "parallelism": "single GPU"},
+        "tflops": round(flops / (ms / 1e3) / 1e12, 2),
+        "frac_bf16_peak": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernels_ms_per_step": {k: round(v["total_ms"] / steps, 4) for k, v in prof.items() if k != "_dropped"},
+        "roofline": roof,
+    }
+    if cpu_samples:
+        import oracle
+        n = max(1, cpu_samples // 8)
+        inp = synth.make_inputs(cfg.with_(B=n), seed=0)
+        go = synth.make_grad_out(n, cfg.D, seed=0)
+        t0 = time.perf_counter()
+        o, _, _ = oracle.forward(inp.X, inp.layers(), cfg.eps)
+        dXo, _ = oracle.backward(inp.X, inp.layers(), go, cfg.eps)
+        el = time.perf_counter() - t0
+        assert np.isfinite(dXo).all()
+        line["cpu_baseline"] = {"value": round(n / el, 3), "unit": "samples/s", "cores": int(blas_threads()),
+                                "kind": "oracle", "sample": f"{n} samples of {cfg.name}: fp64 forward + "
+                                                            f"backward, {el:.1f} s"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -305,6 +386,10 @@ def main():
         return
     from rankmixer_block_forward_amd import synth
     cfg = synth.CONFIGS[args.workload]
+    if args.backward:
+        bench_backward(cfg, args.batch or cfg.B, args.steps, args.warmup,
+                       0 if args.no_cpu_baseline else args.cpu_samples)
+        return
     batches = list(synth.SWEEP_BATCHES) if args.sweep else [args.batch or cfg.B]
     if args.sweep:
         cfg = synth.SWEEP

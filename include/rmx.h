@@ -171,9 +171,9 @@ rmx_status rmx_tokenize(const void* E, const void* Wp, const void* bp, void* X, 
  * (moe_experts == 0) only; the weights are read from W1 and W2 (w->packed must be NULL).
  *
  * rmx_saved_bytes: bytes of the saved activations for B samples (0 for a Sparse-MoE handle,
- * a NULL handle or B < 0).  Per block: S [T, B, D] (dtype), the pre-activations
- * U = S W1 + b1 and the hidden H = GELU(U) [T, B, kD] (dtype), the pre-LN2 rows
- * [T, B, D] (fp32), each padded to 256 bytes.
+ * a NULL handle or B < 0).  Per block: S [T, B, D] (dtype); GELU'(U) at the
+ * pre-activations U = S W1 + b1, and the hidden H = GELU(U), [T, B, kD] each (dtype); the
+ * pre-LN2 rows [T, B, D] (fp32); each padded to 256 bytes.
  *
  * rmx_block_forward_train: rmx_block_forward (same out, bit for bit) that also writes the
  * saved activations to `saved` (device, `saved_bytes` >= rmx_saved_bytes(h, B)).

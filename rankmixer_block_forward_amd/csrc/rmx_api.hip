@@ -70,6 +70,7 @@ struct rmx_handle {
   float* bw_part1 = nullptr;     // [2, max_batch, D]  fp32  per-sample LN1 gamma / beta gradients
   float* bw_part2 = nullptr;     // [2, max_batch, D]  fp32  per-sample LN2 gamma / beta gradients
   float* bw_sum = nullptr;       // column-sum scratch
+  float* bw_cpart = nullptr;     // [T, colsum_rows(max_batch), max(k D, D)] per-wave column sums
   std::vector<void*> allocs;     // everything hipMalloc'd, freed by rmx_destroy
   std::string last_error;
   bool prof = false;
@@ -264,7 +265,8 @@ hipError_t run_colsum(rmx_handle* h, hipStream_t s, int dtype, const void* in, f
   return e;
 }
 
-// Saved activations of one block for B samples (byte offsets, each padded to 256 bytes).
+// Saved activations of one block for B samples (byte offsets, each padded to 256 bytes):
+// S, GELU' at the pre-activations (U), the hidden H and the pre-LN2 rows Y.
 struct SavedLayout {
   size_t S, U, H, Y, per_block;
 };
@@ -670,9 +672,10 @@ static rmx_status ensure_bwd_workspace(rmx_handle* h) {
   alloc(&h->bw_part1, 2 * size_t(c.max_batch) * D * 4);
   alloc(&h->bw_part2, 2 * size_t(c.max_batch) * D * 4);
   alloc(&h->bw_sum, colsum_scratch_floats(c.T, c.max_batch, int64_t(kD > D ? kD : D)) * 4);
+  alloc(&h->bw_cpart, size_t(c.T) * colsum_rows(int(c.max_batch)) * (kD > D ? kD : D) * 4);
   if (!ok) {
     for (void* q : got) (void)hipFree(q);
-    h->bw_gY32 = h->bw_gS = h->bw_gR = h->bw_part1 = h->bw_part2 = h->bw_sum = nullptr;
+    h->bw_gY32 = h->bw_gS = h->bw_gR = h->bw_part1 = h->bw_part2 = h->bw_sum = h->bw_cpart = nullptr;
     h->bw_gY = h->bw_gU = nullptr;
     return fail(h, RMX_ERR_OUT_OF_MEMORY, "backward workspace allocation failed");
   }
@@ -763,7 +766,7 @@ rmx_status rmx_block_backward(rmx_handle* h, const void* X, int64_t B, const rmx
   for (int n = c.L - 1; n >= 0 && e == hipSuccess; --n) {
     const size_t nn = size_t(n);
     void* S_n = blk(n, lay.S);
-    void* U_n = blk(n, lay.U);
+    void* G_n = blk(n, lay.U);  // GELU' at the pre-activations
     void* H_n = blk(n, lay.H);
     if (n == c.L - 1) {
       // gradient of the last block's pre-LN2 rows from the pooled output's
@@ -782,21 +785,24 @@ rmx_status rmx_block_backward(rmx_handle* h, const void* X, int64_t B, const rmx
       ln_sums(h->bw_part2, grads->dln2_g + nn * D, grads->dln2_b + nn * D);
       if (e != hipSuccess) break;
     }
-    // db2 = sum over samples of the pre-LN2 row gradients
-    if ((e = run_colsum(h, s, DT_FP32, h->bw_gY32, grads->db2 + nn * T * D, Ti, Bi, Di)) != hipSuccess) break;
-    // gU = (gY W2^T) * GELU'(U)
+    // gU = (gY W2^T) * GELU'(U); db1 = sum over samples of gU (column sums of the matrix-core
+    // epilogue, else a pass over gU)
     GemmArgs du{};
     du.A = h->bw_gY;
     du.W = at(w->W2, nn * T * kD * D);
     du.bt = 1;
-    du.R = U_n;
+    du.R = G_n;
     du.C = h->bw_gU;
     du.G = Ti;
     du.M = Bi;
     du.N = kDi;
     du.K = Di;
+    const bool du_sums = gemm_writes_colsum(c.dtype, EPI_GELU_BWD, du);
+    du.colsum = du_sums ? h->bw_cpart : nullptr;
     if ((e = run_gemm(h, s, EPI_GELU_BWD, du, RMX_KERNEL_BWD_DU)) != hipSuccess) break;
-    if ((e = run_colsum(h, s, c.dtype, h->bw_gU, grads->db1 + nn * T * kD, Ti, Bi, kDi)) != hipSuccess) break;
+    e = du_sums ? run_colsum(h, s, DT_FP32, h->bw_cpart, grads->db1 + nn * T * kD, Ti, colsum_rows(Bi), kDi)
+                : run_colsum(h, s, c.dtype, h->bw_gU, grads->db1 + nn * T * kD, Ti, Bi, kDi);
+    if (e != hipSuccess) break;
     // dW2 = H^T gY
     GemmArgs dw2{};
     dw2.A = H_n;
@@ -830,7 +836,13 @@ rmx_status rmx_block_backward(rmx_handle* h, const void* X, int64_t B, const rmx
     ds.M = Bi;
     ds.N = Di;
     ds.K = kDi;
+    // db2 = sum over samples of the pre-LN2 row gradients (the residual this product reads)
+    const bool ds_sums = gemm_writes_colsum(c.dtype, EPI_RESID32, ds);
+    ds.colsum = ds_sums ? h->bw_cpart : nullptr;
     if ((e = run_gemm(h, s, EPI_RESID32, ds, RMX_KERNEL_BWD_DS)) != hipSuccess) break;
+    e = ds_sums ? run_colsum(h, s, DT_FP32, h->bw_cpart, grads->db2 + nn * T * D, Ti, colsum_rows(Bi), Di)
+                : run_colsum(h, s, DT_FP32, h->bw_gY32, grads->db2 + nn * T * D, Ti, Bi, Di);
+    if (e != hipSuccess) break;
     // LN1 backward, mixing transpose and first residual; then LN2 backward of block n - 1
     RowsBwdArgs ra{};
     ra.ln1_g = at(w->ln1_g, nn * D);

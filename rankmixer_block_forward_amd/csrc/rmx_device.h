@@ -119,13 +119,15 @@ __device__ __forceinline__ float gelu_erf(float u) {
   return u * (u >= 0.f ? 1.0f - q : q);
 }
 
-// GELU'(u) = Phi(u) + u phi(u), phi(u) = exp(-u^2 / 2) / sqrt(2 pi) the standard normal
-// density ("RankMixer 详解（1）", section 5.2): the same erf evaluation, its exponential
-// reused for phi.
-__device__ __forceinline__ float gelu_grad_erf(float u) {
+// GELU(u) and its derivative GELU'(u) = Phi(u) + u phi(u), phi(u) = exp(-u^2 / 2) /
+// sqrt(2 pi) the standard normal density ("RankMixer 详解（1）", section 5.2), from one erf
+// evaluation: the exponential of the tail serves phi as well.
+__device__ __forceinline__ float gelu_erf_and_grad(float u, float* grad) {
   float e;
   const float q = normal_tail(u, &e);
-  return fmaf(u * 0.39894228040143268f, e, u >= 0.f ? 1.0f - q : q);
+  const float Phi = u >= 0.f ? 1.0f - q : q;
+  *grad = fmaf(u * 0.39894228040143268f, e, Phi);
+  return u * Phi;
 }
 
 }  // namespace rmx

@@ -336,7 +336,7 @@ __device__ __forceinline__ void mfma_tile(f32x16_t (&acc)[4][4], const TileSrc& 
 template <int EPI, int NI, int NJ, bool PK, typename RowOf>
 __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], float* smem_f, const GemmArgs& p,
                                               const bf16_t* bias_g, int n0, int wrow0, int wcol0, int wave,
-                                              int lane, int g, RowOf row_of) {
+                                              int lane, int g, RowOf row_of, int colsum_row = 0) {
   constexpr int LD = NJ * 32 + 4;     // fp32 row stride of the staging rows
   constexpr int LPR = NJ * 4;         // lanes per staged row (8 columns each)
   constexpr int RPP = 64 / LPR;       // rows per pass
@@ -346,9 +346,9 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], flo
   const int rsub = lane / LPR;
   const int n = n0 + wcol0 + col8;
   const bool n_ok = n < N;
-  float bias[8];
+  float bias[8], csum[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) bias[e] = 0.f;
+  for (int e = 0; e < 8; ++e) bias[e] = csum[e] = 0.f;
   if (bias_g && n_ok) load8(bias_g + n, bias);
 
 #pragma unroll
@@ -381,23 +381,28 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], flo
           for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[e]);
           store8(static_cast<bf16_t*>(p.C) + (PK ? pko : off), v);
         } else if constexpr (EPI == EPI_GELU_SAVE) {
+          float gd[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] += bias[e];
-          store8(static_cast<bf16_t*>(p.U) + off, v);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
+          for (int e = 0; e < 8; ++e) v[e] = gelu_erf_and_grad(v[e] + bias[e], &gd[e]);
+          store8(static_cast<bf16_t*>(p.U) + off, gd);
           store8(static_cast<bf16_t*>(p.C) + off, v);
         } else if constexpr (EPI == EPI_GELU_BWD) {
-          float u[8];
-          load8(static_cast<const bf16_t*>(p.R) + off, u);
+          float gd[8];
+          load8(static_cast<const bf16_t*>(p.R) + off, gd);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] *= gelu_grad_erf(u[e]);
+          for (int e = 0; e < 8; ++e) {
+            v[e] *= gd[e];
+            csum[e] += v[e];
+          }
           store8(static_cast<bf16_t*>(p.C) + off, v);
         } else if constexpr (EPI == EPI_RESID32) {
           float rr[8];
           load8(static_cast<const float*>(p.R) + off, rr);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] += rr[e];
+          for (int e = 0; e < 8; ++e) {
+            v[e] += rr[e];
+            csum[e] += rr[e];
+          }
           store8(static_cast<float*>(p.C) + off, v);
         } else if constexpr (EPI == EPI_STORE32) {
           store8(static_cast<float*>(p.C) + off, v);
@@ -420,6 +425,17 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], flo
       }
     }
     asm volatile("" ::: "memory");
+  }
+  if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_RESID32) {
+    // column sums over the wave's rows: lanes that share columns meet by butterfly exchange
+    if (p.colsum) {
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) csum[e] += __shfl_xor(csum[e], off, 64);
+      if (rsub == 0 && n_ok)
+        store8(p.colsum + (size_t(g) * colsum_rows(p.M) + colsum_row) * N + n, csum);
+    }
   }
   // every wave is done with its staging rows before the ring memory is reused
   __syncthreads();
@@ -577,7 +593,8 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
   }
   const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
   tile_epilogue<EPI, 4, 4, PK>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, (wave >> 1) * 128,
-                               (wave & 1) * 128, wave, lane, g, [&](int m) { return m0 + m < M ? m0 + m : -1; });
+                               (wave & 1) * 128, wave, lane, g, [&](int m) { return m0 + m < M ? m0 + m : -1; },
+                               2 * mt + (wave >> 1));
 }
 
 // Sparse-MoE grouped GEMM.  Group g has rows group_start[g] .. group_start[g+1]-1 of the
@@ -869,10 +886,11 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs p) {
       if constexpr (EPI == EPI_GELU) {
         store1(static_cast<T*>(p.C) + off, gelu_erf(acc[i][j] + bias));
       } else if constexpr (EPI == EPI_GELU_SAVE) {
-        store1(static_cast<T*>(p.U) + off, acc[i][j] + bias);
-        store1(static_cast<T*>(p.C) + off, gelu_erf(acc[i][j] + bias));
+        float gd;
+        store1(static_cast<T*>(p.C) + off, gelu_erf_and_grad(acc[i][j] + bias, &gd));
+        store1(static_cast<T*>(p.U) + off, gd);
       } else if constexpr (EPI == EPI_GELU_BWD) {
-        store1(static_cast<T*>(p.C) + off, acc[i][j] * gelu_grad_erf(load1(static_cast<const T*>(p.R) + off)));
+        store1(static_cast<T*>(p.C) + off, acc[i][j] * load1(static_cast<const T*>(p.R) + off));
       } else if constexpr (EPI == EPI_RESID32) {
         static_cast<float*>(p.C)[off] = acc[i][j] + static_cast<const float*>(p.R)[off];
       } else if constexpr (EPI == EPI_STORE32) {
@@ -1024,13 +1042,28 @@ hipError_t launch_dense_mfma_t(int epi, const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_gemm(int dtype, int epi, const GemmArgs& args, hipStream_t stream) {
-  if (args.G == 0 || args.M == 0 || args.N == 0) return hipSuccess;
+namespace {
+
+GemmArgs normalized(const GemmArgs& args) {
   GemmArgs a = args;
   if (a.lda == 0) a.lda = a.at ? a.M : a.K;
   if (a.ldc == 0) a.ldc = a.N;
   if (a.sa == 0) a.sa = a.at ? int64_t(a.K) * a.lda : int64_t(a.M) * a.lda;
   if (a.sc == 0) a.sc = int64_t(a.M) * a.ldc;
+  return a;
+}
+
+}  // namespace
+
+bool gemm_writes_colsum(int dtype, int epi, const GemmArgs& args) {
+  const GemmArgs a = normalized(args);
+  return (epi == EPI_GELU_BWD || epi == EPI_RESID32) && !a.packed &&
+         gemm_uses_mfma(dtype, a.M, a.N, a.K, a.lda, a.at, a.bt) && (a.sa % 8) == 0;
+}
+
+hipError_t launch_gemm(int dtype, int epi, const GemmArgs& args, hipStream_t stream) {
+  if (args.G == 0 || args.M == 0 || args.N == 0) return hipSuccess;
+  GemmArgs a = normalized(args);
   const bool bwd_epi = epi == EPI_GELU_BWD || epi == EPI_RESID32 || epi == EPI_STORE32;
   if ((a.at || a.bt) && !bwd_epi) return hipErrorInvalidValue;
   if (a.packed) {

@@ -141,12 +141,15 @@ hipError_t launch_moe_combine(const MoeArgs& a, hipStream_t stream);
 //   group g owns compacted rows group_start[g] .. group_start[g + 1] - 1.
 //   EPI_BIAS:  C [G, M, N] (dtype) = A W + bias
 //   Backward products (no bias):
-//   EPI_GELU_BWD: C [G, M, N] (dtype) = (A W) * GELU'(R),  R [G, M, N] (dtype, the
-//                 pre-activations U, same layout as C)
+//   EPI_GELU_BWD: C [G, M, N] (dtype) = (A W) * R,  R [G, M, N] (dtype, GELU' at the
+//                 pre-activations, same layout as C)
 //   EPI_RESID32:  C [G, M, N] (fp32)  = A W + R,  R [G, M, N] (fp32)
 //   EPI_STORE32:  C [G, M, N] (fp32)  = A W
+//   With colsum set (matrix-core kernels only), EPI_GELU_BWD also writes the column sums of
+//   its fp32 output and EPI_RESID32 those of R, over the 128 rows of each wave:
+//   colsum [G, colsum_rows(M), N] fp32, row 2 * (row tile) + (row half of the tile).
 //   Training forward:
-//   EPI_GELU_SAVE: EPI_GELU that also stores the pre-activations A W + bias in U
+//   EPI_GELU_SAVE: EPI_GELU that also stores GELU'(A W + bias) in U
 //                  ([G, M, N], dtype, C's layout; row-major operands only)
 enum Epilogue {
   EPI_GELU = 0, EPI_RESID = 1, EPI_MOE1 = 2, EPI_MOE2 = 3, EPI_BIAS = 4,
@@ -176,8 +179,11 @@ struct GemmArgs {
   //   at: A is [G][K][M], element (m, k) at A + g * sa + k * lda + m (lda = 0: M, sa = 0: K * M)
   //   bt: W is [G][N][K], element (k, n) at W + g * N * K + n * K + k
   int at, bt;
-  void* U;  // EPI_GELU_SAVE: the pre-activations
+  void* U;         // EPI_GELU_SAVE: GELU' at the pre-activations
+  float* colsum;   // EPI_GELU_BWD, EPI_RESID32: per-wave column sums, nullable
 };
+// Rows of the per-wave column sums of one group: two per 256-row tile.
+__host__ __device__ inline int colsum_rows(int M) { return 2 * ((M + 255) / 256); }
 // Rows per token up to which the dense launch uses 64-row tiles.
 constexpr int GEMM_SMALL_M = 64;
 
@@ -189,6 +195,8 @@ hipError_t launch_gemm_moe(int epi, const GemmArgs& a, hipStream_t stream);
 bool gemm_moe_supported(int N, int K, int64_t a_rows);
 hipError_t gemm_init();
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t stream);
+// True when launch_gemm(dtype, epi, a) runs a matrix-core kernel that writes a.colsum.
+bool gemm_writes_colsum(int dtype, int epi, const GemmArgs& a);
 // W [G][K][N] (bf16, row-major) -> W^T [G][pk_rows(N) x K] in the packed operand layout
 // (padding rows zero); K % 32 == 0.
 hipError_t launch_pack_weights(const void* W, void* out, int G, int K, int N, hipStream_t stream);

@@ -218,6 +218,7 @@ __global__ __launch_bounds__(256) void colsum_kernel(const T* __restrict__ in, f
   for (int e = 0; e < W; ++e) acc[e] = 0.f;
   if (col < N) {
     const T* src = in + size_t(g) * R * N + col;
+#pragma unroll 4
     for (int r = r0 + wave; r < r1; r += 4) {
       float v[W];
       loadw<W>(src + size_t(r) * N, v);
