@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "samples/sec + achieved TFLOP/s (% bf16 MFMA peak) for RankMixer-1B block fwd"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 GEMM_SOURCE = os.path.join(ROOT, "rankmixer_block_forward_amd", "csrc", "rmx_gemm.hip")
@@ -39,6 +40,8 @@ def parse():
     p.add_argument("--sweep", action="store_true", help="one line per serving batch size")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-samples", type=int, default=384)
+    p.add_argument("--mxfp8", action="store_true",
+                   help="the MXFP8 inference variant (weights prepared with rmx_pack_weights_mxfp8)")
     p.add_argument("--backward", action="store_true",
                    help="time one training step's compute instead: forward keeping activations + backward")
     p.add_argument("--tokenize", action="store_true",
@@ -102,7 +105,7 @@ def moe_active_flops(h, X, w, cfg, B):
     return flops, active / gates.numel()
 
 
-def time_forward(cfg, B, steps, warmup, calibrate_copy=False):
+def time_forward(cfg, B, steps, warmup, calibrate_copy=False, mxfp8=False):
     import torch
     import rankmixer_block_forward_amd as rmx
     from rankmixer_block_forward_amd import synth
@@ -114,7 +117,11 @@ def time_forward(cfg, B, steps, warmup, calibrate_copy=False):
     print(f"[bench] inputs {cfg.name} B={B} generated and resident in {time.time() - t0:.1f}s",
           file=sys.stderr, flush=True)
     h = rmx.Handle.for_config(cfg, max_batch=B)
-    if h.packed_weights_bytes() > 0:
+    if mxfp8:
+        # weights quantized once to MXFP8 (model-load work, outside the timed region)
+        w["packed_mxfp8"] = h.pack_weights_mxfp8(w)
+        torch.cuda.synchronize()
+    elif h.packed_weights_bytes() > 0:
         # weights prepared once for the matrix cores (model-load work, outside the timed region)
         w["packed"] = h.pack_weights(w)
         torch.cuda.synchronize()
@@ -153,19 +160,19 @@ def time_forward(cfg, B, steps, warmup, calibrate_copy=False):
     return elapsed, prof, moe
 
 
-def roofline(cfg, B, prof):
+def roofline(cfg, B, prof, peak_tflops=PEAK_BF16_TFLOPS):
     counts = gemm_counts(cfg, B)
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ridge = peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9)
     # dominant kernel: the grouped GEMM with the larger total time
     kern = max(counts, key=lambda k: prof.get(k, {}).get("total_ms", 0.0))
     flops, nbytes = counts[kern]
     avg_s = prof[kern]["avg_ms"] / 1e3
     mfma_bound = flops / nbytes > ridge
-    traffic = traffic_for(kern, cfg, B)
+    traffic = traffic_for(kern, cfg, B) if peak_tflops == PEAK_BF16_TFLOPS else None
     if mfma_bound:
         achieved = flops / avg_s / 1e12
-        r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-             "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+        r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_tflops, "unit": "TFLOP/s",
+             "frac": round(achieved / peak_tflops, 4)}
     else:
         achieved = nbytes / avg_s / 1e9
         r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -394,7 +401,7 @@ def main():
     if args.sweep:
         cfg = synth.SWEEP
     for B in batches:
-        elapsed, prof, moe = time_forward(cfg, B, args.steps, args.warmup, args.calibrate_copy)
+        elapsed, prof, moe = time_forward(cfg, B, args.steps, args.warmup, args.calibrate_copy, args.mxfp8)
         ms = elapsed / args.steps * 1e3
         flops = B * 4.0 * cfg.k * cfg.L * cfg.T * cfg.D * cfg.D if moe is None else moe[0]
         tflops = flops / (ms / 1e3) / 1e12
@@ -417,8 +424,14 @@ def main():
             "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
             "kernels_ms_per_step": {k: round(v["total_ms"] / args.steps, 4) for k, v in prof.items()
                                     if k != "_dropped"},
-            "roofline": roofline(cfg, B, prof) if moe is None else moe_roofline(cfg, B, prof, moe),
+            "roofline": (moe_roofline(cfg, B, prof, moe) if moe is not None else
+                         roofline(cfg, B, prof, PEAK_FP8_TFLOPS if args.mxfp8 else PEAK_BF16_TFLOPS)),
         }
+        if args.mxfp8:
+            line["metric"] = METRIC.replace("block fwd", "block fwd, MXFP8 inference variant")
+            line["dtype"] = "mxfp8 (E4M3 operands, E8M0 scales per 32; bf16 activations)"
+            line["config"]["workload"] = cfg.name + "-mxfp8"
+            line["frac_fp8_peak"] = round(tflops / PEAK_FP8_TFLOPS, 4)
         if moe is not None:
             line["config"].update(experts=cfg.E, expert_hidden=cfg.moe_hidden, active_fraction=round(moe[1], 4))
         if not args.sweep and not args.no_cpu_baseline:

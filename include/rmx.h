@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RMX_ABI_VERSION 3
+#define RMX_ABI_VERSION 4
 
 typedef struct rmx_handle rmx_handle; /* opaque, owned by the library */
 
@@ -94,7 +94,9 @@ typedef struct {
  * packed: NULL, or W1 and W2 of all blocks prepared by rmx_pack_weights for this handle
  *   (dense bf16 handles whose D and k*D are multiples of 32).  When set, the forward reads
  *   the weights from it (W1 and W2 are then unused and may be NULL); the result is the
- *   same bit for bit.                                                                   */
+ *   same bit for bit.
+ * packed_mxfp8: NULL, or W1 and W2 of all blocks prepared by rmx_pack_weights_mxfp8; when
+ *   set (and packed is NULL) the forward runs the MXFP8 inference variant (see there).   */
 typedef struct {
   const void* W1;
   const void* b1;
@@ -110,6 +112,7 @@ typedef struct {
   const void* We2;
   const void* be2;
   const void* packed;
+  const void* packed_mxfp8;
 } rmx_weights;
 
 /* Validates cfg, checks that the current HIP device is gfx950, and allocates the
@@ -152,6 +155,26 @@ rmx_status rmx_token_mix(const void* X, void* Y, int64_t B, int32_t T, int32_t D
 size_t rmx_packed_weights_bytes(const rmx_handle* h);
 rmx_status rmx_pack_weights(rmx_handle* h, const rmx_weights* w, int32_t L, void* packed, size_t bytes,
                             void* stream);
+
+/* MXFP8 inference variant.  The pages serve the model at reduced precision because its
+ * core is a few large products and halving the operand width doubles the hardware peak
+ * ("RankMixer" paper translation, section 4.6, eq (13)); on gfx950 the step beyond bf16 is
+ * 8-bit operands.  The operands of both per-token products are stored in MXFP8 as the OCP
+ * Microscaling Formats (MX) Specification v1.0 defines it: FP8 E4M3 codes, one power-of-two
+ * scale 2^(floor(log2 amax) - 8) per 32 consecutive values along K, each value rounded to the
+ * nearest E4M3 number (ties to even, saturating at +-448).  Quantized: S along D per row, H
+ * = GELU(S W1 + b1) along kD per row, W1[t] and W2[t] along K per output column.  Products
+ * accumulate in fp32 on the matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4); bias, GELU,
+ * residual (S in bf16), LayerNorm and pool as in the bf16 forward.  Expect about 4e-2
+ * relative difference from the unquantized forward (the format's precision).
+ * rmx_packed_weights_mxfp8_bytes: bytes of W1 and W2 of all L blocks in this form, or 0 when
+ * the handle has no such path (it needs a dense bf16 handle with D and k*D multiples of 64).
+ * rmx_pack_weights_mxfp8: reads w->W1 and w->W2 (device, bf16) and writes them to `packed`
+ * (device, `bytes` >= the size above, 16-byte aligned), enqueued on `stream`; pass it as
+ * rmx_weights.packed_mxfp8. */
+size_t rmx_packed_weights_mxfp8_bytes(const rmx_handle* h);
+rmx_status rmx_pack_weights_mxfp8(rmx_handle* h, const rmx_weights* w, int32_t L, void* packed, size_t bytes,
+                                  void* stream);
 
 /* Tokenisation projection, the step before the first block: the concatenated feature
  * embedding E [B, T*d] (device, dtype) is cut into T half-open slices of d coordinates and

@@ -22,6 +22,7 @@ KERNEL_COUNT = 14
 EXPORTS = (
     "rmx_create", "rmx_destroy", "rmx_block_forward", "rmx_block_forward_ex", "rmx_token_mix",
     "rmx_tokenize", "rmx_packed_weights_bytes", "rmx_pack_weights",
+    "rmx_packed_weights_mxfp8_bytes", "rmx_pack_weights_mxfp8",
     "rmx_saved_bytes", "rmx_block_forward_train", "rmx_block_backward",
     "rmx_profile_enable", "rmx_profile_read", "rmx_profile_reset", "rmx_kernel_name",
     "rmx_status_string", "rmx_last_error", "rmx_abi_version",
@@ -42,7 +43,7 @@ class rmx_config(ctypes.Structure):
 
 
 WEIGHT_NAMES = ("W1", "b1", "W2", "b2", "ln1_g", "ln1_b", "ln2_g", "ln2_b",
-                "Wg", "We1", "be1", "We2", "be2", "packed")
+                "Wg", "We1", "be1", "We2", "be2", "packed", "packed_mxfp8")
 
 
 class rmx_weights(ctypes.Structure):
@@ -78,6 +79,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rmx_packed_weights_bytes.argtypes = [vp]
     lib.rmx_packed_weights_bytes.restype = ctypes.c_size_t
     lib.rmx_pack_weights.argtypes = [vp, ctypes.POINTER(rmx_weights), i32, vp, ctypes.c_size_t, vp]
+    lib.rmx_packed_weights_mxfp8_bytes.argtypes = [vp]
+    lib.rmx_packed_weights_mxfp8_bytes.restype = ctypes.c_size_t
+    lib.rmx_pack_weights_mxfp8.argtypes = [vp, ctypes.POINTER(rmx_weights), i32, vp, ctypes.c_size_t, vp]
     lib.rmx_saved_bytes.argtypes = [vp, i64]
     lib.rmx_saved_bytes.restype = ctypes.c_size_t
     lib.rmx_block_forward_train.argtypes = [vp, vp, i64, ctypes.POINTER(rmx_weights), i32, i32, vp, vp,
@@ -97,7 +101,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rmx_abi_version.restype = i32
     for name in EXPORTS:
         if name not in ("rmx_kernel_name", "rmx_status_string", "rmx_last_error", "rmx_abi_version",
-                        "rmx_packed_weights_bytes", "rmx_saved_bytes"):
+                        "rmx_packed_weights_bytes", "rmx_saved_bytes", "rmx_packed_weights_mxfp8_bytes"):
             getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -182,10 +186,11 @@ class Handle:
         self.close()
 
     def _weights(self, w: dict) -> rmx_weights:
+        import torch
         s = rmx_weights()
         for n in WEIGHT_NAMES:
             t = w.get(n)
-            setattr(s, n, _ptr(t, n, self.dtype))
+            setattr(s, n, _ptr(t, n, torch.uint8 if n == "packed_mxfp8" else self.dtype))
         return s
 
     def packed_weights_bytes(self) -> int:
@@ -203,6 +208,23 @@ class Handle:
         ws = self._weights({"W1": weights["W1"], "W2": weights["W2"]})
         _check(self._lib.rmx_pack_weights(self._h, ctypes.byref(ws), self.cfg.L, _ptr(packed, "packed"), nbytes,
                                           _stream(stream)), self._h)
+        return packed
+
+    def packed_weights_mxfp8_bytes(self) -> int:
+        """Bytes of W1 and W2 in MXFP8 (0 when this handle has no such path)."""
+        return int(self._lib.rmx_packed_weights_mxfp8_bytes(self._h))
+
+    def pack_weights_mxfp8(self, weights: dict, stream=None):
+        """W1 and W2 of all blocks quantized to MXFP8 (rmx_pack_weights_mxfp8): a device byte
+        tensor to pass as weights["packed_mxfp8"]; the forward then runs the MXFP8 variant."""
+        import torch
+        nbytes = self.packed_weights_mxfp8_bytes()
+        if nbytes == 0:
+            raise RmxError(RMX_ERR_UNSUPPORTED, "this handle has no MXFP8 path")
+        packed = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        ws = self._weights({"W1": weights["W1"], "W2": weights["W2"]})
+        _check(self._lib.rmx_pack_weights_mxfp8(self._h, ctypes.byref(ws), self.cfg.L, _ptr(packed, "packed"),
+                                                nbytes, _stream(stream)), self._h)
         return packed
 
     def forward(self, X, weights: dict, out=None, xl_out=None, gate_out=None, stream=None,

@@ -48,6 +48,11 @@ struct rmx_handle {
   // Dense bf16 handles with D and kD multiples of 32 can run on prepared weights; S and H
   // then take the packed operand layout and are sized for pk_rows(max_batch) rows.
   bool pk_capable = false;
+  // pk_capable handles with D and kD multiples of 64 also run the MXFP8 variant: S in MXFP8
+  // (codes [T, pk_rows(max_batch), D] bytes, then their scales, 1/32 of that), and H in
+  // MXFP8 in the H buffer (codes, then scales)
+  bool mx_capable = false;
+  void* S8 = nullptr;
   // Sparse-MoE workspace (moe_experts > 0); G = T * E groups, R = G * max_batch rows
   float* moe_g = nullptr;        // [G, max_batch]
   int* moe_cnt = nullptr;        // [G, nchunk]
@@ -249,6 +254,14 @@ hipError_t run_gemm(rmx_handle* h, hipStream_t s, int epi, const GemmArgs& a, in
   return e;
 }
 
+hipError_t run_gemm_mx(rmx_handle* h, hipStream_t s, int epi, const GemmArgs& a) {
+  ProfPair pp;
+  prof_begin(h, s, &pp, epi == EPI_GELU_MX ? RMX_KERNEL_GEMM1 : RMX_KERNEL_GEMM2);
+  hipError_t e = launch_gemm_mx(epi, a, s);
+  prof_end(h, s, &pp);
+  return e;
+}
+
 hipError_t run_rows_bwd(rmx_handle* h, hipStream_t s, int mode, const RowsBwdArgs& a) {
   ProfPair pp;
   prof_begin(h, s, &pp, RMX_KERNEL_BWD_ROWS);
@@ -371,9 +384,11 @@ rmx_status rmx_create(const rmx_config* cfg, rmx_handle** out_handle) {
   };
   h->pk_capable = cfg->moe_experts == 0 && cfg->dtype == RMX_BF16 && cfg->D % 32 == 0 &&
                   (int64_t(cfg->k) * cfg->D) % 32 == 0;
+  h->mx_capable = h->pk_capable && cfg->D % 64 == 0 && (int64_t(cfg->k) * cfg->D) % 64 == 0;
   const size_t prow = h->pk_capable ? size_t(cfg->T) * size_t(pk_rows(cfg->max_batch)) : rows;
   if (rows > 0) {
     alloc(&h->S, prow * cfg->D * esz);
+    if (h->mx_capable) alloc(&h->S8, prow * cfg->D + prow * cfg->D / 32);
     alloc(&h->Y, nS * sizeof(float));
     if (cfg->moe_experts == 0) {
       alloc(&h->H, prow * size_t(cfg->k) * cfg->D * esz);
@@ -454,7 +469,7 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
   if (train && (st = check_dev(h, saved, rmx_saved_bytes(h, B), dev, "saved")) != RMX_OK) return st;
   const size_t E = size_t(c.moe_experts), hid = size_t(c.moe_hidden);
   if (moe) {
-    if (w->packed) return fail(h, RMX_ERR_UNSUPPORTED, "prepared weights are for dense handles");
+    if (w->packed || w->packed_mxfp8) return fail(h, RMX_ERR_UNSUPPORTED, "prepared weights are for dense handles");
     if ((st = check_dev(h, w->Wg, Ls * T * D * E * esz, dev, "Wg")) != RMX_OK) return st;
     if ((st = check_dev(h, w->We1, Ls * T * E * D * hid * esz, dev, "We1")) != RMX_OK) return st;
     if ((st = check_dev(h, w->We2, Ls * T * E * hid * D * esz, dev, "We2")) != RMX_OK) return st;
@@ -465,6 +480,12 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
     if (!h->pk_capable)
       return fail(h, RMX_ERR_UNSUPPORTED, "prepared weights need a dense bf16 handle with D and k*D multiples of 32");
     if ((st = check_dev(h, w->packed, rmx_packed_weights_bytes(h), dev, "packed")) != RMX_OK) return st;
+  } else if (w->packed_mxfp8) {
+    if (!h->mx_capable)
+      return fail(h, RMX_ERR_UNSUPPORTED, "MXFP8 weights need a dense bf16 handle with D and k*D multiples of 64");
+    if (train) return fail(h, RMX_ERR_INVALID_ARG, "training reads W1 and W2: packed_mxfp8 must be NULL");
+    if ((st = check_dev(h, w->packed_mxfp8, rmx_packed_weights_mxfp8_bytes(h), dev, "packed_mxfp8")) != RMX_OK)
+      return st;
   } else {
     if ((st = check_dev(h, w->W1, Ls * T * D * kD * esz, dev, "W1")) != RMX_OK) return st;
     if ((st = check_dev(h, w->W2, Ls * T * kD * D * esz, dev, "W2")) != RMX_OK) return st;
@@ -511,8 +532,15 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
   hipError_t e = hipSuccess;
   const int Bi = int(B);
   const bool pk = !moe && w->packed != nullptr;
+  const bool mx = !moe && !pk && w->packed_mxfp8 != nullptr;
   // prepared weights of block n: W1^T then W2^T, packed (elements)
   const size_t pk_w1 = T * size_t(pk_rows(int64_t(kD))) * D, pk_w2 = T * size_t(pk_rows(int64_t(D))) * kD;
+  // MXFP8 weights of block n (bytes): W1^T codes, their scales, W2^T codes, their scales;
+  // S and H in MXFP8: codes, then scales
+  const size_t mx_w1 = pk_w1, mx_w2 = pk_w2, mx_blk = (mx_w1 + mx_w2) / 32 * 33;
+  const size_t pkB = size_t(pk_rows(B));
+  char* S8 = static_cast<char*>(h->S8);
+  char* H8 = static_cast<char*>(h->H);
   for (int n = 0; n < c.L && e == hipSuccess; ++n) {
     RowsArgs ra{};
     ra.in = n == 0 ? X : static_cast<const void*>(Y_of(n - 1));
@@ -525,7 +553,11 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
     ra.T = c.T;
     ra.D = c.D;
     ra.eps = c.ln_eps;
-    ra.s_packed = pk ? 1 : 0;
+    ra.s_packed = (pk || mx) ? 1 : 0;
+    if (mx) {
+      ra.s8 = S8;
+      ra.s8_scale = S8 + T * pkB * D;
+    }
     e = run_rows(h, s, n == 0 ? ROWS_FIRST : ROWS_MID, ra);
     if (e != hipSuccess) break;
 
@@ -578,6 +610,37 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
       m2.row_gate = h->moe_row_gate;
       if ((e = run_moe_gemm(h, s, EPI_MOE2, m2)) != hipSuccess) break;
       e = run_moe_combine(h, s, ma);
+      continue;
+    }
+
+    if (mx) {
+      const char* wb = static_cast<const char*>(w->packed_mxfp8) + size_t(n) * mx_blk;
+      GemmArgs m1{};
+      m1.A = S8;
+      m1.A_scale = S8 + T * pkB * D;
+      m1.W = wb;
+      m1.W_scale = wb + mx_w1;
+      m1.bias = at(w->b1, size_t(n) * T * kD);
+      m1.C = H8;
+      m1.C_scale = H8 + T * pkB * kD;
+      m1.G = c.T;
+      m1.M = Bi;
+      m1.N = int(kD);
+      m1.K = c.D;
+      if ((e = run_gemm_mx(h, s, EPI_GELU_MX, m1)) != hipSuccess) break;
+      GemmArgs m2{};
+      m2.A = H8;
+      m2.A_scale = H8 + T * pkB * kD;
+      m2.W = wb + mx_w1 / 32 * 33;
+      m2.W_scale = wb + mx_w1 / 32 * 33 + mx_w2;
+      m2.bias = at(w->b2, size_t(n) * T * D);
+      m2.R = h->S;
+      m2.C = h->Y;
+      m2.G = c.T;
+      m2.M = Bi;
+      m2.N = c.D;
+      m2.K = int(kD);
+      e = run_gemm_mx(h, s, EPI_RESID, m2);
       continue;
     }
 
@@ -916,6 +979,58 @@ rmx_status rmx_pack_weights(rmx_handle* h, const rmx_weights* w, int32_t L, void
     hipError_t e = launch_pack_weights(static_cast<const uint16_t*>(w->W1) + n * T * D * kD, dst, c.T, c.D, int(kD), s);
     if (e == hipSuccess)
       e = launch_pack_weights(static_cast<const uint16_t*>(w->W2) + n * T * kD * D, dst + pk_w1, c.T, int(kD), c.D, s);
+    if (e != hipSuccess) return fail(h, RMX_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
+  return RMX_OK;
+}
+
+size_t rmx_packed_weights_mxfp8_bytes(const rmx_handle* h) {
+  if (!h || !h->mx_capable) return 0;
+  const rmx_config& c = h->cfg;
+  const size_t T = c.T, D = c.D, kD = size_t(c.k) * c.D;
+  const size_t codes = T * size_t(pk_rows(int64_t(kD))) * D + T * size_t(pk_rows(int64_t(D))) * kD;
+  return size_t(c.L) * (codes / 32 * 33);
+}
+
+rmx_status rmx_pack_weights_mxfp8(rmx_handle* h, const rmx_weights* w, int32_t L, void* packed, size_t bytes,
+                                  void* stream) {
+  if (!h) return fail(nullptr, RMX_ERR_INVALID_ARG, "handle is NULL");
+  clear_error(h);
+  const rmx_config& c = h->cfg;
+  if (!w) return fail(h, RMX_ERR_INVALID_ARG, "weights is NULL");
+  if (L != c.L) return fail(h, RMX_ERR_INVALID_ARG, "L=%d but the handle was created with L=%d", L, c.L);
+  if (!h->mx_capable)
+    return fail(h, RMX_ERR_UNSUPPORTED, "MXFP8 weights need a dense bf16 handle with D and k*D multiples of 64");
+  const size_t need = rmx_packed_weights_mxfp8_bytes(h);
+  if (bytes < need) return fail(h, RMX_ERR_INVALID_ARG, "packed buffer of %zu bytes, %zu needed", bytes, need);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
+    (void)hipGetLastError();
+    return fail(h, RMX_ERR_INVALID_ARG, "current device %d is not the handle's device %d", dev, h->device);
+  }
+  const size_t T = c.T, D = c.D, kD = size_t(c.k) * c.D, Ls = c.L;
+  rmx_status st;
+  if ((st = check_dev(h, w->W1, Ls * T * D * kD * 2, dev, "W1")) != RMX_OK) return st;
+  if ((st = check_dev(h, w->W2, Ls * T * kD * D * 2, dev, "W2")) != RMX_OK) return st;
+  if ((st = check_dev(h, packed, need, dev, "packed")) != RMX_OK) return st;
+  const uintptr_t pb = reinterpret_cast<uintptr_t>(packed);
+  for (const void* src : {w->W1, w->W2}) {
+    const uintptr_t sb = reinterpret_cast<uintptr_t>(src);
+    if (pb < sb + Ls * T * D * kD * 2 && sb < pb + need)
+      return fail(h, RMX_ERR_INVALID_ARG, "packed overlaps W1 or W2");
+  }
+  // per block: W1^T codes [T][pk_rows(kD) x D], their scales, W2^T codes [T][pk_rows(D) x kD],
+  // their scales
+  const size_t c1 = T * size_t(pk_rows(int64_t(kD))) * D, c2 = T * size_t(pk_rows(int64_t(D))) * kD;
+  const size_t blk = (c1 + c2) / 32 * 33;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (size_t n = 0; n < Ls; ++n) {
+    char* dst = static_cast<char*>(packed) + n * blk;
+    hipError_t e = launch_pack_weights_mx(static_cast<const uint16_t*>(w->W1) + n * T * D * kD, dst, dst + c1, c.T,
+                                          c.D, int(kD), s);
+    if (e == hipSuccess)
+      e = launch_pack_weights_mx(static_cast<const uint16_t*>(w->W2) + n * T * kD * D, dst + c1 / 32 * 33,
+                                 dst + c1 / 32 * 33 + c2, c.T, int(kD), c.D, s);
     if (e != hipSuccess) return fail(h, RMX_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   }
   return RMX_OK;

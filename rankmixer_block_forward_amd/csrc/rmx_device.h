@@ -75,6 +75,46 @@ __device__ __forceinline__ size_t pk_off(int row, int col, int K) {
   return ((size_t(rb) * size_t(K >> 5) + size_t(kt)) << 13) + size_t(r << 5) + size_t((c ^ pk_swz(r)) << 3);
 }
 
+// ---- MXFP8 operands (OCP Microscaling Formats (MX) Specification v1.0, FP8 E4M3 elements,
+// one E8M0 power-of-two scale per 32 consecutive values along K).  A matrix [rows, K]
+// (K % 64 == 0, rows padded to a multiple of 256) is stored as blocks of 256 rows x 64 K
+// (16 KB), ordered [row block][K step]; inside a block row r holds four 16-byte chunks of
+// 16 consecutive k, chunk c at position c ^ pk_swz(r).  Its scales are 512 bytes per block,
+// laid out so that lane l of the wave that owns rows 128 h .. 128 h + 127 of the block finds
+// the scales of rows 128 h + 32 i + (l % 32), i = 0..3, for the 32-value half l / 32 of the
+// K step in one 32-bit word, byte i: the scale operand of the MFMA.
+// byte offset of (row, k), k % 16 == 0 (the start of a chunk; + 8 for its second half)
+__device__ __forceinline__ size_t mx_off(int row, int k, int K) {
+  const int rb = row >> 8, r = row & 255, kt = k >> 6, c = (k >> 4) & 3;
+  return ((size_t(rb) * size_t(K >> 6) + size_t(kt)) << 14) + size_t(r << 6) + size_t((c ^ pk_swz(r)) << 4);
+}
+// byte offset of the scale of (row, 32-value block kb)
+__device__ __forceinline__ size_t mx_scale_off(int row, int kb, int K) {
+  const int rb = row >> 8, r = row & 255;
+  return ((size_t(rb) * size_t(K >> 6) + size_t(kb >> 1)) << 9) + size_t((r >> 7) << 8) +
+         size_t((((kb & 1) << 5) | (r & 31)) << 2) + size_t((r >> 5) & 3);
+}
+// Biased E8M0 scale of a block whose largest magnitude is amax: 2^(floor(log2 amax) - 8),
+// 8 the top exponent of E4M3, clamped below at 2^-127 (an all-zero block takes 2^-127).
+// From the fp32 exponent field e: floor(log2 amax) - 8 + 127 = e - 8.
+__device__ __forceinline__ uint32_t mx_scale_bits(float amax) {
+  const uint32_t e = (__float_as_uint(amax) >> 23) & 0xffu;
+  return e > 8u ? e - 8u : 0u;
+}
+// 1 / scale as fp32: 2^(127 - bits), a normal number for every bits the above returns.
+__device__ __forceinline__ float mx_inv_scale(uint32_t bits) { return __uint_as_float((254u - bits) << 23); }
+// Eight values (already multiplied by 1 / scale) to E4M3 codes, round to nearest even,
+// saturating at +-448 (the conversion itself would give NaN from 480 up); byte e = v[e].
+__device__ __forceinline__ uint2 e4m3_pack8(const float* v) {
+  auto sat = [](float x) { return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f); };
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat(v[0]), sat(v[1]), lo, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat(v[2]), sat(v[3]), lo, true);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(sat(v[4]), sat(v[5]), hi, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(sat(v[6]), sat(v[7]), hi, true);
+  return make_uint2(lo, hi);
+}
+
 // ---- Token Mixing index map (H = T).  Output row h, column c takes head h of token
 // t = c / q at position r = c % q:  M[h, c] = X[t, h*q + r].  Returns the source column
 // in token t's row; *t_out receives t.  (RankMixer paper translation, section 3.3.1

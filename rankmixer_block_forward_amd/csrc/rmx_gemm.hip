@@ -372,6 +372,29 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], flo
       const float4 x1 = *reinterpret_cast<const float4*>(st + row * LD + col8 + 4);
       v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
       v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+      if constexpr (EPI == EPI_GELU_MX) {
+        // GELU, then MXFP8 along the row: the 32 columns of one scale block are the 8
+        // columns of 4 neighbouring lanes of this row (shuffles run on every lane)
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[e] = gelu_erf(v[e] + bias[e]);
+          amax = fmaxf(amax, fabsf(v[e]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+        const uint32_t sb = mx_scale_bits(amax);
+        const float inv = mx_inv_scale(sb);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= inv;
+        const uint2 q = e4m3_pack8(v);
+        if (orow >= 0 && n_ok) {
+          const size_t gm = size_t(g) * size_t(pk_rows(p.M)) * size_t(N);
+          *reinterpret_cast<uint2*>(static_cast<uint8_t*>(p.C) + gm + mx_off(orow, n, N) + ((n >> 3) & 1) * 8) = q;
+          if ((lane & 3) == 0) static_cast<uint8_t*>(p.C_scale)[gm / 32 + mx_scale_off(orow, n >> 5, N)] = uint8_t(sb);
+        }
+        continue;
+      }
       if (orow >= 0 && n_ok) {
         const size_t off = size_t(g) * size_t(p.sc) + size_t(orow) * size_t(p.ldc) + n;
         size_t pko = 0;
@@ -595,6 +618,206 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
   tile_epilogue<EPI, 4, 4, PK>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, (wave >> 1) * 128,
                                (wave & 1) * 128, wave, lane, g, [&](int m) { return m0 + m < M ? m0 + m : -1; },
                                2 * mt + (wave >> 1));
+}
+
+// ------------------------------------------------------------- MXFP8 products
+// The prepared-operand K loop with 8-bit operands: a K step is 64 values, so a stage holds
+// the same 16 KB per operand (256 rows x 64 E4M3 codes, one contiguous block of the MXFP8
+// layout) plus the step's scales (512 bytes per operand, one 32-bit LDS read per lane and
+// operand).  Each 32 x 32 block takes one v_mfma_scale_f32_32x32x64_f8f6f4 per step: lane l
+// supplies row l % 32 of each operand, h = l / 32: bytes 0-15 are k 16 h .. 16 h + 15 (of
+// the step's first 32-value scale block), bytes 16-31 are k 32 + 16 h .. 32 + 16 h + 15 (of
+// the second), i.e. chunks h and h + 2 of the row (two 16-byte LDS reads); the scale that
+// lanes of half h supply (the byte the instruction selects) is that of scale block h.  The
+// W fragment goes first, as in the bf16 loop, so the accumulator layout (and the epilogue)
+// is the same.  Per stage and wave: 8 code copies of 1 KB and one scale copy of 256 bytes
+// (waves 0, 1: the two halves of A's scales; waves 2, 3: W's).
+constexpr int MX_BK = 64;
+constexpr int MX_CODE_BYTES = 16384;                         // one operand's codes per stage
+constexpr int MX_STAGE_BYTES = 2 * MX_CODE_BYTES + 1024;     // + both operands' scales
+constexpr int MX_COPIES = 9;                                 // LDS-destination loads per wave per step
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// One LDS-destination buffer load of 4 bytes per lane: 64 lanes x 4 B to lds_dst + 4 * lane.
+__device__ __forceinline__ void copy_to_lds_b32(uint32_t lds_dst, uint32_t voff, __amdgpu_buffer_rsrc_t rsrc,
+                                                int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds_dst), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
+struct MxFrags {
+  u32x4_t a[4][2];  // A rows of the 4 row blocks: 32 codes each (two chunks)
+  u32x4_t b[4][2];  // W^T rows (output columns) of the 4 column blocks
+  uint32_t sa, sw;  // scale bytes of the 4 row blocks / 4 column blocks
+};
+
+template <int I, int J>
+__device__ __forceinline__ void mx_mma(f32x16_t (&acc)[4][4], const MxFrags& f) {
+  const u32x4_t a0 = f.a[I][0], a1 = f.a[I][1], b0 = f.b[J][0], b1 = f.b[J][1];
+  const i32x8_t a = {int(a0.x), int(a0.y), int(a0.z), int(a0.w), int(a1.x), int(a1.y), int(a1.z), int(a1.w)};
+  const i32x8_t b = {int(b0.x), int(b0.y), int(b0.z), int(b0.w), int(b1.x), int(b1.y), int(b1.z), int(b1.w)};
+  // format 0 = FP8 E4M3 for both operands; scale byte J of sw for the first, I of sa for the second
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc[I][J], 0, 0, J, int(f.sw), I, int(f.sa));
+}
+
+// the 16 products of a step, in 2 halves of 8 (blocks (i, j) with q = 4 i + j)
+template <int H>
+__device__ __forceinline__ void mx_half(f32x16_t (&acc)[4][4], const MxFrags& f) {
+  mx_mma<2 * H, 0>(acc, f);
+  mx_mma<2 * H, 1>(acc, f);
+  mx_mma<2 * H, 2>(acc, f);
+  mx_mma<2 * H, 3>(acc, f);
+  mx_mma<2 * H + 1, 0>(acc, f);
+  mx_mma<2 * H + 1, 1>(acc, f);
+  mx_mma<2 * H + 1, 2>(acc, f);
+  mx_mma<2 * H + 1, 3>(acc, f);
+}
+
+__device__ __forceinline__ void mfma_tile_mx(f32x16_t (&acc)[4][4], __amdgpu_buffer_rsrc_t rA,
+                                             __amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rS, lds_u8* smem,
+                                             uint32_t lds0, int K, int wave, int lane) {
+  const int nk = K / MX_BK;
+  // copy q (0..8) of K step kt into ring stage `stage`; steps past the end reload the last
+  auto copy = [&](int kt, int stage, int q) {
+    kt = kt < nk ? kt : nk - 1;
+    const uint32_t sbase = lds0 + uint32_t(stage) * MX_STAGE_BYTES;
+    if (q < 8) {
+      const uint32_t piece = uint32_t(4 * wave + (q & 3));
+      const uint32_t voff = piece * 1024u + uint32_t(lane) * 16u;
+      if (q < 4) copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), voff, rA, kt * MX_CODE_BYTES);
+      else copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + MX_CODE_BYTES + piece * 1024u), voff, rW,
+                       kt * MX_CODE_BYTES);
+    } else {
+      const uint32_t voff = uint32_t(wave & 1) * 256u + uint32_t(lane) * 4u;
+      copy_to_lds_b32(__builtin_amdgcn_readfirstlane(sbase + 2 * MX_CODE_BYTES + uint32_t(wave) * 256u), voff, rS,
+                      kt * 512);
+    }
+  };
+  const int wm = wave >> 1, wn = wave & 1, hk = lane >> 5;
+  uint32_t aoff[4][2], boff[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int m = wm * 128 + i * 32 + (lane & 31);
+      aoff[i][c] = uint32_t(m * 64 + (((hk + 2 * c) ^ pk_swz(m)) << 4));
+      const int n = wn * 128 + i * 32 + (lane & 31);
+      boff[i][c] = uint32_t(MX_CODE_BYTES + n * 64 + (((hk + 2 * c) ^ pk_swz(n)) << 4));
+    }
+  const uint32_t sa_off = uint32_t(2 * MX_CODE_BYTES + wm * 256 + lane * 4);
+  const uint32_t sw_off = uint32_t(2 * MX_CODE_BYTES + 512 + wn * 256 + lane * 4);
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  typedef __attribute__((address_space(3))) uint32_t lds_u32;
+  auto read_frags = [&](MxFrags& f, const lds_u8* sp) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        f.a[i][c] = *reinterpret_cast<const lds_u32x4*>(sp + aoff[i][c]);
+        f.b[i][c] = *reinterpret_cast<const lds_u32x4*>(sp + boff[i][c]);
+      }
+    f.sa = *reinterpret_cast<const lds_u32*>(sp + sa_off);
+    f.sw = *reinterpret_cast<const lds_u32*>(sp + sw_off);
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // prologue: steps 0..PK_NS-1; wait for step 0 (MX_COPIES loads per step)
+#pragma unroll
+  for (int st = 0; st < PK_NS; ++st)
+#pragma unroll
+    for (int q = 0; q < MX_COPIES; ++q) copy(st, st, q);
+  asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory");
+  MxFrags f0, f1;
+  read_frags(f0, smem);
+  // One step: `cur` holds step it (read during the previous step).  After the barrier step
+  // it+1 is visible (the MX_COPIES loads of step it+2 may be outstanding) and every wave is
+  // done reading stage(it), which then takes step it+PK_NS.
+  auto step = [&](MxFrags& cur, MxFrags& nxt, int it, int stage) {
+    const int nstage = stage + 1 == PK_NS ? 0 : stage + 1;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(nxt, smem + nstage * MX_STAGE_BYTES);
+    mx_half<0>(acc, cur);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_mma<2, 0>(acc, cur);
+    copy(it + PK_NS, stage, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_mma<2, 1>(acc, cur);
+    copy(it + PK_NS, stage, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_mma<2, 2>(acc, cur);
+    copy(it + PK_NS, stage, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_mma<2, 3>(acc, cur);
+    copy(it + PK_NS, stage, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_mma<3, 0>(acc, cur);
+    copy(it + PK_NS, stage, 4);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_mma<3, 1>(acc, cur);
+    copy(it + PK_NS, stage, 5);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_mma<3, 2>(acc, cur);
+    copy(it + PK_NS, stage, 6);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_mma<3, 3>(acc, cur);
+    copy(it + PK_NS, stage, 7);
+    copy(it + PK_NS, stage, 8);
+    __builtin_amdgcn_sched_barrier(0);
+    return nstage;
+  };
+  int stage = 0;
+  int it = 0;
+  for (; it + 1 < nk; it += 2) {
+    stage = step(f0, f1, it, stage);
+    stage = step(f1, f0, it + 1, stage);
+  }
+  if (it < nk) step(f0, f1, it, stage);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+template <int EPI>
+__global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_mx_mfma(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[PK_NS * MX_STAGE_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_g;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nMt = (M + BM - 1) / BM, nNt = (N + BN - 1) / BN;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = id / (nMt * nNt);
+  const int rem = id - g * nMt * nNt;
+  const int band = rem / (TILE_BAND * nNt);
+  const int in_band = rem - band * TILE_BAND * nNt;
+  const int bm = min(TILE_BAND, nMt - band * TILE_BAND);
+  const int nt = in_band / bm, mt = band * TILE_BAND + (in_band - (in_band / bm) * bm);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const uint32_t nk = uint32_t(K / MX_BK);
+  const uint8_t* A = static_cast<const uint8_t*>(p.A) + (size_t(g) * nMt + mt) * (size_t(nk) * MX_CODE_BYTES);
+  const uint8_t* W = static_cast<const uint8_t*>(p.W) + (size_t(g) * nNt + nt) * (size_t(nk) * MX_CODE_BYTES);
+  const uint8_t* SA = static_cast<const uint8_t*>(p.A_scale) + (size_t(g) * nMt + mt) * (size_t(nk) * 512);
+  const uint8_t* SW = static_cast<const uint8_t*>(p.W_scale) + (size_t(g) * nNt + nt) * (size_t(nk) * 512);
+  f32x16_t acc[4][4];
+  mfma_tile_mx(acc, make_rsrc(A, nk * MX_CODE_BYTES), make_rsrc(W, nk * MX_CODE_BYTES),
+               make_rsrc(wave < 2 ? SA : SW, nk * 512u), smem, lds0, K, wave, lane);
+  const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
+  tile_epilogue<EPI, 4, 4, true>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, (wave >> 1) * 128,
+                                 (wave & 1) * 128, wave, lane, g, [&](int m) { return m0 + m < M ? m0 + m : -1; });
 }
 
 // Sparse-MoE grouped GEMM.  Group g has rows group_start[g] .. group_start[g+1]-1 of the
@@ -1059,6 +1282,72 @@ bool gemm_writes_colsum(int dtype, int epi, const GemmArgs& args) {
   const GemmArgs a = normalized(args);
   return (epi == EPI_GELU_BWD || epi == EPI_RESID32) && !a.packed &&
          gemm_uses_mfma(dtype, a.M, a.N, a.K, a.lda, a.at, a.bt) && (a.sa % 8) == 0;
+}
+
+namespace {
+
+// W [G][K][N] -> W^T [G][pk_rows(N) x K] in MXFP8: one thread per (output row n, 32-value
+// block of K), n fastest so that the reads of W rows coalesce; padding rows zero.
+__global__ __launch_bounds__(256) void pack_weights_mx_kernel(const bf16_t* __restrict__ W, uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales, int G, int K, int N) {
+  const int64_t rows = pk_rows(N), nkb = K / 32;
+  const int64_t total = int64_t(G) * rows * nkb;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += int64_t(gridDim.x) * blockDim.x) {
+    const int n = int(i % rows);
+    const int64_t rest = i / rows;
+    const int kb = int(rest % nkb);
+    const int g = int(rest / nkb);
+    float v[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      v[j] = n < N ? load1(W + (size_t(g) * K + size_t(kb) * 32 + j) * N + n) : 0.f;
+      amax = fmaxf(amax, fabsf(v[j]));
+    }
+    const uint32_t sb = mx_scale_bits(amax);
+    const float inv = mx_inv_scale(sb);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] *= inv;
+    uint8_t* cg = codes + size_t(g) * size_t(rows) * K;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<uint2*>(cg + mx_off(n, kb * 32 + 16 * (c >> 1), K) + (c & 1) * 8) = e4m3_pack8(v + 8 * c);
+    scales[size_t(g) * size_t(rows) * K / 32 + mx_scale_off(n, kb, K)] = uint8_t(sb);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack_weights_mx(const void* W, void* codes, void* scales, int G, int K, int N, hipStream_t stream) {
+  if (G == 0 || N == 0) return hipSuccess;
+  if (K % MX_BK) return hipErrorInvalidValue;
+  const int64_t total = int64_t(G) * pk_rows(N) * (K / 32);
+  const int64_t want = (total + 255) / 256;
+  hipLaunchKernelGGL(pack_weights_mx_kernel, dim3(unsigned(want < 65536 ? want : 65536)), dim3(256), 0, stream,
+                     static_cast<const bf16_t*>(W), static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales), G, K,
+                     N);
+  return hipGetLastError();
+}
+
+bool gemm_mx_supported(int M, int N, int K) {
+  return M > 0 && N > 0 && K >= MX_BK && K % MX_BK == 0 && N % 32 == 0 &&
+         uint64_t(K) * MX_CODE_BYTES / MX_BK < (uint64_t(1) << 31);
+}
+
+hipError_t launch_gemm_mx(int epi, const GemmArgs& args, hipStream_t stream) {
+  if (args.G == 0 || args.M == 0 || args.N == 0) return hipSuccess;
+  if (!gemm_mx_supported(args.M, args.N, args.K)) return hipErrorInvalidValue;
+  GemmArgs a = args;  // the fp32 output of EPI_RESID is row-major [G, M, N]
+  if (a.ldc == 0) a.ldc = a.N;
+  if (a.sc == 0) a.sc = int64_t(a.M) * a.ldc;
+  const dim3 tiles(unsigned(a.G * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN)));
+  if (epi == EPI_GELU_MX)
+    hipLaunchKernelGGL((gemm_mx_mfma<EPI_GELU_MX>), tiles, dim3(MFMA_THREADS), 0, stream, a);
+  else if (epi == EPI_RESID)
+    hipLaunchKernelGGL((gemm_mx_mfma<EPI_RESID>), tiles, dim3(MFMA_THREADS), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& args, hipStream_t stream) {

@@ -34,6 +34,10 @@ struct RowsArgs {
   int B, T, D;
   float eps;
   int s_packed;  // S in the packed operand layout, token t at S + t * pk_rows(B) * D
+  // With s_packed: also S in MXFP8 (token t's codes at s8 + t * pk_rows(B) * D bytes, its
+  // scales at s8_scale + t * pk_rows(B) * D / 32 bytes), nullable
+  void* s8;
+  void* s8_scale;
 };
 
 // Largest D the row kernel's per-lane registers hold.
@@ -151,9 +155,13 @@ hipError_t launch_moe_combine(const MoeArgs& a, hipStream_t stream);
 //   Training forward:
 //   EPI_GELU_SAVE: EPI_GELU that also stores GELU'(A W + bias) in U
 //                  ([G, M, N], dtype, C's layout; row-major operands only)
+//   MXFP8 products (launch_gemm_mx; A, W and their scales in the MXFP8 layout):
+//   EPI_GELU_MX: C = GELU(A W + bias) quantized to MXFP8 along N: codes in C, scales in
+//                C_scale ([G][pk_rows(M) x N], the A operand of the second product)
+//   EPI_RESID as above (R in the packed bf16 layout).
 enum Epilogue {
   EPI_GELU = 0, EPI_RESID = 1, EPI_MOE1 = 2, EPI_MOE2 = 3, EPI_BIAS = 4,
-  EPI_GELU_BWD = 5, EPI_RESID32 = 6, EPI_STORE32 = 7, EPI_GELU_SAVE = 8
+  EPI_GELU_BWD = 5, EPI_RESID32 = 6, EPI_STORE32 = 7, EPI_GELU_SAVE = 8, EPI_GELU_MX = 9
 };
 
 struct GemmArgs {
@@ -180,6 +188,9 @@ struct GemmArgs {
   //   bt: W is [G][N][K], element (k, n) at W + g * N * K + n * K + k
   int at, bt;
   void* U;         // EPI_GELU_SAVE: GELU' at the pre-activations
+  const void* A_scale;  // MXFP8 products: scales of A, of W (per group [pk_rows x K / 32]),
+  const void* W_scale;  // and of C (EPI_GELU_MX)
+  void* C_scale;
   float* colsum;   // EPI_GELU_BWD, EPI_RESID32: per-wave column sums, nullable
 };
 // Rows of the per-wave column sums of one group: two per 256-row tile.
@@ -197,6 +208,15 @@ hipError_t gemm_init();
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t stream);
 // True when launch_gemm(dtype, epi, a) runs a matrix-core kernel that writes a.colsum.
 bool gemm_writes_colsum(int dtype, int epi, const GemmArgs& a);
+// MXFP8 products on the matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4): A [G][pk_rows(M)
+// x K] and W^T [G][pk_rows(N) x K] in the MXFP8 layout (codes in A / W, scales in A_scale /
+// W_scale); K % 64 == 0, N % 32 == 0; epi EPI_GELU_MX or EPI_RESID.
+bool gemm_mx_supported(int M, int N, int K);
+hipError_t launch_gemm_mx(int epi, const GemmArgs& a, hipStream_t stream);
+// W [G][K][N] (bf16, row-major) -> W^T [G][pk_rows(N) x K] in MXFP8 (codes to `codes`,
+// scales to `scales`, padding rows zero); K % 64 == 0.
+hipError_t launch_pack_weights_mx(const void* W, void* codes, void* scales, int G, int K, int N,
+                                  hipStream_t stream);
 // W [G][K][N] (bf16, row-major) -> W^T [G][pk_rows(N) x K] in the packed operand layout
 // (padding rows zero); K % 32 == 0.
 hipError_t launch_pack_weights(const void* W, void* out, int G, int K, int N, hipStream_t stream);

@@ -153,6 +153,33 @@ __global__ __launch_bounds__(64 * rows_max_waves(NC, MODE)) void rows_kernel(Row
           const int c = lane + 64 * i;
           if (c < nchunks) storew<W>(dst + pk_off(b, c * W, D), r[i]);
         }
+        if (a.s8) {
+          // S in MXFP8 along D: the 32 columns of a scale block are the chunks of 4
+          // neighbouring lanes (shuffles run on every lane; D % 64 == 0 keeps such a group
+          // wholly inside or outside the row)
+          uint8_t* codes = static_cast<uint8_t*>(a.s8) + size_t(h) * size_t(pk_rows(B)) * D;
+          uint8_t* scales = static_cast<uint8_t*>(a.s8_scale) + size_t(h) * size_t(pk_rows(B)) * D / 32;
+#pragma unroll
+          for (int i = 0; i < NC; ++i) {
+            const int c = lane + 64 * i;
+            float amax = 0.f;
+            if (c < nchunks)
+#pragma unroll
+              for (int e = 0; e < W; ++e) amax = fmaxf(amax, fabsf(r[i][e]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+            const uint32_t sb = mx_scale_bits(amax);
+            const float inv = mx_inv_scale(sb);
+            if (c < nchunks) {
+              float v[W];
+#pragma unroll
+              for (int e = 0; e < W; ++e) v[e] = r[i][e] * inv;
+              const int col = c * W;
+              *reinterpret_cast<uint2*>(codes + mx_off(b, col, D) + ((col >> 3) & 1) * 8) = e4m3_pack8(v);
+              if ((lane & 3) == 0) scales[mx_scale_off(b, col >> 5, D)] = uint8_t(sb);
+            }
+          }
+        }
         continue;
       }
     }

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "rmx.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(rmx_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(rmx_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_and_binding_agree():
@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = rmx.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.rmx_abi_version() == 3
+    assert lib.rmx_abi_version() == 4
 
 
 def test_status_strings_and_kernel_names():
@@ -111,3 +111,16 @@ def test_grads_struct_matches_header():
     body = re.search(r"typedef struct \{([^}]*)\} rmx_grads;", src).group(1)
     fields = re.findall(r"float\*\s+(\w+);", body)
     assert fields == [f for f, _ in binding.rmx_grads._fields_]
+
+
+def test_mxfp8_host_side():
+    lib = rmx.load_library()
+    assert lib.rmx_packed_weights_mxfp8_bytes(None) == 0
+    assert lib.rmx_pack_weights_mxfp8(None, None, 1, None, 0, None) == binding.RMX_ERR_INVALID_ARG
+
+
+def test_weights_struct_matches_header():
+    src = open(os.path.join(ROOT, "include", "rmx.h")).read()
+    body = re.search(r"typedef struct \{([^}]*)\} rmx_weights;", src).group(1)
+    fields = re.findall(r"const void\*\s+(\w+);", body)
+    assert fields == list(binding.WEIGHT_NAMES)
