@@ -51,6 +51,24 @@ def _linear(x, W, bias):
     return y
 
 
+def _attn(x, Wq, Wk, Wv):
+    """Single-head self-attention of one sample x[T][D], scalar loops, softmax along keys."""
+    T = len(x)
+    zero = [0.0] * len(Wq[0])
+    q = [_linear(x[t], Wq, zero) for t in range(T)]
+    k = [_linear(x[t], Wk, zero) for t in range(T)]
+    v = [_linear(x[t], Wv, [0.0] * len(Wv[0])) for t in range(T)]
+    da = len(Wq[0])
+    out = []
+    for t in range(T):
+        sc = [sum(q[t][i] * k[j][i] for i in range(da)) / math.sqrt(da) for j in range(T)]
+        mx = max(sc)
+        ex = [math.exp(c - mx) for c in sc]
+        z = sum(ex)
+        out.append([sum(ex[j] / z * v[j][c] for j in range(T)) for c in range(len(v[0]))])
+    return out
+
+
 def _tolist(a):
     return a.tolist() if hasattr(a, "tolist") else a
 
@@ -62,7 +80,7 @@ def forward_sample(x, layers, eps=1e-5):
     gates_all = []
     for p in layers:
         p = {key: _tolist(v) for key, v in p.items()}
-        m = _mix(x, T, D)
+        m = _attn(x, p["Wq"], p["Wk"], p["Wv"]) if "Wq" in p else _mix(x, T, D)
         s = [_ln_row([m[t][j] + x[t][j] for j in range(D)], p["ln1_g"], p["ln1_b"], eps)
              for t in range(T)]
         v = []

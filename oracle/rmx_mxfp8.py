@@ -7,8 +7,9 @@ large products and halving the operand width doubles the hardware peak ("RankMix
 translation, section 4.6, eq (13) and its quantization item: fp16 inference).  On a part
 whose bf16 and fp16 peaks are equal, the same step is 8-bit operands: the variant here
 quantizes the operands of the two per-token products to MXFP8 as the OCP Microscaling
-Formats (MX) Specification v1.0 defines it (a published format, not the pages'): every block of 32 consecutive values along
-the reduction axis shares one power-of-two scale X = 2^(floor(log2(amax)) - 8), 8 being the
+Formats (MX) Specification v1.0 defines it (a published format, not the pages'): every
+block of 32 consecutive values along the reduction axis shares one power-of-two scale
+X = 2^(floor(log2(amax)) - 8), 8 being the
 largest exponent of the FP8 E4M3 element format, and each value is stored as the E4M3 number
 nearest to v / X (round to nearest, ties to even; E4M3 has 3 mantissa bits, exponent bias 7,
 subnormals below 2^-6 in steps of 2^-9, largest finite 448; values beyond saturate to

@@ -25,6 +25,9 @@ Readings taken where the pages leave a step open (each is listed in the design doc):
   * Sparse-MoE: gate g = ReLU(s W_g) with no bias and no renormalisation, an expert
     is a Linear-GELU-Linear of the eq (6)-(7) form, V = sum_e g_e * expert_e(s)
     summed in expert order ([paper] 3.4 eq (10)).
+  * Self-attention routing (the comparator of [paper] 4.4, written out in [exp1] 3.4): one
+    head, Q/K/V projections D x D shared by the T tokens, no output projection, scores
+    scaled by 1 / sqrt(D); its output takes the place of TokenMixing(X) in the block.
   * Tokenisation: token i projects its own slice of the concatenated embedding with
     its own linear layer ([uni] eq (9) makes the layer token-specific; [paper] 3.2
     eq (2) and [exp1] 2 leave the sharing open), in the row-vector convention of the
@@ -40,7 +43,7 @@ import numpy as np
 from scipy.special import erf
 
 __all__ = ["tokenize", "token_mix", "layer_norm", "gelu", "pffn", "moe_gates", "moe_pffn",
-           "block", "forward"]
+           "self_attention", "block", "forward"]
 
 
 def _f64(a) -> np.ndarray:
@@ -149,13 +152,31 @@ def moe_pffn(S: np.ndarray, Wg, We1, be1, We2, be2):
     return V, G
 
 
+def self_attention(X: np.ndarray, Wq, Wk, Wv) -> np.ndarray:
+    """Single-head self-attention over the T tokens of each sample ([exp1] 3.4):
+    Q = X Wq, K = X Wk, V = X Wv, out = softmax(Q K^T / sqrt(d_a)) V with the softmax along
+    each row (over the keys).  X[..., T, D]; Wq, Wk of shape D x d_a, Wv of shape D x D
+    (the output replaces TokenMixing(X), so it keeps width D)."""
+    X = _f64(X)
+    Q, K, V = X @ _f64(Wq), X @ _f64(Wk), X @ _f64(Wv)
+    scores = Q @ np.swapaxes(K, -1, -2) / np.sqrt(Q.shape[-1])
+    scores = scores - scores.max(axis=-1, keepdims=True)
+    P = np.exp(scores)
+    P /= P.sum(axis=-1, keepdims=True)
+    return P @ V
+
+
 def block(X: np.ndarray, p: dict, eps: float):
     """One RankMixer block ([paper] 3.1 eq (1), 3.3.1 eq (5)):
         S = LN1(TokenMixing(X) + X),   X' = LN2(PFFN(S) + S).
     p holds W1, b1, W2, b2, ln1_g, ln1_b, ln2_g, ln2_b (and Wg, We1, be1, We2, be2 for
-    the Sparse-MoE variant).  Returns (X', G) with G the MoE gates or None."""
+    the Sparse-MoE variant).  With Wq, Wk, Wv in p the block is the routing comparator of
+    [paper] 4.4 (self-attention between the tokens instead of Token Mixing):
+        S = LN1(SelfAttention(X) + X).
+    Returns (X', G) with G the MoE gates or None."""
     X = _f64(X)
-    S = layer_norm(token_mix(X) + X, p["ln1_g"], p["ln1_b"], eps)
+    routed = self_attention(X, p["Wq"], p["Wk"], p["Wv"]) if "Wq" in p else token_mix(X)
+    S = layer_norm(routed + X, p["ln1_g"], p["ln1_b"], eps)
     if "Wg" in p:
         V, G = moe_pffn(S, p["Wg"], p["We1"], p["be1"], p["We2"], p["be2"])
     else:
