@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--sweep", action="store_true", help="one line per serving batch size")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-samples", type=int, default=384)
+    p.add_argument("--routing-comparison", action="store_true",
+                   help="Token Mixing versus the self-attention comparator at the 100M and 1B shapes")
     p.add_argument("--mxfp8", action="store_true",
                    help="the MXFP8 inference variant (weights prepared with rmx_pack_weights_mxfp8)")
     p.add_argument("--backward", action="store_true",
@@ -105,7 +107,7 @@ def moe_active_flops(h, X, w, cfg, B):
     return flops, active / gates.numel()
 
 
-def time_forward(cfg, B, steps, warmup, calibrate_copy=False, mxfp8=False):
+def time_forward(cfg, B, steps, warmup, calibrate_copy=False, mxfp8=False, prepare=True):
     import torch
     import rankmixer_block_forward_amd as rmx
     from rankmixer_block_forward_amd import synth
@@ -121,7 +123,7 @@ def time_forward(cfg, B, steps, warmup, calibrate_copy=False, mxfp8=False):
         # weights quantized once to MXFP8 (model-load work, outside the timed region)
         w["packed_mxfp8"] = h.pack_weights_mxfp8(w)
         torch.cuda.synchronize()
-    elif h.packed_weights_bytes() > 0:
+    elif prepare and h.packed_weights_bytes() > 0:
         # weights prepared once for the matrix cores (model-load work, outside the timed region)
         w["packed"] = h.pack_weights(w)
         torch.cuda.synchronize()
@@ -376,6 +378,39 @@ def bench_backward(cfg, B, steps, warmup, cpu_samples):
     print(json.dumps(line), flush=True)
 
 
+def bench_routing(steps, warmup):
+    """The pages' routing ablation on this harness: the same blocks with Token Mixing and with
+    the self-attention comparator, both on the row-major weights (the comparator has no
+    prepared-weights path), at the 100M shape (where the pages ran it) and the 1B shape."""
+    from rankmixer_block_forward_amd import synth
+    for mix in (synth.M100, synth.B1):
+        att = mix.with_(name=mix.name + "-attention", routing="attention")
+        T, D, k, L = mix.T, mix.D, mix.k, mix.L
+        t_mix, prof_mix, _ = time_forward(mix, mix.B, steps, warmup, prepare=False)
+        t_att, prof_att, _ = time_forward(att, mix.B, steps, warmup, prepare=False)
+        f_mix = 4.0 * k * L * T * D * D                          # per sample
+        f_att = f_mix + L * (6.0 * T * D * D + 4.0 * T * T * D)  # + Q, K, V and the scores / sum
+        p_mix = L * 2.0 * T * D * k * D                          # per-token FFN weights
+        p_att = p_mix + L * 3.0 * D * D
+        ms_mix, ms_att = t_mix / steps * 1e3, t_att / steps * 1e3
+        print(json.dumps({
+            "metric": "routing comparison: Token Mixing vs self-attention, samples/s of each",
+            "value": round(mix.B / (ms_att / 1e3), 1), "unit": "samples/s (attention routing)", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "higher_is_better": True, "vs_baseline": None, "dtype": mix.dtype,
+            "data": "synthetic (seeded Gaussian inputs and random-init weights)",
+            "config": {"workload": mix.name + "-routing", "B": mix.B, "T": T, "D": D, "k": k, "L": L},
+            "mix": {"samples_per_s": round(mix.B / (ms_mix / 1e3), 1), "ms_per_step": round(ms_mix, 4),
+                    "flops_per_sample": f_mix, "ffn_params": p_mix,
+                    "kernels_ms_per_step": {n: round(v["total_ms"] / steps, 4) for n, v in prof_mix.items()
+                                            if n != "_dropped"}},
+            "attention": {"samples_per_s": round(mix.B / (ms_att / 1e3), 1), "ms_per_step": round(ms_att, 4),
+                          "flops_per_sample": f_att, "params": p_att,
+                          "kernels_ms_per_step": {n: round(v["total_ms"] / steps, 4) for n, v in prof_att.items()
+                                                  if n != "_dropped"}},
+            "flops_ratio": round(f_att / f_mix, 4), "param_ratio": round(p_att / p_mix, 4),
+            "time_ratio": round(ms_att / ms_mix, 4)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -393,6 +428,9 @@ def main():
         return
     from rankmixer_block_forward_amd import synth
     cfg = synth.CONFIGS[args.workload]
+    if args.routing_comparison:
+        bench_routing(args.steps, args.warmup)
+        return
     if args.backward:
         bench_backward(cfg, args.batch or cfg.B, args.steps, args.warmup,
                        0 if args.no_cpu_baseline else args.cpu_samples)

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RMX_ABI_VERSION 4
+#define RMX_ABI_VERSION 5
 
 typedef struct rmx_handle rmx_handle; /* opaque, owned by the library */
 
@@ -56,6 +56,12 @@ typedef enum {
 
 typedef enum { RMX_FP32 = 0, RMX_BF16 = 1 } rmx_dtype;
 
+/* How the tokens of a sample exchange information before LN1. */
+typedef enum {
+  RMX_ROUTING_MIX = 0,       /* Token Mixing (the RankMixer block) */
+  RMX_ROUTING_ATTENTION = 1  /* self-attention between the tokens: the comparator of the pages' routing ablation */
+} rmx_routing;
+
 /* Model configuration, fixed for the life of a handle.
  *   T, D     tokens per sample and width; H = T always, D % T == 0 required
  *            (paper section 3.3.1: H = T keeps the token count for the residual).
@@ -67,6 +73,13 @@ typedef enum { RMX_FP32 = 0, RMX_BF16 = 1 } rmx_dtype;
  *   max_batch  largest B a forward call may pass; the workspace is sized for it.
  *   moe_experts  0 = dense per-token FFN; E > 0 = Sparse-MoE PFFN with E experts per
  *            token (paper section 3.4 eq (10)); moe_hidden = hidden width of one expert.
+ *   routing  rmx_routing.  RMX_ROUTING_ATTENTION replaces TokenMixing(X) in every block by
+ *            single-head self-attention between the sample's tokens,
+ *            softmax(Q K^T / sqrt(D)) V with Q = X Wq, K = X Wk, V = X Wv (D x D projections
+ *            shared by the tokens, no output projection): the comparator of the paper's
+ *            routing ablation (section 4.4; attention as "RankMixer 详解（1）" section 3.4
+ *            writes it).  Dense handles with T <= 64; forward only (no prepared weights,
+ *            no training).
  * Limits: dtype BF16 needs D % 8 == 0 and (D/T) % 8 == 0, dtype FP32 needs nothing
  * more; D <= 4096; T*D*sizeof(dtype) <= 96 KiB (one sample must fit the on-chip LDS
  * of one workgroup).  Beyond a limit rmx_create returns RMX_ERR_UNSUPPORTED. */
@@ -80,6 +93,7 @@ typedef struct {
   int64_t max_batch;
   int32_t moe_experts;
   int32_t moe_hidden;
+  int32_t routing;    /* rmx_routing */
 } rmx_config;
 
 /* Device pointers to the parameters of all L blocks, each stacked over L, in the
@@ -96,7 +110,9 @@ typedef struct {
  *   the weights from it (W1 and W2 are then unused and may be NULL); the result is the
  *   same bit for bit.
  * packed_mxfp8: NULL, or W1 and W2 of all blocks prepared by rmx_pack_weights_mxfp8; when
- *   set (and packed is NULL) the forward runs the MXFP8 inference variant (see there).   */
+ *   set (and packed is NULL) the forward runs the MXFP8 inference variant (see there).
+ * Wq, Wk, Wv [L, D, D]: the self-attention projections of RMX_ROUTING_ATTENTION handles
+ *   (row-vector convention x W), else NULL.                                               */
 typedef struct {
   const void* W1;
   const void* b1;
@@ -113,6 +129,9 @@ typedef struct {
   const void* be2;
   const void* packed;
   const void* packed_mxfp8;
+  const void* Wq;
+  const void* Wk;
+  const void* Wv;
 } rmx_weights;
 
 /* Validates cfg, checks that the current HIP device is gfx950, and allocates the
@@ -256,7 +275,9 @@ typedef enum {
   RMX_KERNEL_BWD_DW1 = 11, /* backward: per-token S^T gU -> dW1 */
   RMX_KERNEL_BWD_DW2 = 12, /* backward: per-token H^T gY -> dW2 */
   RMX_KERNEL_BWD_SUMS = 13, /* backward: batch sums of the bias and LayerNorm gradients */
-  RMX_KERNEL_COUNT = 14
+  RMX_KERNEL_ATTN_QKV = 14, /* attention routing: the Q, K, V projections */
+  RMX_KERNEL_ATTN = 15,     /* attention routing: softmax(Q K^T / sqrt(D)) V + X, LN1 */
+  RMX_KERNEL_COUNT = 16
 } rmx_kernel_kind;
 
 rmx_status rmx_profile_enable(rmx_handle* h, int32_t enable);

@@ -9,9 +9,8 @@ whose bf16 and fp16 peaks are equal, the same step is 8-bit operands: the varian
 quantizes the operands of the two per-token products to MXFP8 as the OCP Microscaling
 Formats (MX) Specification v1.0 defines it (a published format, not the pages'): every
 block of 32 consecutive values along the reduction axis shares one power-of-two scale
-X = 2^(floor(log2(amax)) - 8), 8 being the
-largest exponent of the FP8 E4M3 element format, and each value is stored as the E4M3 number
-nearest to v / X (round to nearest, ties to even; E4M3 has 3 mantissa bits, exponent bias 7,
+X = 2^(floor(log2(amax)) - 8), 8 being the largest exponent of the FP8 E4M3 element format,
+and each value is stored as the E4M3 number nearest to v / X (round to nearest, ties to even; E4M3 has 3 mantissa bits, exponent bias 7,
 subnormals below 2^-6 in steps of 2^-9, largest finite 448; values beyond saturate to
 +-448).  Where the quantization sits (a reading; the pages say nothing about it):
   * S, the LN1 output, along D (the K of the first product) for each (sample, token) row;

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(PKG, "librmx.so")
 
 RMX_OK, RMX_ERR_INVALID_ARG, RMX_ERR_UNSUPPORTED, RMX_ERR_OUT_OF_MEMORY, RMX_ERR_HIP = range(5)
 RMX_FP32, RMX_BF16 = 0, 1
-KERNEL_COUNT = 14
+RMX_ROUTING_MIX, RMX_ROUTING_ATTENTION = 0, 1
+KERNEL_COUNT = 16
 
 # Every symbol include/rmx.h declares.
 EXPORTS = (
@@ -39,11 +40,11 @@ class rmx_config(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("D", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("L", ctypes.c_int32), ("dtype", ctypes.c_int32), ("ln_eps", ctypes.c_float),
                 ("max_batch", ctypes.c_int64), ("moe_experts", ctypes.c_int32),
-                ("moe_hidden", ctypes.c_int32)]
+                ("moe_hidden", ctypes.c_int32), ("routing", ctypes.c_int32)]
 
 
 WEIGHT_NAMES = ("W1", "b1", "W2", "b2", "ln1_g", "ln1_b", "ln2_g", "ln2_b",
-                "Wg", "We1", "be1", "We2", "be2", "packed", "packed_mxfp8")
+                "Wg", "We1", "be1", "We2", "be2", "packed", "packed_mxfp8", "Wq", "Wk", "Wv")
 
 
 class rmx_weights(ctypes.Structure):
@@ -154,9 +155,12 @@ class Handle:
     """One rmx_handle: a model configuration and its workspace on the current device."""
 
     def __init__(self, T: int, D: int, k: int, L: int, dtype="bf16", ln_eps: float = 1e-5,
-                 max_batch: int = 2048, moe_experts: int = 0, moe_hidden: int = 0):
+                 max_batch: int = 2048, moe_experts: int = 0, moe_hidden: int = 0, routing: str = "mix"):
         self._lib = load_library()
-        self.cfg = rmx_config(T, D, k, L, _dtype_code(dtype), ln_eps, max_batch, moe_experts, moe_hidden)
+        if routing not in ("mix", "attention"):
+            raise ValueError(f"unknown routing {routing!r}")
+        code = RMX_ROUTING_ATTENTION if routing == "attention" else RMX_ROUTING_MIX
+        self.cfg = rmx_config(T, D, k, L, _dtype_code(dtype), ln_eps, max_batch, moe_experts, moe_hidden, code)
         self.dtype = _torch_dtype(self.cfg.dtype)
         h = ctypes.c_void_p()
         _check(self._lib.rmx_create(ctypes.byref(self.cfg), ctypes.byref(h)))
@@ -166,7 +170,7 @@ class Handle:
     def for_config(cls, cfg, max_batch: int | None = None) -> "Handle":
         """Handle for a synth.Config workload."""
         return cls(cfg.T, cfg.D, cfg.k, cfg.L, cfg.dtype, cfg.eps,
-                   cfg.B if max_batch is None else max_batch, cfg.E, cfg.moe_hidden)
+                   cfg.B if max_batch is None else max_batch, cfg.E, cfg.moe_hidden, cfg.routing)
 
     def close(self):
         if getattr(self, "_h", None):
@@ -365,5 +369,7 @@ def upload(inputs, device="cuda"):
 
     w = {n: dev(getattr(inputs, n)) for n in ("W1", "b1", "W2", "b2", "ln1_g", "ln1_b", "ln2_g", "ln2_b")}
     for n, a in inputs.moe.items():
+        w[n] = dev(a)
+    for n, a in inputs.attn.items():
         w[n] = dev(a)
     return dev(inputs.X), w

@@ -65,6 +65,14 @@ struct rmx_handle {
   int* moe_pos = nullptr;        // [G, max_batch]
   void* moe_hidden = nullptr;    // [R, h]  bf16
   float* moe_out = nullptr;      // [R, D]  fp32
+  // Self-attention routing (routing == RMX_ROUTING_ATTENTION): Q, K, V and the block input
+  // of blocks 2..L, each [max_batch, T, D] dtype, and a scratch for the unused pool of the
+  // launch that forms that input
+  void* aQ = nullptr;
+  void* aK = nullptr;
+  void* aV = nullptr;
+  void* aX = nullptr;
+  float* a_pool = nullptr;       // [max_batch, D]
   // Backward workspace, allocated by the first backward call (all for max_batch samples)
   bool bwd_ready = false;
   float* bw_gY32 = nullptr;      // [T, max_batch, D]  fp32  gradient of the pre-LN2 rows
@@ -184,6 +192,17 @@ rmx_status validate_config(const rmx_config* c) {
         !gemm_moe_supported(c->D, h, c->max_batch))
       return fail(nullptr, RMX_ERR_UNSUPPORTED, "MoE GEMMs need D %% 32 == 0, moe_hidden %% 32 == 0 and slices < 2 GiB");
   }
+  if (c->routing != RMX_ROUTING_MIX && c->routing != RMX_ROUTING_ATTENTION)
+    return fail(nullptr, RMX_ERR_INVALID_ARG, "unknown routing %d", c->routing);
+  if (c->routing == RMX_ROUTING_ATTENTION) {
+    if (c->moe_experts > 0)
+      return fail(nullptr, RMX_ERR_UNSUPPORTED, "attention routing is built for the dense per-token FFN");
+    if (int64_t(c->T) * c->max_batch >= (int64_t(1) << 31))
+      return fail(nullptr, RMX_ERR_UNSUPPORTED, "attention routing needs T * max_batch < 2^31");
+    if (!attn_supported(c->dtype, c->T, c->D))
+      return fail(nullptr, RMX_ERR_UNSUPPORTED, "attention routing needs T <= %d and D <= %d", ATTN_MAX_T,
+                  ATTN_MAX_D);
+  }
   const bool vec = rows_vectorized(c->T, c->D);
   if (c->dtype == RMX_BF16 && !vec)
     return fail(nullptr, RMX_ERR_UNSUPPORTED, "bf16 needs D %% 8 == 0 and (D/T) %% 8 == 0");
@@ -258,6 +277,14 @@ hipError_t run_gemm_mx(rmx_handle* h, hipStream_t s, int epi, const GemmArgs& a)
   ProfPair pp;
   prof_begin(h, s, &pp, epi == EPI_GELU_MX ? RMX_KERNEL_GEMM1 : RMX_KERNEL_GEMM2);
   hipError_t e = launch_gemm_mx(epi, a, s);
+  prof_end(h, s, &pp);
+  return e;
+}
+
+hipError_t run_attn(rmx_handle* h, hipStream_t s, const AttnArgs& a) {
+  ProfPair pp;
+  prof_begin(h, s, &pp, RMX_KERNEL_ATTN);
+  hipError_t e = launch_attn_rows(h->cfg.dtype, a, s);
   prof_end(h, s, &pp);
   return e;
 }
@@ -344,7 +371,8 @@ const char* rmx_kernel_name(int32_t kind) {
                                                 "rows_ln2_pool",    "moe_gate",     "moe_ffn1",
                                                 "moe_ffn2",         "moe_combine",  "bwd_rows",
                                                 "bwd_gemm_dU",      "bwd_gemm_dS",  "bwd_gemm_dW1",
-                                                "bwd_gemm_dW2",     "bwd_sums"};
+                                                "bwd_gemm_dW2",     "bwd_sums",     "attn_qkv",
+                                                "attn_rows"};
   return (kind >= 0 && kind < RMX_KERNEL_COUNT) ? names[kind] : "unknown";
 }
 
@@ -389,6 +417,13 @@ rmx_status rmx_create(const rmx_config* cfg, rmx_handle** out_handle) {
   if (rows > 0) {
     alloc(&h->S, prow * cfg->D * esz);
     if (h->mx_capable) alloc(&h->S8, prow * cfg->D + prow * cfg->D / 32);
+    if (cfg->routing == RMX_ROUTING_ATTENTION) {
+      alloc(&h->aQ, nS * esz);
+      alloc(&h->aK, nS * esz);
+      alloc(&h->aV, nS * esz);
+      alloc(&h->aX, nS * esz);
+      alloc(&h->a_pool, size_t(cfg->max_batch) * cfg->D * sizeof(float));
+    }
     alloc(&h->Y, nS * sizeof(float));
     if (cfg->moe_experts == 0) {
       alloc(&h->H, prow * size_t(cfg->k) * cfg->D * esz);
@@ -447,6 +482,11 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
                 (long long)c.max_batch);
   const bool moe = c.moe_experts > 0;
   const bool train = saved != nullptr;
+  const bool attn = c.routing == RMX_ROUTING_ATTENTION;
+  if (attn && (train || w->packed || w->packed_mxfp8))
+    return fail(h, RMX_ERR_UNSUPPORTED, "attention routing runs the forward on W1 and W2 only");
+  if (!attn && (w->Wq || w->Wk || w->Wv))
+    return fail(h, RMX_ERR_INVALID_ARG, "Wq / Wk / Wv given to a Token Mixing handle");
   if (gate_out && !moe) return fail(h, RMX_ERR_INVALID_ARG, "gate_out must be NULL for a dense handle");
   if (train && moe) return fail(h, RMX_ERR_UNSUPPORTED, "training needs a dense handle");
   if (train && w->packed) return fail(h, RMX_ERR_INVALID_ARG, "training reads W1 and W2: packed must be NULL");
@@ -500,6 +540,11 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
   if ((st = check_dev(h, w->ln1_b, Ls * D * esz, dev, "ln1_b")) != RMX_OK) return st;
   if ((st = check_dev(h, w->ln2_g, Ls * D * esz, dev, "ln2_g")) != RMX_OK) return st;
   if ((st = check_dev(h, w->ln2_b, Ls * D * esz, dev, "ln2_b")) != RMX_OK) return st;
+  if (attn) {
+    if ((st = check_dev(h, w->Wq, Ls * D * D * esz, dev, "Wq")) != RMX_OK) return st;
+    if ((st = check_dev(h, w->Wk, Ls * D * D * esz, dev, "Wk")) != RMX_OK) return st;
+    if ((st = check_dev(h, w->Wv, Ls * D * D * esz, dev, "Wv")) != RMX_OK) return st;
+  }
   // The outputs must not overlap the inputs: out and xl_out are written while X is read.
   auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -542,24 +587,71 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
   char* S8 = static_cast<char*>(h->S8);
   char* H8 = static_cast<char*>(h->H);
   for (int n = 0; n < c.L && e == hipSuccess; ++n) {
-    RowsArgs ra{};
-    ra.in = n == 0 ? X : static_cast<const void*>(Y_of(n - 1));
-    ra.ln2_g = n == 0 ? nullptr : at(w->ln2_g, size_t(n - 1) * D);
-    ra.ln2_b = n == 0 ? nullptr : at(w->ln2_b, size_t(n - 1) * D);
-    ra.ln1_g = at(w->ln1_g, size_t(n) * D);
-    ra.ln1_b = at(w->ln1_b, size_t(n) * D);
-    ra.S = S_of(n);
-    ra.B = Bi;
-    ra.T = c.T;
-    ra.D = c.D;
-    ra.eps = c.ln_eps;
-    ra.s_packed = (pk || mx) ? 1 : 0;
-    if (mx) {
-      ra.s8 = S8;
-      ra.s8_scale = S8 + T * pkB * D;
+    if (attn) {
+      // block input: X, or LN2 of the previous block written out by the pooling row launch
+      const void* Xn = X;
+      if (n > 0) {
+        RowsArgs ra{};
+        ra.in = Y_of(n - 1);
+        ra.ln2_g = at(w->ln2_g, size_t(n - 1) * D);
+        ra.ln2_b = at(w->ln2_b, size_t(n - 1) * D);
+        ra.pool = h->a_pool;
+        ra.xl = h->aX;
+        ra.B = Bi;
+        ra.T = c.T;
+        ra.D = c.D;
+        ra.eps = c.ln_eps;
+        if ((e = run_rows(h, s, ROWS_FINAL, ra)) != hipSuccess) break;
+        Xn = h->aX;
+      }
+      // Q, K, V over the B*T rows, one product each (no bias)
+      void* qkv[3] = {h->aQ, h->aK, h->aV};
+      const void* wqkv[3] = {w->Wq, w->Wk, w->Wv};
+      for (int m = 0; m < 3 && e == hipSuccess; ++m) {
+        GemmArgs pa{};
+        pa.A = Xn;
+        pa.W = at(wqkv[m], size_t(n) * D * D);
+        pa.C = qkv[m];
+        pa.G = 1;
+        pa.M = Bi * c.T;
+        pa.N = c.D;
+        pa.K = c.D;
+        e = run_gemm(h, s, EPI_BIAS, pa, RMX_KERNEL_ATTN_QKV);
+      }
+      if (e != hipSuccess) break;
+      AttnArgs aa{};
+      aa.Q = h->aQ;
+      aa.K = h->aK;
+      aa.V = h->aV;
+      aa.X = Xn;
+      aa.ln1_g = at(w->ln1_g, size_t(n) * D);
+      aa.ln1_b = at(w->ln1_b, size_t(n) * D);
+      aa.S = h->S;
+      aa.B = Bi;
+      aa.T = c.T;
+      aa.D = c.D;
+      aa.eps = c.ln_eps;
+      if ((e = run_attn(h, s, aa)) != hipSuccess) break;
+    } else {
+      RowsArgs ra{};
+      ra.in = n == 0 ? X : static_cast<const void*>(Y_of(n - 1));
+      ra.ln2_g = n == 0 ? nullptr : at(w->ln2_g, size_t(n - 1) * D);
+      ra.ln2_b = n == 0 ? nullptr : at(w->ln2_b, size_t(n - 1) * D);
+      ra.ln1_g = at(w->ln1_g, size_t(n) * D);
+      ra.ln1_b = at(w->ln1_b, size_t(n) * D);
+      ra.S = S_of(n);
+      ra.B = Bi;
+      ra.T = c.T;
+      ra.D = c.D;
+      ra.eps = c.ln_eps;
+      ra.s_packed = (pk || mx) ? 1 : 0;
+      if (mx) {
+        ra.s8 = S8;
+        ra.s8_scale = S8 + T * pkB * D;
+      }
+      e = run_rows(h, s, n == 0 ? ROWS_FIRST : ROWS_MID, ra);
+      if (e != hipSuccess) break;
     }
-    e = run_rows(h, s, n == 0 ? ROWS_FIRST : ROWS_MID, ra);
-    if (e != hipSuccess) break;
 
     if (moe) {
       // Sparse-MoE PFFN: route, expert FFN1 over gathered rows, gate-scaled FFN2, combine.

@@ -101,6 +101,25 @@ inline size_t colsum_scratch_floats(int64_t G, int64_t R, int64_t N) {
 hipError_t launch_colsum(int dtype, const void* in, float* out, float* scratch, int G, int R, int N,
                          hipStream_t stream);
 
+// ---------------------------------------------------------------- self-attention routing
+// The routing comparator: S = LN1(softmax(Q K^T / sqrt(D)) V + X) per sample, one
+// workgroup per sample.  Q, K, V, X [B, T, D] (dtype, sample-major); S [T, B, D] (dtype).
+struct AttnArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* X;
+  const void* ln1_g;
+  const void* ln1_b;
+  void* S;
+  int B, T, D;
+  float eps;
+};
+constexpr int ATTN_MAX_T = 64;     // one key per lane in the softmax
+constexpr int ATTN_MAX_D = 2048;   // vectorized path (D % 8 == 0, (D / T) % 8 == 0)
+bool attn_supported(int dtype, int T, int D);
+hipError_t launch_attn_rows(int dtype, const AttnArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- Sparse-MoE routing
 // Group gi = t * E + e.  Rows of a group are listed in ascending sample order.
 constexpr int MOE_MAX_E = 16;

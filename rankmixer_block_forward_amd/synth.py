@@ -31,6 +31,7 @@ KIND_G1, KIND_BE1, KIND_G2, KIND_BE2 = 20, 21, 22, 23
 KIND_WG, KIND_WE1, KIND_BEXP1, KIND_WE2, KIND_BEXP2 = 30, 31, 32, 33, 34
 KIND_E, KIND_WP, KIND_BP = 40, 41, 42
 KIND_GOUT = 50
+KIND_WQ, KIND_WK, KIND_WV = 60, 61, 62
 
 X_BLOCK = 64
 
@@ -51,6 +52,7 @@ class Config:
     E: int = 0                   # Sparse-MoE experts per token (0 = dense per-token FFN)
     moe_hidden: int = 0          # hidden width of one expert
     eps: float = 1e-5
+    routing: str = "mix"         # "mix": Token Mixing; "attention": the self-attention comparator
 
     @property
     def H(self) -> int:
@@ -74,7 +76,11 @@ SWEEP_BATCHES = (64, 256, 1024, 4096, 16384)
 SWEEP = B1.with_(name="rankmixer-1b-sweep", zero_frac=0.10)
 MOE = Config("rankmixer-1b-moe", B=2048, T=32, D=1536, k=4, L=2, dtype="bf16",
              E=8, moe_hidden=3072)
-CONFIGS = {c.name: c for c in (TINY, M100, B1, SWEEP, MOE)}
+# The routing comparator of the pages' ablation: the same blocks with self-attention in place
+# of Token Mixing (the pages ran it at the 100M scale).
+M100_ATTN = M100.with_(name="rankmixer-100m-attention", routing="attention")
+B1_ATTN = B1.with_(name="rankmixer-1b-attention", routing="attention")
+CONFIGS = {c.name: c for c in (TINY, M100, B1, SWEEP, MOE, M100_ATTN, B1_ATTN)}
 
 
 def round_bf16(a: np.ndarray) -> np.ndarray:
@@ -117,6 +123,7 @@ class Inputs:
     ln2_g: np.ndarray
     ln2_b: np.ndarray
     moe: dict = field(default_factory=dict)   # Wg [L,T,D,E], We1 [L,T,E,D,h], be1, We2, be2
+    attn: dict = field(default_factory=dict)  # Wq, Wk, Wv [L, D, D] (self-attention routing)
 
     def layer(self, n: int) -> dict:
         """Parameters of block n (0-based) as a dict of views."""
@@ -124,6 +131,8 @@ class Inputs:
                  ln1_g=self.ln1_g[n], ln1_b=self.ln1_b[n],
                  ln2_g=self.ln2_g[n], ln2_b=self.ln2_b[n])
         for key, arr in self.moe.items():
+            d[key] = arr[n]
+        for key, arr in self.attn.items():
             d[key] = arr[n]
         return d
 
@@ -206,6 +215,9 @@ def make_inputs(cfg: Config, seed: int = 0, B: int | None = None) -> Inputs:
             We2=_stacked_expert(cfg, seed, KIND_WE2, (h, D), 1.0 / np.sqrt(h)),
             be2=_expert_bias(cfg, seed, KIND_BEXP2, (D,)),
         )
+    if cfg.routing == "attention":
+        inp.attn = {name: stacked(kind, (D, D), 1.0 / np.sqrt(D), per_token=False)
+                    for name, kind in (("Wq", KIND_WQ), ("Wk", KIND_WK), ("Wv", KIND_WV))}
     return inp
 
 

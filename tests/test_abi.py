@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = rmx.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.rmx_abi_version() == 4
+    assert lib.rmx_abi_version() == 5
 
 
 def test_status_strings_and_kernel_names():
@@ -40,7 +40,8 @@ def test_status_strings_and_kernel_names():
 
 def _create(**kw):
     lib = rmx.load_library()
-    base = dict(T=4, D=8, k=2, L=1, dtype=binding.RMX_FP32, ln_eps=1e-5, max_batch=8, moe_experts=0, moe_hidden=0)
+    base = dict(T=4, D=8, k=2, L=1, dtype=binding.RMX_FP32, ln_eps=1e-5, max_batch=8, moe_experts=0, moe_hidden=0,
+                routing=binding.RMX_ROUTING_MIX)
     base.update(kw)
     cfg = binding.rmx_config(**base)
     h = ctypes.c_void_p(1234)
@@ -59,6 +60,8 @@ def _create(**kw):
     (dict(T=32, D=1536, dtype=binding.RMX_FP32), binding.RMX_ERR_UNSUPPORTED, "LDS"),
     (dict(D=8192, T=1), binding.RMX_ERR_UNSUPPORTED, "row kernel limit"),
     (dict(D=520, T=130), binding.RMX_ERR_UNSUPPORTED, "row kernel limit"),
+    (dict(routing=7), binding.RMX_ERR_INVALID_ARG, "routing"),
+    (dict(routing=binding.RMX_ROUTING_ATTENTION, T=65, D=130), binding.RMX_ERR_UNSUPPORTED, "attention"),
 ])
 def test_create_rejects_bad_configs_on_the_host(kw, status, text):
     st, h, msg = _create(**kw)
@@ -124,3 +127,10 @@ def test_weights_struct_matches_header():
     body = re.search(r"typedef struct \{([^}]*)\} rmx_weights;", src).group(1)
     fields = re.findall(r"const void\*\s+(\w+);", body)
     assert fields == list(binding.WEIGHT_NAMES)
+
+
+def test_config_struct_matches_header():
+    src = open(os.path.join(ROOT, "include", "rmx.h")).read()
+    body = re.search(r"typedef struct \{([^}]*)\} rmx_config;", src).group(1)
+    fields = re.findall(r"(?:int32_t|int64_t|float)\s+(\w+);", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    assert fields == [f for f, _ in binding.rmx_config._fields_]
