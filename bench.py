@@ -13,7 +13,6 @@ sample on this host's cores.  --sweep prints one line per serving batch size ins
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -27,7 +26,6 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-GEMM_SOURCE = os.path.join(ROOT, "rankmixer_block_forward_amd", "csrc", "rmx_gemm.hip")
 
 
 def parse():
@@ -73,11 +71,6 @@ def gemm_counts(cfg, B):
     return {"gemm1_gelu": (flops, g1), "gemm2_residual": (flops, g2)}
 
 
-def file_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
 def traffic_for(kernel, cfg, B):
     """Per-launch HBM bytes measured with rocprofv3 counters, if taken on the current
     kernel source at this workload; else None."""
@@ -86,7 +79,8 @@ def traffic_for(kernel, cfg, B):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("gemm_source_sha256_16") != file_hash(GEMM_SOURCE):
+    from rankmixer_block_forward_amd import counters
+    if rec.get("gemm_source_sha256_16") != counters.gemm_hash():
         return None
     entry = rec.get("kernels", {}).get(kernel)
     if not entry or entry.get("workload") != f"{cfg.name} B={B}":

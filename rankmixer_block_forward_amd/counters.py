@@ -5,8 +5,8 @@ Two counter passes of the same bench command (rocprofv3 --pmc FETCH_SIZE, then
 written to HBM through the L2.  The bench's --calibrate-copy dispatches of the token-mixing
 kernel move a known number of bytes each way; what the counters read for them gives the
 scale factor from counter KiB to bytes, applied to every other kernel.  The record is
-keyed by the hash of the GEMM source, so the bench reports it only while that source is
-unchanged.
+keyed by the hash of the sources the GEMM kernels are compiled from, so the bench reports
+it only while they are unchanged.
 
     python -m rankmixer_block_forward_amd.counters --fetch F.csv --write W.csv \\
         --workload "rankmixer-1b B=2048" --copy-bytes N --out profiles/traffic_counters.json
@@ -22,7 +22,9 @@ import re
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-GEMM_SOURCE = os.path.join(PKG, "csrc", "rmx_gemm.hip")
+# Every source the grouped-GEMM kernels are compiled from: a record taken on other sources
+# no longer describes the kernels.
+GEMM_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("rmx_gemm.hip", "rmx_device.h", "rmx_internal.h")]
 
 # kernel-name patterns -> the names the library's profiling uses
 KERNELS = [
@@ -55,8 +57,13 @@ def per_dispatch_kib(path, counter):
 
 
 def gemm_hash():
-    with open(GEMM_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of the GEMM kernels' sources, concatenated in the
+    order of GEMM_SOURCES."""
+    h = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def build_record(fetch_csv, write_csv, workload, copy_bytes):

@@ -140,34 +140,43 @@ __device__ __forceinline__ float wave_sum(float v) {
 // With x = |u| / sqrt 2 and q = (1 - erf(x)) / 2 (the a_k halved), Phi(u) = 1 - q for
 // u >= 0 and q for u < 0, so the left tail keeps its relative accuracy.  The 1 / sqrt 2
 // is folded into p and into the exponent: exp(-x^2) = exp2(-u^2 log2(e) / 2).
-// Branch-free: 13 VALU operations, one reciprocal, one exp2.
-// normal_tail(u, &e) returns q = (1 - erf(|u| / sqrt 2)) / 2 and sets e = exp(-u^2 / 2).
-__device__ __forceinline__ float normal_tail(float u, float* e) {
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, fabsf(u), 1.0f));
-  float poly = fmaf(0.5307027145f, t, -0.7265760135f);
-  poly = fmaf(poly, t, 0.7107068705f);
-  poly = fmaf(poly, t, -0.142248368f);
-  poly = fmaf(poly, t, 0.127414796f);
-  poly *= t;
-  *e = __builtin_amdgcn_exp2f((u * -0.72134752044448170f) * u);
-  return poly * *e;
+// The pieces shared by the two GELU entry points below: for a = |u|,
+// t = 1 / (1 + p a / sqrt 2), poly = (a1 + a2 t + ... + a5 t^4) / 2 and e = exp(-u^2 / 2),
+// so that q = (1 - erf(a / sqrt 2)) / 2 = t poly e.
+struct NormalTail {
+  float a, t, poly, e;
+};
+__device__ __forceinline__ NormalTail normal_tail(float u) {
+  NormalTail r;
+  r.a = fabsf(u);
+  r.t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, r.a, 1.0f));
+  float poly = fmaf(0.5307027145f, r.t, -0.7265760135f);
+  poly = fmaf(poly, r.t, 0.7107068705f);
+  poly = fmaf(poly, r.t, -0.142248368f);
+  r.poly = fmaf(poly, r.t, 0.127414796f);
+  r.e = __builtin_amdgcn_exp2f((u * -0.72134752044448170f) * u);
+  return r;
 }
 
-__device__ __forceinline__ float gelu_erf(float u) {
-  float e;
-  const float q = normal_tail(u, &e);
-  return u * (u >= 0.f ? 1.0f - q : q);
+// GELU in the form u Phi(u) = max(u, 0) - |u| q (u q for u < 0, u (1 - q) for u >= 0), with
+// |u| q grouped as (|u| t)(poly e) so that the last step is one fused multiply-add:
+// 10 VALU operations, one reciprocal, one exp2, branch-free.
+__device__ __forceinline__ float gelu_from_tail(float u, const NormalTail& n) {
+  return fmaf(-(n.a * n.t), n.poly * n.e, fmaxf(u, 0.0f));
 }
+
+__device__ __forceinline__ float gelu_erf(float u) { return gelu_from_tail(u, normal_tail(u)); }
 
 // GELU(u) and its derivative GELU'(u) = Phi(u) + u phi(u), phi(u) = exp(-u^2 / 2) /
 // sqrt(2 pi) the standard normal density ("RankMixer 详解（1）", section 5.2), from one erf
-// evaluation: the exponential of the tail serves phi as well.
+// evaluation: the exponential of the tail serves phi as well.  The value is computed
+// exactly as gelu_erf computes it.
 __device__ __forceinline__ float gelu_erf_and_grad(float u, float* grad) {
-  float e;
-  const float q = normal_tail(u, &e);
+  const NormalTail n = normal_tail(u);
+  const float q = n.t * (n.poly * n.e);
   const float Phi = u >= 0.f ? 1.0f - q : q;
-  *grad = fmaf(u * 0.39894228040143268f, e, Phi);
-  return u * Phi;
+  *grad = fmaf(u * 0.39894228040143268f, n.e, Phi);
+  return gelu_from_tail(u, n);
 }
 
 }  // namespace rmx
