@@ -126,6 +126,16 @@ __device__ __forceinline__ int mix_source(int h, int c, int q, int* t_out) {
   return h * q + (c - t * q);
 }
 
+// ---- maximum over the 4 lanes of a quad (lanes 4i .. 4i + 3, the lanes that hold one MX
+// scale block), every lane of the quad receives it.  Two DPP quad permutations (lane i takes
+// lane i ^ 1, then i ^ 2) instead of LDS-routed shuffles.  The lane read is always active
+// where this is called; were it not, DPP would return the `old` operand 0, which leaves a
+// maximum of absolute values unchanged.
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+}
+
 // ---- wavefront (64 lanes) sum, every lane receives the total.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

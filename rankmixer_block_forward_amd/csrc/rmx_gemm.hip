@@ -374,15 +374,14 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], flo
       v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
       if constexpr (EPI == EPI_GELU_MX) {
         // GELU, then MXFP8 along the row: the 32 columns of one scale block are the 8
-        // columns of 4 neighbouring lanes of this row (shuffles run on every lane)
+        // columns of 4 neighbouring lanes of this row (the exchange runs on every lane)
         float amax = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           v[e] = gelu_erf(v[e] + bias[e]);
           amax = fmaxf(amax, fabsf(v[e]));
         }
-        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+        amax = quad_max(amax);
         const uint32_t sb = mx_scale_bits(amax);
         const float inv = mx_inv_scale(sb);
 #pragma unroll

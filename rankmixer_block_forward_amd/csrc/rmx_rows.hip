@@ -155,7 +155,7 @@ __global__ __launch_bounds__(64 * rows_max_waves(NC, MODE)) void rows_kernel(Row
         }
         if (a.s8) {
           // S in MXFP8 along D: the 32 columns of a scale block are the chunks of 4
-          // neighbouring lanes (shuffles run on every lane; D % 64 == 0 keeps such a group
+          // neighbouring lanes (the exchange runs on every lane; D % 64 == 0 keeps such a group
           // wholly inside or outside the row)
           uint8_t* codes = static_cast<uint8_t*>(a.s8) + size_t(h) * size_t(pk_rows(B)) * D;
           uint8_t* scales = static_cast<uint8_t*>(a.s8_scale) + size_t(h) * size_t(pk_rows(B)) * D / 32;
@@ -166,8 +166,7 @@ __global__ __launch_bounds__(64 * rows_max_waves(NC, MODE)) void rows_kernel(Row
             if (c < nchunks)
 #pragma unroll
               for (int e = 0; e < W; ++e) amax = fmaxf(amax, fabsf(r[i][e]));
-            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+            amax = quad_max(amax);
             const uint32_t sb = mx_scale_bits(amax);
             const float inv = mx_inv_scale(sb);
             if (c < nchunks) {
