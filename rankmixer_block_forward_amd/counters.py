@@ -10,6 +10,11 @@ it only while they are unchanged.
 
     python -m rankmixer_block_forward_amd.counters --fetch F.csv --write W.csv \\
         --workload "rankmixer-1b B=2048" --copy-bytes N --out profiles/traffic_counters.json
+
+A pass of SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and SQ_INSTS_VALU_MFMA_MOPS_BF16 gives the
+matrix cores' utilisation and the clock they ran at, per kernel:
+
+    python -m rankmixer_block_forward_amd.counters --mfma C.csv --agents A.csv
 """
 from __future__ import annotations
 
@@ -90,14 +95,66 @@ def build_record(fetch_csv, write_csv, workload, copy_bytes):
             "kernels": kernels}
 
 
+def gpu_agent(agent_csv):
+    """(SIMD count, XCC count) of the first GPU agent in a rocprofv3 agent-info file."""
+    with open(agent_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Agent_Type") == "GPU":
+                return int(row["Simd_Count"]), int(row["Num_Xcc"])
+    raise SystemExit("no GPU agent in " + agent_csv)
+
+
+def mfma_utilisation(counter_csv, agent_csv):
+    """Matrix-core utilisation per kernel class from one counter pass of
+    SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and SQ_INSTS_VALU_MFMA_MOPS_BF16.
+
+    Per dispatch: the GPU clock in GHz is GRBM_GUI_ACTIVE (summed over the XCCs) / XCCs / the
+    dispatch's duration in ns; utilisation is the MFMA busy cycles (summed over the SIMDs)
+    / (SIMDs x GRBM_GUI_ACTIVE / XCCs), i.e. the fraction of the kernel's cycles in which an
+    average SIMD's matrix core was busy; FLOPs are 512 x the MOPS counter.  Means over the
+    dispatches of each class."""
+    simds, xcc = gpu_agent(agent_csv)
+    disp = defaultdict(dict)
+    with open(counter_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            k = classify(row.get("Kernel_Name", ""))
+            if k is None:
+                continue
+            d = disp[(k, row["Dispatch_Id"])]
+            d[row["Counter_Name"]] = float(row["Counter_Value"])
+            d["ns"] = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+    out = defaultdict(lambda: defaultdict(list))
+    for (k, _), d in disp.items():
+        cycles = d["GRBM_GUI_ACTIVE"] / xcc
+        out[k]["ms"].append(d["ns"] / 1e6)
+        out[k]["clock_ghz"].append(cycles / d["ns"])
+        out[k]["mfma_busy"].append(d["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cycles))
+        out[k]["tflops"].append(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / d["ns"] / 1e3)
+    return {k: dict({n: sum(v) / len(v) for n, v in c.items()}, dispatches=len(c["ms"]))
+            for k, c in out.items()}
+
+
 def main():
     p = argparse.ArgumentParser()
-    p.add_argument("--fetch", required=True)
-    p.add_argument("--write", required=True)
-    p.add_argument("--workload", required=True)
-    p.add_argument("--copy-bytes", type=int, required=True)
-    p.add_argument("--out", required=True)
+    p.add_argument("--fetch")
+    p.add_argument("--write")
+    p.add_argument("--workload")
+    p.add_argument("--copy-bytes", type=int)
+    p.add_argument("--out")
+    p.add_argument("--mfma", help="counter file of an MFMA utilisation pass: print the table instead")
+    p.add_argument("--agents", help="the agent-info file of the same pass (with --mfma)")
     a = p.parse_args()
+    if a.mfma:
+        if not a.agents:
+            p.error("--mfma needs --agents")
+        print("| kernel | dispatches | ms (instrumented) | clock (GHz) | MFMA busy | TFLOP/s |")
+        print("|---|---|---|---|---|---|")
+        for k, e in sorted(mfma_utilisation(a.mfma, a.agents).items()):
+            print(f"| {k} | {e['dispatches']} | {e['ms']:.4f} | {e['clock_ghz']:.3f} | "
+                  f"{100 * e['mfma_busy']:.1f}% | {e['tflops']:.1f} |")
+        return
+    if not (a.fetch and a.write and a.workload and a.copy_bytes and a.out):
+        p.error("the traffic record needs --fetch, --write, --workload, --copy-bytes and --out")
     rec = build_record(a.fetch, a.write, a.workload, a.copy_bytes)
     with open(a.out, "w") as f:
         json.dump(rec, f, indent=1)

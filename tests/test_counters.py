@@ -49,3 +49,35 @@ def test_committed_record_is_well_formed():
     for k, e in rec["kernels"].items():
         assert e["bytes_per_launch"] == e["fetch_bytes"] + e["write_bytes"] or \
             abs(e["bytes_per_launch"] - e["fetch_bytes"] - e["write_bytes"]) <= 1
+
+
+def test_mfma_utilisation_arithmetic(tmp_path):
+    """Clock = GRBM_GUI_ACTIVE / XCCs / duration; busy = MFMA busy cycles / (SIMDs x cycles);
+    FLOPs = 512 x MOPS.  One GPU agent with 4 SIMDs on 2 XCCs, two dispatches of GEMM1."""
+    with open(tmp_path / "a.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Agent_Type", "Simd_Count", "Num_Xcc"])
+        w.writeheader()
+        w.writerow({"Agent_Type": "CPU", "Simd_Count": 0, "Num_Xcc": 0})
+        w.writerow({"Agent_Type": "GPU", "Simd_Count": 4, "Num_Xcc": 2})
+    g1 = "void rmx::(anonymous namespace)::gemm_bf16_mfma<0, true, false, false>(rmx::GemmArgs)"
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    with open(tmp_path / "c.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for disp, (gui, busy, start, end) in enumerate([(2000.0, 2000.0, 100, 600), (4000.0, 1000.0, 0, 1000)]):
+            for name, val in (("GRBM_GUI_ACTIVE", gui), ("SQ_VALU_MFMA_BUSY_CYCLES", busy),
+                              ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 1000.0)):
+                w.writerow({"Dispatch_Id": disp, "Kernel_Name": g1, "Counter_Name": name, "Counter_Value": val,
+                            "Start_Timestamp": start, "End_Timestamp": end})
+            w.writerow({"Dispatch_Id": 9, "Kernel_Name": "other", "Counter_Name": "GRBM_GUI_ACTIVE",
+                        "Counter_Value": 1.0, "Start_Timestamp": 0, "End_Timestamp": 1})
+    u = counters.mfma_utilisation(str(tmp_path / "c.csv"), str(tmp_path / "a.csv"))
+    assert set(u) == {"gemm1_gelu"}
+    e = u["gemm1_gelu"]
+    assert e["dispatches"] == 2
+    # dispatch 0: 1000 cycles in 500 ns = 2 GHz, busy 2000 / (4 x 1000) = 0.5, 512000 FLOP / 500 ns
+    # dispatch 1: 2000 cycles in 1000 ns = 2 GHz, busy 1000 / (4 x 2000) = 0.125, 512000 / 1000 ns
+    assert abs(e["clock_ghz"] - 2.0) < 1e-12
+    assert abs(e["mfma_busy"] - (0.5 + 0.125) / 2) < 1e-12
+    assert abs(e["ms"] - (500 + 1000) / 2 / 1e6) < 1e-15
+    assert abs(e["tflops"] - (512000 / 500 + 512000 / 1000) / 2 / 1e3) < 1e-9
