@@ -85,8 +85,9 @@ def test_zero_token_rows_fp32():
     (50, 4, 96, 2, 2),     # 64-row tiles, odd K-step count (K = 96)
     (50, 5, 40, 2, 2),     # K = 40 not a multiple of 32: generic kernel in bf16
     (1, 16, 768, 4, 2),    # one sample at the 100M width (64-row tiles)
-    (64, 8, 512, 4, 1),    # largest batch on the 64-row tiles
-    (65, 8, 512, 4, 1),    # smallest batch on the 256-row tiles
+    (64, 8, 512, 4, 1),    # one full 64-row tile
+    (128, 8, 512, 4, 1),   # largest batch on the 64-row tiles
+    (129, 8, 512, 4, 1),   # smallest batch on the 256-row tiles
     (513, 16, 768, 4, 1),  # one row past a tile boundary
 ])
 def test_bf16_shapes(B, T, D, k, L):
@@ -132,8 +133,9 @@ def test_small_batch_deterministic():
     (300, 4, 256, 4, 2),   # 256-row tiles, ragged rows
     (77, 5, 320, 2, 1),    # ragged column tiles (kD = 640, D = 320)
     (33, 8, 256, 4, 2),    # 64-row tiles
-    (64, 8, 512, 4, 1),    # largest batch on the 64-row tiles
-    (65, 8, 512, 4, 1),    # smallest batch on the 256-row tiles
+    (65, 8, 512, 4, 1),    # 64-row tiles, one row into the second
+    (128, 8, 512, 4, 1),   # largest batch on the 64-row tiles
+    (129, 8, 512, 4, 1),   # smallest batch on the 256-row tiles
     (1, 16, 768, 4, 2),    # one sample
 ])
 def test_prepared_weights_bit_identical(B, T, D, k, L):
