@@ -84,9 +84,7 @@ __global__ __launch_bounds__(64 * ATTN_MAX_WAVES) void attn_rows_kernel(AttnArgs
     float p[QG];
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
-      float m = sc[g];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      const float m = wave_max(sc[g]);
       const float ex = lane < Tn ? __expf(sc[g] - m) : 0.f;
       p[g] = ex / wave_sum(ex);
     }

@@ -126,21 +126,45 @@ __device__ __forceinline__ int mix_source(int h, int c, int q, int* t_out) {
   return h * q + (c - t * q);
 }
 
-// ---- maximum over the 4 lanes of a quad (lanes 4i .. 4i + 3, the lanes that hold one MX
-// scale block), every lane of the quad receives it.  Two DPP quad permutations (lane i takes
-// lane i ^ 1, then i ^ 2) instead of LDS-routed shuffles.  The lane read is always active
-// where this is called; were it not, DPP would return the `old` operand 0, which leaves a
-// maximum of absolute values unchanged.
-__device__ __forceinline__ float quad_max(float v) {
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
-  return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+// ---- cross-lane exchanges through DPP (the VALU reads a neighbouring lane directly), not
+// through LDS-routed shuffles.  dpp_take<CTRL>(v) returns v of the lane that the DPP control
+// CTRL names: 0xB1 = quad_perm [1,0,3,2] (lane ^ 1), 0x4E = quad_perm [2,3,0,1] (lane ^ 2),
+// 0x141 = row_half_mirror (lane i <-> 7 - i within 8), 0x140 = row_mirror (i <-> 15 - i
+// within 16).  Callers run them with every lane of the wave active; a lane read while
+// inactive would give the `old` operand 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp_take(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
-// ---- wavefront (64 lanes) sum, every lane receives the total.
+// Maximum over the 4 lanes of a quad (lanes 4i .. 4i + 3, the lanes that hold one MX scale
+// block); every lane of the quad receives it.
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_take<0xB1>(v));
+  return fmaxf(v, dpp_take<0x4E>(v));
+}
+
+// Wavefront (64 lanes) sum; every lane receives the same total.  Butterflies within each
+// 16-lane row (each pairwise sum is formed by both partners, so the lanes of a row agree bit
+// for bit), then the four row sums read from lanes 0, 16, 32, 48 and added in a fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v += dpp_take<0xB1>(v);
+  v += dpp_take<0x4E>(v);
+  v += dpp_take<0x141>(v);
+  v += dpp_take<0x140>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+// Wavefront maximum, the same pattern.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_take<0xB1>(v));
+  v = fmaxf(v, dpp_take<0x4E>(v));
+  v = fmaxf(v, dpp_take<0x141>(v));
+  v = fmaxf(v, dpp_take<0x140>(v));
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
 // GELU(u) = u * Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), the exact (erf) form.
