@@ -33,8 +33,8 @@ GEMM_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("rmx_gemm.hip", "rmx_devi
 
 # kernel-name patterns -> the names the library's profiling uses
 KERNELS = [
-    (re.compile(r"gemm_bf16_mfma<0[,>]"), "gemm1_gelu"),
-    (re.compile(r"gemm_bf16_mfma<1[,>]"), "gemm2_residual"),
+    (re.compile(r"gemm_bf16_mfma(_n384)?<0[,>]"), "gemm1_gelu"),
+    (re.compile(r"gemm_bf16_mfma(_n384)?<1[,>]"), "gemm2_residual"),
     (re.compile(r"gemm_bf16_moe<2>"), "moe_ffn1"),
     (re.compile(r"gemm_bf16_moe<3>"), "moe_ffn2"),
     (re.compile(r"token_mix_kernel"), "copy"),

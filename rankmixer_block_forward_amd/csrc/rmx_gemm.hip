@@ -619,6 +619,248 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
                                2 * mt + (wave >> 1));
 }
 
+// ------------------------------------------------------------- 256 x 384 tiles
+// Where N is a multiple of 384, the packed-operand products run 256 x 384 tiles: each wave
+// owns 128 x 192 outputs (4 x 6 blocks of 32 x 32), and the operand bytes copied into LDS per
+// FLOP drop by 17 % against 256 x 256 tiles (the copy rate of a CU bounds the K loop).  The
+// 384 accumulators per lane exceed the 256 AGPRs: column blocks 0..3 use the builtin (the
+// compiler keeps them in AGPRs), blocks 4..5 an MFMA in inline assembly with VGPR
+// accumulators.  The compiler does not see the instruction inside the assembly, so explicit
+// wait states guard its VGPR hazards: after the VALU zeroes the accumulators, before a
+// fragment register an assembly MFMA has read is rewritten by an LDS read, and before the
+// epilogue reads the results.  Per block, the products are accumulated in the same order as
+// in the 256 x 256 kernel, so the two give the same bits.
+constexpr int BN6 = 384;
+constexpr int STAGE6_BYTES = A_STAGE_BYTES + BN6 * BK * 2;  // 16 KB of A + 24 KB of W^T
+constexpr int PK6_NS = 3;
+constexpr int LD6 = 2 * 32 + 4;                             // epilogue staging rows: 64 columns
+
+// K loop of one 256 x 384 tile.  A stage holds the tile's 16 KB A block and three 8 KB halves
+// (128 output columns each) of W^T blocks: 40 contiguous 1 KB pieces, 10 per wave (wave w
+// takes pieces w, w + 4, ...: 4 of A and 6 of W^T).  W^T half-block H = 3 nt + (piece / 8)
+// of the token is rows 128 H .. 128 H + 127: block H / 2, half H % 2.  Row r of the stage's
+// W^T part is tile column r; the chunk swizzle depends on r % 8, which a half-block keeps.
+__device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (&accV)[4][2],
+                                              __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rW, lds_u8* smem,
+                                              uint32_t lds0, int K, int nt, int wave, int lane) {
+  const int nk = K / BK;
+  uint32_t voffW[6];
+#pragma unroll
+  for (int c = 0; c < 6; ++c) {
+    const int q = wave + 4 * c;
+    const int hb = 3 * nt + (q >> 3);
+    voffW[c] = uint32_t(hb >> 1) * uint32_t(nk) * 16384u + uint32_t(hb & 1) * 8192u + uint32_t(q & 7) * 1024u +
+               uint32_t(lane) * 16u;
+  }
+  // copy c (0..9) of K step kt into ring stage `stage`; steps past the end reload the last
+  // step (in bounds, never read) so that every K step issues the same number of loads
+  auto copy = [&](int kt, int stage, int c) {
+    kt = kt < nk ? kt : nk - 1;
+    const uint32_t sbase = lds0 + uint32_t(stage) * STAGE6_BYTES;
+    if (c < 4) {
+      const uint32_t piece = uint32_t(wave + 4 * c);
+      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), piece * 1024u + uint32_t(lane) * 16u, rA,
+                  kt * 16384);
+    } else {
+      const uint32_t q = uint32_t(wave + 4 * (c - 4));
+      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + A_STAGE_BYTES + q * 1024u), voffW[c - 4], rW, kt * 16384);
+    }
+  };
+  const int wm = wave >> 1, wn = wave & 1;
+  uint32_t aoff[2], boff[2];  // row block i / column block j at + 2048 i / + 2048 j
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int c = kk * 2 + (lane >> 5);
+    const int m = wm * 128 + (lane & 31);
+    aoff[kk] = uint32_t(m * 64 + ((c ^ pk_swz(m)) << 4));
+    const int n = wn * 192 + (lane & 31);
+    boff[kk] = uint32_t(A_STAGE_BYTES + n * 64 + ((c ^ pk_swz(n)) << 4));
+  }
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  // a0 / a1: A fragments of sub-steps 0 / 1; b[j]: the W^T fragment of column block j,
+  // refilled right after the MFMAs that use it (sub-step 1 of this stage, then sub-step 0 of
+  // the next), which keeps the fragments at 56 registers
+  u32x4_t a0[4], a1[4], b[6];
+  auto read_a = [&](u32x4_t (&a)[4], const lds_u8* sp, int kk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const lds_u32x4*>(sp + aoff[kk] + i * 2048);
+  };
+  auto read_b = [&](const lds_u8* sp, int kk, int j) {
+    if (j >= 4) asm volatile("s_nop 7" ::: "memory");  // an assembly MFMA read b[j] just before
+    b[j] = *reinterpret_cast<const lds_u32x4*>(sp + boff[kk] + j * 2048);
+  };
+  auto mm = [&](const u32x4_t (&a)[4], int i, int j) {
+    if (j < 4)
+      accA[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[j]),
+                                                           __builtin_bit_cast(bf16x8_t, a[i]), accA[i][j], 0, 0, 0);
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(accV[i][j - 4]) : "v"(b[j]), "v"(a[i]));
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) accA[i][j][r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) accV[i][j][r] = 0.f;
+  }
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // the zeroed VGPR accumulators settle
+  // prologue: steps 0..PK6_NS-1; wait for step 0 (10 loads per step)
+#pragma unroll
+  for (int st = 0; st < PK6_NS; ++st)
+#pragma unroll
+    for (int c = 0; c < 10; ++c) copy(st, st, c);
+  asm volatile("s_waitcnt vmcnt(20)\n\ts_barrier" ::: "memory");
+  read_a(a0, smem, 0);
+#pragma unroll
+  for (int j = 0; j < 6; ++j) read_b(smem, 0, j);
+  int stage = 0;
+  for (int it = 0; it < nk; ++it) {
+    const lds_u8* sp = smem + stage * STAGE6_BYTES;
+    const int nstage = stage + 1 == PK6_NS ? 0 : stage + 1;
+    // sub-step 0 on a0 / b; sub-step 1's fragments of this stage read behind the MFMAs
+    read_a(a1, sp, 1);
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mm(a0, i, j);
+      __builtin_amdgcn_sched_barrier(0);
+      read_b(sp, 1, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // every read of this stage has returned; after the barrier step it+1 is visible (the 10
+    // loads of the step after it may be outstanding) and this stage takes step it+PK6_NS
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // sub-step 1 on a1 / b; the next stage's sub-step 0 fragments and this stage's refill
+    // between the MFMAs
+    const lds_u8* np = smem + nstage * STAGE6_BYTES;
+    read_a(a0, np, 0);
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        mm(a1, 2 * h, j);
+        mm(a1, 2 * h + 1, j);
+        if (2 * j + h < 10) {
+          __builtin_amdgcn_sched_barrier(0);
+          copy(it + PK6_NS, stage, 2 * j + h);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      read_b(np, 0, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    stage = nstage;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");  // the last MFMAs' results settle
+  __syncthreads();
+}
+
+// GELU (packed H out) or residual (packed S in, fp32 Y out) epilogue of a 256 x 384 tile, the
+// arithmetic of tile_epilogue: per row block i of the wave and group of two column blocks,
+// 32 rows x 64 columns are staged through LDS so that each lane then owns 8 consecutive
+// columns of one row (8 lanes per row, 8 rows per pass).
+template <int EPI>
+__device__ __forceinline__ void tile_epilogue6(const f32x16_t (&accA)[4][4], const f32x16_t (&accV)[4][2],
+                                               float* smem_f, const GemmArgs& p, int g, int m0, int n0, int wave,
+                                               int lane) {
+  const int M = p.M, N = p.N;
+  const int wrow0 = (wave >> 1) * 128, wcol0 = (wave & 1) * 192;
+  float* st = smem_f + wave * 32 * LD6;
+  const int col8 = (lane & 7) * 8;
+  const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
+  float bias[3][8];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bias[s][e] = 0.f;
+    const int n = n0 + wcol0 + s * 64 + col8;
+    if (bias_g && n < N) load8(bias_g + n, bias[s]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int jb = 2 * s + jj;
+        const f32x16_t& a = jb < 4 ? accA[i][jb] : accV[i][jb - 4];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<float4*>(st + (lane & 31) * LD6 + jj * 32 + 8 * g4 + 4 * (lane >> 5)) =
+              make_float4(a[4 * g4], a[4 * g4 + 1], a[4 * g4 + 2], a[4 * g4 + 3]);
+      }
+      // the staging rows are private to this wave, whose LDS operations complete in order
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        const int row = pass * 8 + (lane >> 3);
+        const int m = m0 + wrow0 + i * 32 + row;
+        const int n = n0 + wcol0 + s * 64 + col8;
+        float v[8];
+        const float4 x0 = *reinterpret_cast<const float4*>(st + row * LD6 + col8);
+        const float4 x1 = *reinterpret_cast<const float4*>(st + row * LD6 + col8 + 4);
+        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+        if (m < M && n < N) {
+          const size_t pko = size_t(g) * size_t(pk_rows(M)) * N + pk_off(m, n, N);
+          if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[s][e]);
+            store8(static_cast<bf16_t*>(p.C) + pko, v);
+          } else {
+            float rr[8];
+            load8(static_cast<const bf16_t*>(p.R) + pko, rr);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = v[e] + bias[s][e] + rr[e];
+            store8(static_cast<float*>(p.C) + size_t(g) * size_t(p.sc) + size_t(m) * size_t(p.ldc) + n, v);
+          }
+        }
+      }
+      asm volatile("" ::: "memory");
+    }
+}
+
+// Dense per-token product on packed operands with 256 x 384 tiles: G * ceil(M/256) * N/384
+// workgroups, N % 384 == 0; EPI_GELU or EPI_RESID.
+template <int EPI>
+__global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384(GemmArgs p) {
+  static_assert(EPI == EPI_GELU || EPI == EPI_RESID, "256 x 384 tiles serve the inference epilogues");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[PK6_NS * STAGE6_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_g;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nMt = (M + BM - 1) / BM, nNt = N / BN6;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = id / (nMt * nNt);
+  const int rem = id - g * nMt * nNt;
+  // bands of TILE_BAND row tiles, M-fastest inside a band (as in the 256 x 256 kernel)
+  const int band = rem / (TILE_BAND * nNt);
+  const int in_band = rem - band * TILE_BAND * nNt;
+  const int bm = min(TILE_BAND, nMt - band * TILE_BAND);
+  const int nt = in_band / bm, mt = band * TILE_BAND + (in_band - (in_band / bm) * bm);
+  // the tile's A blocks (row block mt, K/32 x 16 KB) and the token's whole W^T (pk_rows(N)
+  // rows; slices < 2^31 bytes, checked at launch)
+  const uint32_t blk = uint32_t(K / BK) * 16384u;
+  const uint32_t wbytes = uint32_t(pk_rows(N) / 256) * blk;
+  const __amdgpu_buffer_rsrc_t rA =
+      make_rsrc(static_cast<const uint16_t*>(p.A) + (size_t(g) * nMt + mt) * (size_t(blk) / 2), blk);
+  const __amdgpu_buffer_rsrc_t rW =
+      make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * (size_t(wbytes) / 2), wbytes);
+  f32x16_t accA[4][4], accV[4][2];
+  mfma_tile_pk6(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane);
+  tile_epilogue6<EPI>(accA, accV, reinterpret_cast<float*>(smem_g), p, g, mt * BM, nt * BN6, wave, lane);
+}
+
 // ------------------------------------------------------------- MXFP8 products
 // The prepared-operand K loop with 8-bit operands: a K step is 64 values, so a stage holds
 // the same 16 KB per operand (256 rows x 64 E4M3 codes, one contiguous block of the MXFP8
@@ -1179,6 +1421,17 @@ hipError_t launch_dense_mfma(int epi, const GemmArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_BIAS, false>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
     else
       hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_RESID, PK>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+    return hipGetLastError();
+  }
+  // 256 x 384 tiles where N allows them; their buffer descriptor spans a token's whole packed
+  // W^T, which must stay below 2^31 bytes
+  if (PK && a.N % BN6 == 0 && (epi == EPI_GELU || epi == EPI_RESID) &&
+      uint64_t(pk_rows(a.N)) * uint64_t(a.K) * 2u < (uint64_t(1) << 31)) {
+    const int tiles6 = a.G * ((a.M + BM - 1) / BM) * (a.N / BN6);
+    if (epi == EPI_GELU)
+      hipLaunchKernelGGL((gemm_bf16_mfma_n384<EPI_GELU>), dim3(tiles6), dim3(MFMA_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_mfma_n384<EPI_RESID>), dim3(tiles6), dim3(MFMA_THREADS), 0, stream, a);
     return hipGetLastError();
   }
   const int tiles = a.G * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);

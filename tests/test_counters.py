@@ -16,7 +16,7 @@ def _write(path, rows):
 
 def test_record_scales_by_copy_calibration(tmp_path):
     g1 = "void rmx::(anonymous namespace)::gemm_bf16_mfma<0>(rmx::GemmArgs)"
-    g2 = "void rmx::(anonymous namespace)::gemm_bf16_mfma<1>(rmx::GemmArgs)"
+    g2 = "void rmx::(anonymous namespace)::gemm_bf16_mfma_n384<1>(rmx::GemmArgs)"
     cp = "void rmx::(anonymous namespace)::token_mix_kernel<rmx::bf16_t, 8>(rmx::bf16_t const*, ...)"
     other = "void at::native::vectorized_elementwise_kernel<4>(...)"
     copy_bytes = 1 << 30

@@ -137,6 +137,10 @@ def test_small_batch_deterministic():
     (128, 8, 512, 4, 1),   # largest batch on the 64-row tiles
     (129, 8, 512, 4, 1),   # smallest batch on the 256-row tiles
     (1, 16, 768, 4, 2),    # one sample
+    (300, 4, 384, 4, 2),   # 256 x 384 tiles in both products, ragged rows
+    (129, 8, 384, 2, 1),   # 256 x 384 tiles, one row past the 64-row kernel
+    (257, 4, 1152, 2, 1),  # 256 x 384 tiles, three (D) and six (kD) column tiles, two row tiles
+    (300, 4, 256, 3, 2),   # GEMM1 on 256 x 384 tiles (kD = 768), GEMM2 on 256 x 256 (D = 256)
 ])
 def test_prepared_weights_bit_identical(B, T, D, k, L):
     """Weights prepared by rmx_pack_weights (and the packed S and H they bring) give the
