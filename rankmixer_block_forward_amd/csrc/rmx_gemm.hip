@@ -12,6 +12,9 @@
 //                   (the fp32 path and shapes the MFMA kernel does not take).
 // Epilogues: EPI_GELU writes GELU(acc + bias) in the input dtype (the hidden
 // activations); EPI_RESID writes acc + bias + R in fp32 (the pre-LN2 rows).
+#include <cstdlib>
+#include <cstring>
+
 #include "rmx_device.h"
 #include "rmx_internal.h"
 
@@ -1411,6 +1414,25 @@ hipError_t launch_gemm_moe(int epi, const GemmArgs& args, hipStream_t stream) {
 
 namespace {
 
+// 256 x 384 tiles where N allows them (their buffer descriptor spans a token's whole packed
+// W^T, which must stay below 2^31 bytes) and where they take fewer rounds of the whole
+// device: a 256 x 384 tile runs about 1.4x as long as a 256 x 256 one, so with rounds =
+// ceil(tiles / CUs) they win when 1.4 x rounds(384) < rounds(256).  (Measured at the 1B
+// shapes: B = 256, GEMM2 on 128 wide tiles for 256 CUs, 231 against 197 us.)  The
+// environment variable RMX_WIDE_TILES = "always" / "never" overrides the choice (tests and
+// tuning); both kernels give the same bits.
+bool wide_tiles_pay(const GemmArgs& a) {
+  const char* force = getenv("RMX_WIDE_TILES");
+  if (force && strcmp(force, "never") == 0) return false;
+  if (a.N % BN6 != 0 || uint64_t(pk_rows(a.N)) * uint64_t(a.K) * 2u >= (uint64_t(1) << 31)) return false;
+  if (force && strcmp(force, "always") == 0) return true;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t mt = (a.M + BM - 1) / BM;
+  const int64_t t6 = int64_t(a.G) * mt * (a.N / BN6), t4 = int64_t(a.G) * mt * ((a.N + BN - 1) / BN);
+  return 7 * ((t6 + cus - 1) / cus) < 5 * ((t4 + cus - 1) / cus);
+}
+
 template <bool PK>
 hipError_t launch_dense_mfma(int epi, const GemmArgs& a, hipStream_t stream) {
   if (a.M <= GEMM_SMALL_M) {
@@ -1423,10 +1445,7 @@ hipError_t launch_dense_mfma(int epi, const GemmArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_RESID, PK>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
     return hipGetLastError();
   }
-  // 256 x 384 tiles where N allows them; their buffer descriptor spans a token's whole packed
-  // W^T, which must stay below 2^31 bytes
-  if (PK && a.N % BN6 == 0 && (epi == EPI_GELU || epi == EPI_RESID) &&
-      uint64_t(pk_rows(a.N)) * uint64_t(a.K) * 2u < (uint64_t(1) << 31)) {
+  if (PK && (epi == EPI_GELU || epi == EPI_RESID) && wide_tiles_pay(a)) {
     const int tiles6 = a.G * ((a.M + BM - 1) / BM) * (a.N / BN6);
     if (epi == EPI_GELU)
       hipLaunchKernelGGL((gemm_bf16_mfma_n384<EPI_GELU>), dim3(tiles6), dim3(MFMA_THREADS), 0, stream, a);

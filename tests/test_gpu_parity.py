@@ -142,14 +142,21 @@ def test_small_batch_deterministic():
     (257, 4, 1152, 2, 1),  # 256 x 384 tiles, three (D) and six (kD) column tiles, two row tiles
     (300, 4, 256, 3, 2),   # GEMM1 on 256 x 384 tiles (kD = 768), GEMM2 on 256 x 256 (D = 256)
 ])
-def test_prepared_weights_bit_identical(B, T, D, k, L):
+def test_prepared_weights_bit_identical(B, T, D, k, L, monkeypatch):
     """Weights prepared by rmx_pack_weights (and the packed S and H they bring) give the
-    same bits as the row-major path, and match the oracle."""
+    same bits as the row-major path, and match the oracle; the same with the 256 x 384 tiles
+    forced where N % 384 == 0 (RMX_WIDE_TILES=always) and forbidden (=never), since at these
+    sizes the launch would pick by device occupancy."""
     cfg = synth.Config("pk", B=B, T=T, D=D, k=k, L=L, dtype="bf16", bias_std=0.02)
     inp = synth.make_inputs(cfg, seed=B + 3 * D)
     o1, xl1 = run_gpu(cfg, inp)
     o2, xl2 = run_gpu(cfg, inp, packed=True)
     assert np.array_equal(o1, o2) and np.array_equal(xl1, xl2)
+    for policy in ("always", "never"):
+        monkeypatch.setenv("RMX_WIDE_TILES", policy)
+        o3, xl3 = run_gpu(cfg, inp, packed=True)
+        assert np.array_equal(o1, o3) and np.array_equal(xl1, xl3), policy
+    monkeypatch.delenv("RMX_WIDE_TILES")
     rows = sample_rows(B, 32)
     o_ref, xl_ref = run_oracle(cfg, inp, rows)
     check(cfg, o2[rows], xl2[rows], o_ref, xl_ref, f"prepared {B}x{T}x{D} k{k} L{L}")
