@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--sweep", action="store_true", help="one line per serving batch size")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-samples", type=int, default=384)
+    p.add_argument("--cpu-samples", type=int, default=1152)
     p.add_argument("--routing-comparison", action="store_true",
                    help="Token Mixing versus the self-attention comparator at the 100M and 1B shapes")
     p.add_argument("--mxfp8", action="store_true",
