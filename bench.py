@@ -51,6 +51,9 @@ def parse():
                    help="time the vendor library's bf16 GEMM (torch.mm / torch.bmm on contiguous "
                         "operands) at reference shapes and at the two grouped-GEMM shapes, one JSON "
                         "line each, for scale; no RankMixer work")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the same forward captured once in a HIP graph and replayed "
+                        "(torch.cuda.CUDAGraph on the caller's stream): adds a hip_graph object")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="after the timed region, run the library's token-mixing kernel (a pure "
                         "permutation copy of the input, bytes known) three times: the reference "
@@ -154,6 +157,45 @@ def time_forward(cfg, B, steps, warmup, calibrate_copy=False, mxfp8=False, prepa
         del calib
     h.close()
     return elapsed, prof, moe
+
+
+def time_graph(cfg, B, steps, warmup, mxfp8=False):
+    """The forward captured once into a HIP graph and replayed: wall time of `steps` replays
+    after `warmup` replays (inputs resident, weights prepared as in time_forward)."""
+    import torch
+    import rankmixer_block_forward_amd as rmx
+    from rankmixer_block_forward_amd import synth
+
+    inp = synth.make_inputs(cfg.with_(B=B), seed=0)
+    X, w = rmx.upload(inp)
+    del inp
+    h = rmx.Handle.for_config(cfg, max_batch=B)
+    if mxfp8:
+        w["packed_mxfp8"] = h.pack_weights_mxfp8(w)
+    elif h.packed_weights_bytes() > 0:
+        w["packed"] = h.pack_weights(w)
+    out = torch.empty((B, cfg.D), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        h.forward(X, w, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h.forward(X, w, out=out)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert torch.isfinite(out).all().item(), "non-finite output"
+    del g
+    h.close()
+    return elapsed
 
 
 def roofline(cfg, B, prof, peak_tflops=PEAK_BF16_TFLOPS):
@@ -466,6 +508,11 @@ def main():
             line["frac_fp8_peak"] = round(tflops / PEAK_FP8_TFLOPS, 4)
         if moe is not None:
             line["config"].update(experts=cfg.E, expert_hidden=cfg.moe_hidden, active_fraction=round(moe[1], 4))
+        if args.graph and moe is None:
+            g_el = time_graph(cfg, B, args.steps, args.warmup, args.mxfp8)
+            g_ms = g_el / args.steps * 1e3
+            line["hip_graph"] = {"value": round(B / (g_ms / 1e3), 1), "unit": "samples/s",
+                                 "ms_per_step": round(g_ms, 4)}
         if not args.sweep and not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_samples)
         print(json.dumps(line), flush=True)
