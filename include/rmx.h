@@ -105,10 +105,11 @@ typedef struct {
  *   Wg  [L, T, D, E]              router weights, no bias
  *   We1 [L, T, E, D, h]  be1 [L, T, E, h]   (be1 may be NULL)
  *   We2 [L, T, E, h, D]  be2 [L, T, E, D]   (be2 may be NULL)
- * packed: NULL, or W1 and W2 of all blocks prepared by rmx_pack_weights for this handle
- *   (dense bf16 handles whose D and k*D are multiples of 32).  When set, the forward reads
- *   the weights from it (W1 and W2 are then unused and may be NULL); the result is the
- *   same bit for bit.
+ * packed: NULL, or the weights of all blocks prepared by rmx_pack_weights for this handle:
+ *   W1 and W2 (dense bf16 handles whose D and k*D are multiples of 32), or We1 and We2
+ *   (Sparse-MoE handles whose D and h are multiples of 384).  When set, the forward reads
+ *   those weights from it (W1 and W2, or We1 and We2, are then unused and may be NULL);
+ *   the result is the same bit for bit.
  * packed_mxfp8: NULL, or W1 and W2 of all blocks prepared by rmx_pack_weights_mxfp8; when
  *   set (and packed is NULL) the forward runs the MXFP8 inference variant (see there).
  * Wq, Wk, Wv [L, D, D]: the self-attention projections of RMX_ROUTING_ATTENTION handles
@@ -164,13 +165,17 @@ rmx_status rmx_token_mix(const void* X, void* Y, int64_t B, int32_t T, int32_t D
                          int32_t dtype, void* stream);
 
 /* Weights prepared once for the matrix cores.  rmx_packed_weights_bytes gives the size of
- * the prepared copy of W1 and W2 of all L blocks for this handle, or 0 when the handle has
- * no such path (fp32, Sparse-MoE, or D or k*D not a multiple of 32).  rmx_pack_weights
- * reads w->W1 and w->W2 (device, [L, T, D, kD] and [L, T, kD, D]) and writes the copy to
- * `packed` (device, `bytes` >= rmx_packed_weights_bytes(h), 16-byte aligned), enqueued on
- * `stream`: each token's W^T in blocks of 256 rows x 32 columns, so that a K step of a
- * 256-column weight tile is one contiguous 16 KB.  Pass it as rmx_weights.packed.  The
- * caller owns the buffer; it stays valid while W1 and W2 are unchanged. */
+ * the prepared copy of W1 and W2 (dense handles) or We1 and We2 (Sparse-MoE handles) of all
+ * L blocks for this handle, or 0 when the handle has no such path (fp32; dense with D or
+ * k*D not a multiple of 32; Sparse-MoE with D or moe_hidden not a multiple of 384).
+ * rmx_pack_weights reads w->W1 and w->W2 (device, [L, T, D, kD] and [L, T, kD, D]), or
+ * w->We1 and w->We2 ([L, T, E, D, h] and [L, T, E, h, D]), and writes the copy to `packed`
+ * (device, `bytes` >= rmx_packed_weights_bytes(h), 16-byte aligned, not overlapping the
+ * sources), enqueued on `stream`: each token's (each expert's) W^T in blocks of 256 rows x
+ * 32 columns, so that a K step of a 256-column weight tile is one contiguous 16 KB.  Pass it
+ * as rmx_weights.packed.  The caller owns the buffer; it stays valid while the source
+ * weights are unchanged.  Errors: INVALID_ARG for a short or overlapping buffer, a wrong L
+ * or a pointer off the handle's device; UNSUPPORTED where the size above is 0. */
 size_t rmx_packed_weights_bytes(const rmx_handle* h);
 rmx_status rmx_pack_weights(rmx_handle* h, const rmx_weights* w, int32_t L, void* packed, size_t bytes,
                             void* stream);

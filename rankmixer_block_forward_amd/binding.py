@@ -202,14 +202,16 @@ class Handle:
         return int(self._lib.rmx_packed_weights_bytes(self._h))
 
     def pack_weights(self, weights: dict, stream=None):
-        """W1 and W2 of all blocks prepared for the matrix cores (rmx_pack_weights): a device
-        tensor to pass as weights["packed"]; the forward then reads the weights from it."""
+        """W1 and W2 (We1 and We2 for a Sparse-MoE handle) of all blocks prepared for the
+        matrix cores (rmx_pack_weights): a device tensor to pass as weights["packed"]; the
+        forward then reads those weights from it."""
         import torch
         nbytes = self.packed_weights_bytes()
         if nbytes == 0:
             raise RmxError(RMX_ERR_UNSUPPORTED, "this handle has no prepared-weights path")
         packed = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
-        ws = self._weights({"W1": weights["W1"], "W2": weights["W2"]})
+        names = ("We1", "We2") if self.cfg.moe_experts > 0 else ("W1", "W2")
+        ws = self._weights({n: weights[n] for n in names})
         _check(self._lib.rmx_pack_weights(self._h, ctypes.byref(ws), self.cfg.L, _ptr(packed, "packed"), nbytes,
                                           _stream(stream)), self._h)
         return packed

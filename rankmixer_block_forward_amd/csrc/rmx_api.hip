@@ -52,6 +52,9 @@ struct rmx_handle {
   // (codes [T, pk_rows(max_batch), D] bytes, then their scales, 1/32 of that), and H in
   // MXFP8 in the H buffer (codes, then scales)
   bool mx_capable = false;
+  // Sparse-MoE bf16 handles with D and moe_hidden multiples of 384 can run their expert
+  // products on prepared expert weights (each expert's W^T packed, 256 x 384 tiles)
+  bool moe_pk_capable = false;
   void* S8 = nullptr;
   // Sparse-MoE workspace (moe_experts > 0); G = T * E groups, R = G * max_batch rows
   float* moe_g = nullptr;        // [G, max_batch]
@@ -188,8 +191,8 @@ rmx_status validate_config(const rmx_config* c) {
     if (moe_gate_lds_bytes(c->D, E) > MOE_MAX_GATE_LDS)
       return fail(nullptr, RMX_ERR_UNSUPPORTED, "MoE router weights of one token exceed %zu bytes of LDS",
                   size_t(MOE_MAX_GATE_LDS));
-    if (!gemm_moe_supported(h, c->D, int64_t(c->T) * c->max_batch) ||
-        !gemm_moe_supported(c->D, h, c->max_batch))
+    if (!gemm_moe_supported(h, c->D, int64_t(c->T) * c->max_batch, false) ||
+        !gemm_moe_supported(c->D, h, c->max_batch, false))
       return fail(nullptr, RMX_ERR_UNSUPPORTED, "MoE GEMMs need D %% 32 == 0, moe_hidden %% 32 == 0 and slices < 2 GiB");
   }
   if (c->routing != RMX_ROUTING_MIX && c->routing != RMX_ROUTING_ATTENTION)
@@ -413,6 +416,10 @@ rmx_status rmx_create(const rmx_config* cfg, rmx_handle** out_handle) {
   h->pk_capable = cfg->moe_experts == 0 && cfg->dtype == RMX_BF16 && cfg->D % 32 == 0 &&
                   (int64_t(cfg->k) * cfg->D) % 32 == 0;
   h->mx_capable = h->pk_capable && cfg->D % 64 == 0 && (int64_t(cfg->k) * cfg->D) % 64 == 0;
+  h->moe_pk_capable = cfg->moe_experts > 0 && cfg->dtype == RMX_BF16 && cfg->D % 384 == 0 &&
+                      cfg->moe_hidden % 384 == 0 &&
+                      gemm_moe_supported(cfg->moe_hidden, cfg->D, int64_t(cfg->T) * cfg->max_batch, true) &&
+                      gemm_moe_supported(cfg->D, cfg->moe_hidden, cfg->max_batch, true);
   const size_t prow = h->pk_capable ? size_t(cfg->T) * size_t(pk_rows(cfg->max_batch)) : rows;
   if (rows > 0) {
     alloc(&h->S, prow * cfg->D * esz);
@@ -509,10 +516,17 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
   if (train && (st = check_dev(h, saved, rmx_saved_bytes(h, B), dev, "saved")) != RMX_OK) return st;
   const size_t E = size_t(c.moe_experts), hid = size_t(c.moe_hidden);
   if (moe) {
-    if (w->packed || w->packed_mxfp8) return fail(h, RMX_ERR_UNSUPPORTED, "prepared weights are for dense handles");
+    if (w->packed_mxfp8) return fail(h, RMX_ERR_UNSUPPORTED, "MXFP8 weights are for dense handles");
     if ((st = check_dev(h, w->Wg, Ls * T * D * E * esz, dev, "Wg")) != RMX_OK) return st;
-    if ((st = check_dev(h, w->We1, Ls * T * E * D * hid * esz, dev, "We1")) != RMX_OK) return st;
-    if ((st = check_dev(h, w->We2, Ls * T * E * hid * D * esz, dev, "We2")) != RMX_OK) return st;
+    if (w->packed) {
+      if (!h->moe_pk_capable)
+        return fail(h, RMX_ERR_UNSUPPORTED,
+                    "prepared expert weights need a bf16 handle with D and moe_hidden multiples of 384");
+      if ((st = check_dev(h, w->packed, rmx_packed_weights_bytes(h), dev, "packed")) != RMX_OK) return st;
+    } else {
+      if ((st = check_dev(h, w->We1, Ls * T * E * D * hid * esz, dev, "We1")) != RMX_OK) return st;
+      if ((st = check_dev(h, w->We2, Ls * T * E * hid * D * esz, dev, "We2")) != RMX_OK) return st;
+    }
     if ((st = check_dev_opt(h, w->be1, Ls * T * E * hid * esz, dev, "be1")) != RMX_OK) return st;
     if ((st = check_dev_opt(h, w->be2, Ls * T * E * D * esz, dev, "be2")) != RMX_OK) return st;
     if ((st = check_dev_opt(h, gate_out, Ls * size_t(B) * T * E * 4, dev, "gate_out")) != RMX_OK) return st;
@@ -577,6 +591,9 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
   hipError_t e = hipSuccess;
   const int Bi = int(B);
   const bool pk = !moe && w->packed != nullptr;
+  const bool moe_pk = moe && w->packed != nullptr;
+  // prepared expert weights of block n: the T*E groups' We1^T, then their We2^T (elements)
+  const size_t pk_we1 = T * E * size_t(pk_rows(int64_t(hid))) * D, pk_we2 = T * E * size_t(pk_rows(int64_t(D))) * hid;
   const bool mx = !moe && !pk && w->packed_mxfp8 != nullptr;
   // prepared weights of block n: W1^T then W2^T, packed (elements)
   const size_t pk_w1 = T * size_t(pk_rows(int64_t(kD))) * D, pk_w2 = T * size_t(pk_rows(int64_t(D))) * kD;
@@ -676,9 +693,11 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
       ma.E = c.moe_experts;
       ma.nchunk = (Bi + 63) / 64;
       if ((e = run_moe_route(h, s, ma)) != hipSuccess) break;
+      const uint16_t* pkw = moe_pk ? static_cast<const uint16_t*>(w->packed) + size_t(n) * (pk_we1 + pk_we2) : nullptr;
       GemmArgs m1{};
       m1.A = h->S;
-      m1.W = at(w->We1, size_t(n) * T * E * D * hid);
+      m1.W = moe_pk ? static_cast<const void*>(pkw) : at(w->We1, size_t(n) * T * E * D * hid);
+      m1.packed = moe_pk ? 1 : 0;
       m1.bias = at(w->be1, size_t(n) * T * E * hid);
       m1.C = h->moe_hidden;
       m1.G = int(T * E);
@@ -691,7 +710,8 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
       if ((e = run_moe_gemm(h, s, EPI_MOE1, m1)) != hipSuccess) break;
       GemmArgs m2{};
       m2.A = h->moe_hidden;
-      m2.W = at(w->We2, size_t(n) * T * E * hid * D);
+      m2.W = moe_pk ? static_cast<const void*>(pkw + pk_we1) : at(w->We2, size_t(n) * T * E * hid * D);
+      m2.packed = moe_pk ? 1 : 0;
       m2.bias = at(w->be2, size_t(n) * T * E * D);
       m2.C = h->moe_out;
       m2.G = int(T * E);
@@ -1030,8 +1050,13 @@ rmx_status rmx_block_backward(rmx_handle* h, const void* X, int64_t B, const rmx
 }
 
 size_t rmx_packed_weights_bytes(const rmx_handle* h) {
-  if (!h || !h->pk_capable) return 0;
+  if (!h) return 0;
   const rmx_config& c = h->cfg;
+  if (h->moe_pk_capable) {
+    const size_t G = size_t(c.T) * size_t(c.moe_experts), D = c.D, hid = c.moe_hidden;
+    return size_t(c.L) * G * (size_t(pk_rows(int64_t(hid))) * D + size_t(pk_rows(int64_t(D))) * hid) * 2;
+  }
+  if (!h->pk_capable) return 0;
   const size_t T = c.T, D = c.D, kD = size_t(c.k) * c.D;
   const size_t per_layer = T * size_t(pk_rows(int64_t(kD))) * D + T * size_t(pk_rows(int64_t(D))) * kD;
   return size_t(c.L) * per_layer * 2;
@@ -1044,7 +1069,10 @@ rmx_status rmx_pack_weights(rmx_handle* h, const rmx_weights* w, int32_t L, void
   const rmx_config& c = h->cfg;
   if (!w) return fail(h, RMX_ERR_INVALID_ARG, "weights is NULL");
   if (L != c.L) return fail(h, RMX_ERR_INVALID_ARG, "L=%d but the handle was created with L=%d", L, c.L);
-  if (!h->pk_capable)
+  if (c.moe_experts > 0 && !h->moe_pk_capable)
+    return fail(h, RMX_ERR_UNSUPPORTED,
+                "prepared expert weights need a bf16 handle with D and moe_hidden multiples of 384");
+  if (c.moe_experts == 0 && !h->pk_capable)
     return fail(h, RMX_ERR_UNSUPPORTED, "prepared weights need a dense bf16 handle with D and k*D multiples of 32");
   const size_t need = rmx_packed_weights_bytes(h);
   if (bytes < need) return fail(h, RMX_ERR_INVALID_ARG, "packed buffer of %zu bytes, %zu needed", bytes, need);
@@ -1055,10 +1083,34 @@ rmx_status rmx_pack_weights(rmx_handle* h, const rmx_weights* w, int32_t L, void
   }
   const size_t T = c.T, D = c.D, kD = size_t(c.k) * c.D, Ls = c.L;
   rmx_status st;
+  const uintptr_t pb = reinterpret_cast<uintptr_t>(packed);
+  if (c.moe_experts > 0) {
+    // each expert's We1 [D, hid] and We2 [hid, D], groups t * E + e, as the dense W1 / W2
+    const size_t G = T * size_t(c.moe_experts), hid = c.moe_hidden;
+    const size_t src = Ls * G * D * hid * 2;
+    if ((st = check_dev(h, w->We1, src, dev, "We1")) != RMX_OK) return st;
+    if ((st = check_dev(h, w->We2, src, dev, "We2")) != RMX_OK) return st;
+    if ((st = check_dev(h, packed, need, dev, "packed")) != RMX_OK) return st;
+    for (const void* p : {w->We1, w->We2}) {
+      const uintptr_t sb = reinterpret_cast<uintptr_t>(p);
+      if (pb < sb + src && sb < pb + need) return fail(h, RMX_ERR_INVALID_ARG, "packed overlaps We1 or We2");
+    }
+    const size_t pk1 = G * size_t(pk_rows(int64_t(hid))) * D, pk2 = G * size_t(pk_rows(int64_t(D))) * hid;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (size_t n = 0; n < Ls; ++n) {
+      uint16_t* dst = static_cast<uint16_t*>(packed) + n * (pk1 + pk2);
+      hipError_t e = launch_pack_weights(static_cast<const uint16_t*>(w->We1) + n * G * D * hid, dst, int(G), c.D,
+                                         int(hid), s);
+      if (e == hipSuccess)
+        e = launch_pack_weights(static_cast<const uint16_t*>(w->We2) + n * G * hid * D, dst + pk1, int(G), int(hid),
+                                c.D, s);
+      if (e != hipSuccess) return fail(h, RMX_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return RMX_OK;
+  }
   if ((st = check_dev(h, w->W1, Ls * T * D * kD * 2, dev, "W1")) != RMX_OK) return st;
   if ((st = check_dev(h, w->W2, Ls * T * kD * D * 2, dev, "W2")) != RMX_OK) return st;
   if ((st = check_dev(h, packed, need, dev, "packed")) != RMX_OK) return st;
-  const uintptr_t pb = reinterpret_cast<uintptr_t>(packed);
   for (const void* src : {w->W1, w->W2}) {
     const uintptr_t sb = reinterpret_cast<uintptr_t>(src);
     if (pb < sb + Ls * T * D * kD * 2 && sb < pb + need)

@@ -643,9 +643,14 @@ constexpr int LD6 = 2 * 32 + 4;                             // epilogue staging 
 // takes pieces w, w + 4, ...: 4 of A and 6 of W^T).  W^T half-block H = 3 nt + (piece / 8)
 // of the token is rows 128 H .. 128 H + 127: block H / 2, half H % 2.  Row r of the stage's
 // W^T part is tile column r; the chunk swizzle depends on r % 8, which a half-block keeps.
+// GATHER_A: A is not packed but gathered from row-major rows; offA[c] is this lane's byte
+// offset of piece wave + 4 c at K step 0 (the 16 bytes that belong at the lane's place in
+// the packed layout), and a K step advances it by 64 bytes.
+template <bool GATHER_A>
 __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (&accV)[4][2],
                                               __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rW, lds_u8* smem,
-                                              uint32_t lds0, int K, int nt, int wave, int lane) {
+                                              uint32_t lds0, int K, int nt, int wave, int lane,
+                                              const uint32_t (&offA)[4]) {
   const int nk = K / BK;
   uint32_t voffW[6];
 #pragma unroll
@@ -662,8 +667,11 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
     const uint32_t sbase = lds0 + uint32_t(stage) * STAGE6_BYTES;
     if (c < 4) {
       const uint32_t piece = uint32_t(wave + 4 * c);
-      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), piece * 1024u + uint32_t(lane) * 16u, rA,
-                  kt * 16384);
+      if constexpr (GATHER_A)
+        copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), offA[c], rA, kt * BK * 2);
+      else
+        copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), piece * 1024u + uint32_t(lane) * 16u, rA,
+                    kt * 16384);
     } else {
       const uint32_t q = uint32_t(wave + 4 * (c - 4));
       copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + A_STAGE_BYTES + q * 1024u), voffW[c - 4], rW, kt * 16384);
@@ -767,19 +775,20 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
   __syncthreads();
 }
 
-// GELU (packed H out) or residual (packed S in, fp32 Y out) epilogue of a 256 x 384 tile, the
-// arithmetic of tile_epilogue: per row block i of the wave and group of two column blocks,
-// 32 rows x 64 columns are staged through LDS so that each lane then owns 8 consecutive
-// columns of one row (8 lanes per row, 8 rows per pass).
-template <int EPI>
+// Epilogue of a 256 x 384 tile, the arithmetic of tile_epilogue: GELU (packed H out),
+// residual (packed S in, fp32 Y out), or the Sparse-MoE ones (GELU to the compacted hidden
+// rows; gate times result to the compacted output rows).  Per row block i of the wave and
+// group of two column blocks, 32 rows x 64 columns are staged through LDS so that each lane
+// then owns 8 consecutive columns of one row (8 lanes per row, 8 rows per pass).
+// row_of(r) maps tile row r to its output row, or -1 where the tile runs past the rows.
+template <int EPI, typename RowOf>
 __device__ __forceinline__ void tile_epilogue6(const f32x16_t (&accA)[4][4], const f32x16_t (&accV)[4][2],
-                                               float* smem_f, const GemmArgs& p, int g, int m0, int n0, int wave,
-                                               int lane) {
+                                               float* smem_f, const GemmArgs& p, int g, const bf16_t* bias_g,
+                                               int n0, int wave, int lane, RowOf row_of) {
   const int M = p.M, N = p.N;
   const int wrow0 = (wave >> 1) * 128, wcol0 = (wave & 1) * 192;
   float* st = smem_f + wave * 32 * LD6;
   const int col8 = (lane & 7) * 8;
-  const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
   float bias[3][8];
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
@@ -806,25 +815,35 @@ __device__ __forceinline__ void tile_epilogue6(const f32x16_t (&accA)[4][4], con
 #pragma unroll
       for (int pass = 0; pass < 4; ++pass) {
         const int row = pass * 8 + (lane >> 3);
-        const int m = m0 + wrow0 + i * 32 + row;
+        const int m = row_of(wrow0 + i * 32 + row);
         const int n = n0 + wcol0 + s * 64 + col8;
         float v[8];
         const float4 x0 = *reinterpret_cast<const float4*>(st + row * LD6 + col8);
         const float4 x1 = *reinterpret_cast<const float4*>(st + row * LD6 + col8 + 4);
         v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
         v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-        if (m < M && n < N) {
-          const size_t pko = size_t(g) * size_t(pk_rows(M)) * N + pk_off(m, n, N);
+        if (m >= 0 && n < N) {
           if constexpr (EPI == EPI_GELU) {
+            const size_t pko = size_t(g) * size_t(pk_rows(M)) * N + pk_off(m, n, N);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[s][e]);
             store8(static_cast<bf16_t*>(p.C) + pko, v);
-          } else {
+          } else if constexpr (EPI == EPI_RESID) {
+            const size_t pko = size_t(g) * size_t(pk_rows(M)) * N + pk_off(m, n, N);
             float rr[8];
             load8(static_cast<const bf16_t*>(p.R) + pko, rr);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = v[e] + bias[s][e] + rr[e];
             store8(static_cast<float*>(p.C) + size_t(g) * size_t(p.sc) + size_t(m) * size_t(p.ldc) + n, v);
+          } else if constexpr (EPI == EPI_MOE1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[s][e]);
+            store8(static_cast<bf16_t*>(p.C) + size_t(m) * size_t(N) + n, v);
+          } else {
+            const float gv = p.row_gate[m];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = gv * (v[e] + bias[s][e]);
+            store8(static_cast<float*>(p.C) + size_t(m) * size_t(N) + n, v);
           }
         }
       }
@@ -860,8 +879,81 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384(GemmArgs 
   const __amdgpu_buffer_rsrc_t rW =
       make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * (size_t(wbytes) / 2), wbytes);
   f32x16_t accA[4][4], accV[4][2];
-  mfma_tile_pk6(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane);
-  tile_epilogue6<EPI>(accA, accV, reinterpret_cast<float*>(smem_g), p, g, mt * BM, nt * BN6, wave, lane);
+  const uint32_t no_gather[4] = {0u, 0u, 0u, 0u};
+  mfma_tile_pk6<false>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, no_gather);
+  const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
+  const int m0 = mt * BM;
+  tile_epilogue6<EPI>(accA, accV, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN6, wave, lane,
+                      [&](int r) { return m0 + r < M ? m0 + r : -1; });
+}
+
+// Sparse-MoE grouped GEMM on prepared expert weights with 256 x 384 tiles: the persistent
+// tile walk of gemm_bf16_moe (same device-built tile table, each XCD a contiguous range of
+// tiles, row tiles fastest inside a group), the K loop of gemm_bf16_mfma_n384 with A gathered
+// from row-major rows, and tile_epilogue6.  W is group g's W^T in the packed layout
+// (pk_rows(N) x K, N % 384 == 0).  Same products in the same order as gemm_bf16_moe, so
+// the two give the same bits.
+template <int EPI>
+__global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_moe_n384(GemmArgs p) {
+  static_assert(EPI == EPI_MOE1 || EPI == EPI_MOE2, "the Sparse-MoE epilogues");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[PK6_NS * STAGE6_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_g;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int N = p.N, K = p.K, G = p.G;
+  const int nNt = N / BN6;
+  const int total = p.tile_start[G] * nNt;
+  const int per_xcd = int(gridDim.x) / NUM_XCD;  // gridDim.x is a multiple of NUM_XCD
+  const int xcd = int(blockIdx.x) % NUM_XCD, slot = int(blockIdx.x) / NUM_XCD;
+  const int chunk = (total + NUM_XCD - 1) / NUM_XCD;
+  const int lo = xcd * chunk, hi = min(total, lo + chunk);
+  const uint32_t blk = uint32_t(K / BK) * 16384u;
+  const uint32_t wbytes = uint32_t(pk_rows(N) / 256) * blk;
+
+  for (int tile = lo + slot; tile < hi; tile += per_xcd) {
+    // group of this tile: the last g with tile_start[g] * nNt <= tile
+    int glo = 0, ghi = G;  // invariant: tile_start[glo]*nNt <= tile < tile_start[ghi]*nNt
+    while (ghi - glo > 1) {
+      const int mid = (glo + ghi) >> 1;
+      if (p.tile_start[mid] * nNt <= tile) glo = mid; else ghi = mid;
+    }
+    const int g = glo;
+    const int mtiles = p.tile_start[g + 1] - p.tile_start[g];
+    const int local = tile - p.tile_start[g] * nNt;
+    const int nt = local / mtiles, mt = local - nt * mtiles;
+    const int row0 = p.group_start[g], rows = p.group_start[g + 1] - row0;
+    const int m0 = mt * BM;
+    const __amdgpu_buffer_rsrc_t rW =
+        make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * (size_t(wbytes) / 2), wbytes);
+    // A rows: S through the row list (layer 1) or the group's compacted hidden rows (layer 2);
+    // rows past the group read as zeros (offset past the descriptor's end)
+    const uint32_t row_bytes = uint32_t(K) * 2u;
+    const uint32_t bytesA = uint32_t(EPI == EPI_MOE1 ? p.a_rows : rows) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rA =
+        EPI == EPI_MOE1 ? make_rsrc(p.A, bytesA)
+                        : make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(row0) * K, bytesA);
+    uint32_t offA[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      // piece wave + 4 c is tile rows 16 (wave + 4 c) .. + 15; lane l fills slot l % 4 of row
+      // l / 4, which holds 16-byte chunk (l % 4) ^ pk_swz(row) of that row's 64-byte K step
+      const int r = 16 * (wave + 4 * c) + (lane >> 2);
+      const uint32_t chunk16 = uint32_t((lane & 3) ^ pk_swz(r)) * 16u;
+      if (m0 + r < rows) {
+        const uint32_t src = EPI == EPI_MOE1 ? uint32_t(p.src_row[row0 + m0 + r]) : uint32_t(m0 + r);
+        offA[c] = src * row_bytes + chunk16;
+      } else {
+        offA[c] = bytesA;
+      }
+    }
+    f32x16_t accA[4][4], accV[4][2];
+    mfma_tile_pk6<true>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA);
+    const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
+    tile_epilogue6<EPI>(accA, accV, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN6, wave, lane,
+                        [&](int r) { return m0 + r < rows ? row0 + m0 + r : -1; });
+    // every wave is done with its staging rows before the next tile's copies reuse the ring
+    __syncthreads();
+  }
 }
 
 // ------------------------------------------------------------- MXFP8 products
@@ -1389,8 +1481,9 @@ bool gemm_uses_mfma(int dtype, int M, int N, int K, int64_t lda, int at, int bt)
 
 hipError_t gemm_init() { return hipSuccess; }
 
-bool gemm_moe_supported(int N, int K, int64_t a_rows) {
+bool gemm_moe_supported(int N, int K, int64_t a_rows, bool packed) {
   const uint64_t lim = uint64_t(1) << 31;
+  if (packed && (N % BN6 != 0 || uint64_t(pk_rows(N)) * K * 2 >= lim)) return false;
   return K % BK == 0 && N % 8 == 0 && uint64_t(a_rows) * K * 2 < lim && uint64_t(K) * N * 2 < lim &&
          uint64_t(a_rows) * N * 2 < lim;
 }
@@ -1400,15 +1493,21 @@ hipError_t launch_gemm_moe(int epi, const GemmArgs& args, hipStream_t stream) {
   GemmArgs a = args;  // outputs are the compacted rows [rows, N]
   a.ldc = a.N;
   a.sc = 0;
-  a.packed = 0;
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int grid = ((cus + NUM_XCD - 1) / NUM_XCD) * NUM_XCD;  // one workgroup per CU, whole XCDs
-  if (epi == EPI_MOE1)
+  if (a.packed) {
+    if (a.N % BN6 != 0) return hipErrorInvalidValue;
+    if (epi == EPI_MOE1)
+      hipLaunchKernelGGL((gemm_bf16_moe_n384<EPI_MOE1>), dim3(grid), dim3(MFMA_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_moe_n384<EPI_MOE2>), dim3(grid), dim3(MFMA_THREADS), 0, stream, a);
+  } else if (epi == EPI_MOE1) {
     hipLaunchKernelGGL((gemm_bf16_moe<EPI_MOE1>), dim3(grid), dim3(MFMA_THREADS), 0, stream, a);
-  else
+  } else {
     hipLaunchKernelGGL((gemm_bf16_moe<EPI_MOE2>), dim3(grid), dim3(MFMA_THREADS), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -224,7 +224,8 @@ constexpr int GEMM_SMALL_M = 128;
 bool gemm_uses_mfma(int dtype, int M, int N, int K, int64_t lda = 0, int at = 0, int bt = 0);
 // Sparse-MoE grouped GEMM launch (bf16 MFMA only); `max_rows` bounds every group's rows.
 hipError_t launch_gemm_moe(int epi, const GemmArgs& a, hipStream_t stream);
-bool gemm_moe_supported(int N, int K, int64_t a_rows);
+// packed: W is the groups' W^T in the packed operand layout (256 x 384 tiles, N % 384 == 0).
+bool gemm_moe_supported(int N, int K, int64_t a_rows, bool packed);
 hipError_t gemm_init();
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t stream);
 // True when launch_gemm(dtype, epi, a) runs a matrix-core kernel that writes a.colsum.

@@ -287,11 +287,16 @@ def test_profile_counts_launches():
 
 # ------------------------------------------------------------------ Sparse-MoE
 
-def _run_moe(cfg, inp, with_xl=True):
+def _run_moe(cfg, inp, with_xl=True, packed=False):
+    """The MoE forward; packed: on expert weights prepared by rmx_pack_weights (We1 and We2
+    are then withheld, so the forward must read the prepared copy)."""
     rmx = _rmx()
     X, w = rmx.upload(inp)
     B = X.shape[0]
     with rmx.Handle.for_config(cfg, max_batch=B) as h:
+        if packed:
+            w["packed"] = h.pack_weights(w)
+            w["We1"] = w["We2"] = None
         out = torch.full((B, cfg.D), float("nan"), dtype=torch.float32, device="cuda")
         xl = torch.full_like(X, float("nan")) if with_xl else None
         gates = torch.full((cfg.L, B, cfg.T, cfg.E), float("nan"), dtype=torch.float32, device="cuda")
@@ -323,6 +328,49 @@ def test_moe_shapes(B, T, D, E, h, L):
     _check_gates(g, g_ref, f"moe {B}x{T}x{D} E{E}")
 
 
+@pytest.mark.parametrize("B,T,D,E,h,L", [(100, 2, 384, 4, 384, 2), (300, 4, 384, 3, 768, 1), (1, 2, 768, 2, 384, 1),
+                                         (700, 2, 384, 8, 1152, 1)])
+def test_moe_prepared_weights_bit_identical(B, T, D, E, h, L):
+    """Prepared expert weights (256 x 384 tiles, A rows gathered into the packed LDS layout)
+    give the bits of the row-major expert products: same MFMA inputs in the same K order.
+    Group row counts here are partial tiles, single tiles and several tiles with a tail."""
+    cfg = synth.Config("moe-pk", B=B, T=T, D=D, k=2, L=L, dtype="bf16", E=E, moe_hidden=h, bias_std=0.02)
+    inp = synth.make_inputs(cfg, seed=B + 7 * E)
+    o1, xl1, g1 = _run_moe(cfg, inp)
+    o2, xl2, g2 = _run_moe(cfg, inp, packed=True)
+    assert np.array_equal(g1, g2)
+    assert np.array_equal(o1, o2) and np.array_equal(xl1, xl2)
+    rows = sample_rows(B, 16)
+    sub = synth.Inputs(cfg, inp.X[rows], inp.W1, inp.b1, inp.W2, inp.b2, inp.ln1_g, inp.ln1_b,
+                       inp.ln2_g, inp.ln2_b, inp.moe)
+    o_ref, xl_ref, g_ref = oracle.forward(sub.X, sub.layers(), cfg.eps)
+    check(cfg, o2[rows], xl2[rows], o_ref, xl_ref, f"moe prepared {B}x{T}x{D} E{E} h{h} L{L}")
+    _check_gates(g2[:, rows], g_ref, f"moe prepared {B}x{T}x{D} E{E}")
+
+
+def test_moe_prepared_weights_size_and_rejection():
+    rmx = _rmx()
+    from rankmixer_block_forward_amd import binding
+    cfg = synth.Config("moe-pk", B=8, T=2, D=384, k=2, L=2, dtype="bf16", E=3, moe_hidden=384)
+    with rmx.Handle.for_config(cfg, max_batch=8) as h:
+        # per block and expert: We1^T (h = 384 rows of D) and We2^T (D = 384 rows of h), each
+        # padded to 512 rows (whole 256-row blocks), bf16
+        assert h.packed_weights_bytes() == 2 * 2 * 3 * (512 * 384 + 512 * 384) * 2
+        X, w = rmx.upload(synth.make_inputs(cfg, seed=1))
+        fake = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+        with pytest.raises(binding.RmxError):  # MXFP8 weights are a dense-only variant
+            h.forward(X, dict(w, packed_mxfp8=fake))
+    odd = synth.Config("moe-odd", B=8, T=2, D=384, k=2, L=1, dtype="bf16", E=2, moe_hidden=256)
+    with rmx.Handle.for_config(odd, max_batch=8) as h:
+        assert h.packed_weights_bytes() == 0
+        X, w = rmx.upload(synth.make_inputs(odd, seed=1))
+        with pytest.raises(binding.RmxError):
+            h.pack_weights(w)
+        fake = torch.empty(1 << 20, dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(binding.RmxError):
+            h.forward(X, dict(w, packed=fake))
+
+
 def test_moe_zero_router_is_ffn_free_block():
     cfg = synth.Config("moe0", B=64, T=4, D=64, k=2, L=2, dtype="bf16", E=4, moe_hidden=64)
     inp = synth.make_inputs(cfg, seed=3)
@@ -344,3 +392,6 @@ def test_rankmixer_1b_moe_full_size():
     o_ref, _, g_ref = oracle.forward(sub.X, sub.layers(), cfg.eps)
     check(cfg, o[rows], None, o_ref, None, "1B MoE B=2048")
     _check_gates(g[:, rows], g_ref, "1B MoE B=2048")
+    # the benchmark's launch: prepared expert weights, same bits
+    o2, _, g2 = _run_moe(cfg, inp, with_xl=False, packed=True)
+    assert np.array_equal(g, g2) and np.array_equal(o, o2)
