@@ -645,8 +645,11 @@ constexpr int LD6 = 2 * 32 + 4;                             // epilogue staging 
 // W^T part is tile column r; the chunk swizzle depends on r % 8, which a half-block keeps.
 // GATHER_A: A is not packed but gathered from row-major rows; offA[c] is this lane's byte
 // offset of piece wave + 4 c at K step 0 (the 16 bytes that belong at the lane's place in
-// the packed layout), and a K step advances it by 64 bytes.
-template <bool GATHER_A>
+// the packed layout), and a K step advances it by 64 bytes.  NI < 4: only the wave's first
+// NI row blocks hold rows (a tile past the end of its rows); the others are neither read
+// nor multiplied and their accumulators stay zero.  Copies and barriers are the same for
+// every NI, so the waves of one workgroup may run different NI.
+template <bool GATHER_A, int NI>
 __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (&accV)[4][2],
                                               __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rW, lds_u8* smem,
                                               uint32_t lds0, int K, int nt, int wave, int lane,
@@ -694,13 +697,14 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
   u32x4_t a0[4], a1[4], b[6];
   auto read_a = [&](u32x4_t (&a)[4], const lds_u8* sp, int kk) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const lds_u32x4*>(sp + aoff[kk] + i * 2048);
+    for (int i = 0; i < NI; ++i) a[i] = *reinterpret_cast<const lds_u32x4*>(sp + aoff[kk] + i * 2048);
   };
   auto read_b = [&](const lds_u8* sp, int kk, int j) {
     if (j >= 4) asm volatile("s_nop 7" ::: "memory");  // an assembly MFMA read b[j] just before
     b[j] = *reinterpret_cast<const lds_u32x4*>(sp + boff[kk] + j * 2048);
   };
   auto mm = [&](const u32x4_t (&a)[4], int i, int j) {
+    if (i >= NI) return;
     if (j < 4)
       accA[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[j]),
                                                            __builtin_bit_cast(bf16x8_t, a[i]), accA[i][j], 0, 0, 0);
@@ -784,7 +788,7 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
 template <int EPI, typename RowOf>
 __device__ __forceinline__ void tile_epilogue6(const f32x16_t (&accA)[4][4], const f32x16_t (&accV)[4][2],
                                                float* smem_f, const GemmArgs& p, int g, const bf16_t* bias_g,
-                                               int n0, int wave, int lane, RowOf row_of) {
+                                               int n0, int wave, int lane, RowOf row_of, int nib = 4) {
   const int M = p.M, N = p.N;
   const int wrow0 = (wave >> 1) * 128, wcol0 = (wave & 1) * 192;
   float* st = smem_f + wave * 32 * LD6;
@@ -798,7 +802,8 @@ __device__ __forceinline__ void tile_epilogue6(const f32x16_t (&accA)[4][4], con
     if (bias_g && n < N) load8(bias_g + n, bias[s]);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    if (i >= nib) break;  // row blocks past the rows (wave-uniform)
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
 #pragma unroll
@@ -849,6 +854,7 @@ __device__ __forceinline__ void tile_epilogue6(const f32x16_t (&accA)[4][4], con
       }
       asm volatile("" ::: "memory");
     }
+  }
 }
 
 // Dense per-token product on packed operands with 256 x 384 tiles: G * ceil(M/256) * N/384
@@ -880,7 +886,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384(GemmArgs 
       make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * (size_t(wbytes) / 2), wbytes);
   f32x16_t accA[4][4], accV[4][2];
   const uint32_t no_gather[4] = {0u, 0u, 0u, 0u};
-  mfma_tile_pk6<false>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, no_gather);
+  mfma_tile_pk6<false, 4>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, no_gather);
   const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
   const int m0 = mt * BM;
   tile_epilogue6<EPI>(accA, accV, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN6, wave, lane,
@@ -946,11 +952,20 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_moe_n384(GemmArgs p
         offA[c] = bytesA;
       }
     }
+    // row blocks of this wave (32 rows each) that hold rows of the group: 4 except in a
+    // group's last row tile, where the MFMA work past the rows is skipped
+    const int nib = __builtin_amdgcn_readfirstlane(max(0, min(4, (rows - m0 - (wave >> 1) * 128 + 31) / 32)));
     f32x16_t accA[4][4], accV[4][2];
-    mfma_tile_pk6<true>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA);
+    switch (nib) {
+      case 4: mfma_tile_pk6<true, 4>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+      case 3: mfma_tile_pk6<true, 3>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+      case 2: mfma_tile_pk6<true, 2>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+      case 1: mfma_tile_pk6<true, 1>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+      default: mfma_tile_pk6<true, 0>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+    }
     const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
     tile_epilogue6<EPI>(accA, accV, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN6, wave, lane,
-                        [&](int r) { return m0 + r < rows ? row0 + m0 + r : -1; });
+                        [&](int r) { return m0 + r < rows ? row0 + m0 + r : -1; }, nib);
     // every wave is done with its staging rows before the next tile's copies reuse the ring
     __syncthreads();
   }
