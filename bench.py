@@ -244,20 +244,50 @@ def blas_threads():
         return os.cpu_count() or 1
 
 
-def cpu_baseline(cfg, n):
-    """The fp64 oracle, as it stands, on n samples of the same workload."""
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(cfg, n, single_thread=True):
+    """The fp64 oracle, as it stands, on n samples of the same workload with the BLAS
+    threads the host gives it; with single_thread, also on n/16 samples with one thread."""
     import numpy as np
     import oracle
     from rankmixer_block_forward_amd import synth
     threads = blas_threads()
-    inp = synth.make_inputs(cfg.with_(B=n), seed=0)
-    t0 = time.perf_counter()
-    o, _, _ = oracle.forward(inp.X, inp.layers(), cfg.eps)
-    el = time.perf_counter() - t0
-    assert np.isfinite(o).all()
-    return {"value": round(n / el, 3), "unit": "samples/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} samples of {cfg.name} (T={cfg.T}, D={cfg.D}, k={cfg.k}, L={cfg.L}), "
-                      f"fp64 NumPy, {el:.1f} s"}
+
+    def run(m):
+        inp = synth.make_inputs(cfg.with_(B=m), seed=0)
+        t0 = time.perf_counter()
+        o, _, _ = oracle.forward(inp.X, inp.layers(), cfg.eps)
+        el = time.perf_counter() - t0
+        assert np.isfinite(o).all()
+        return el
+
+    el = run(n)
+    res = {"value": round(n / el, 3), "unit": "samples/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{n} samples of {cfg.name} (T={cfg.T}, D={cfg.D}, k={cfg.k}, L={cfg.L}), "
+                     f"fp64 NumPy, {el:.1f} s",
+           "cpu_model": cpu_model(), "logical_cpus": os.cpu_count()}
+    if single_thread:
+        try:
+            from threadpoolctl import threadpool_limits
+        except ImportError:
+            return res
+        n1 = max(1, n // 16)
+        with threadpool_limits(limits=1, user_api="blas"):
+            el1 = run(n1)
+        res["single_thread"] = {"value": round(n1 / el1, 3), "unit": "samples/s",
+                                "sample": f"{n1} samples, one BLAS thread, {el1:.1f} s"}
+    return res
 
 
 def library_reference():
