@@ -645,15 +645,26 @@ constexpr int LD6 = 2 * 32 + 4;                             // epilogue staging 
 // W^T part is tile column r; the chunk swizzle depends on r % 8, which a half-block keeps.
 // GATHER_A: A is not packed but gathered from row-major rows; offA[c] is this lane's byte
 // offset of piece wave + 4 c at K step 0 (the 16 bytes that belong at the lane's place in
-// the packed layout), and a K step advances it by 64 bytes.  NI < 4: only the wave's first
-// NI row blocks hold rows (a tile past the end of its rows); the others are neither read
-// nor multiplied and their accumulators stay zero.  Copies and barriers are the same for
-// every NI, so the waves of one workgroup may run different NI.
-template <bool GATHER_A, int NI>
+// the packed layout), and a K step advances it by 64 bytes.  NI < TM / 64: only the wave's
+// first NI row blocks hold rows (a tile past the end of its rows); the others are neither
+// read nor multiplied and their accumulators stay zero.  Copies and barriers are the same
+// for every NI, so the waves of one workgroup may run different NI.
+// TM = 128: tiles of 128 x 384 (waves of 64 x 192, 2 x 6 blocks) for launches that would
+// leave CUs idle with 256-row tiles; the A part of a stage is then 8 KB (the first or second
+// half of a packed 256-row block, selected by the caller's rA) and a wave copies 8 pieces
+// per K step instead of 10.  The sums run in the same order for every TM.
+template <bool GATHER_A, int NI, int TM = 256>
 __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (&accV)[4][2],
                                               __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rW, lds_u8* smem,
                                               uint32_t lds0, int K, int nt, int wave, int lane,
                                               const uint32_t (&offA)[4]) {
+  static_assert(TM == 256 || TM == 128, "256- or 128-row tiles");
+  static_assert(!GATHER_A || TM == 256, "gathered rows use 256-row tiles");
+  static_assert(NI <= TM / 64, "row blocks of a wave");
+  constexpr int APW = TM / 64;                 // A pieces per wave and K step
+  constexpr int NCP = APW + 6;                 // copies per wave and K step
+  constexpr int ABYTES = TM * BK * 2;          // A part of a stage
+  constexpr int STG = ABYTES + BN6 * BK * 2;   // stage bytes
   const int nk = K / BK;
   uint32_t voffW[6];
 #pragma unroll
@@ -663,12 +674,12 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
     voffW[c] = uint32_t(hb >> 1) * uint32_t(nk) * 16384u + uint32_t(hb & 1) * 8192u + uint32_t(q & 7) * 1024u +
                uint32_t(lane) * 16u;
   }
-  // copy c (0..9) of K step kt into ring stage `stage`; steps past the end reload the last
-  // step (in bounds, never read) so that every K step issues the same number of loads
+  // copy c (0..NCP-1) of K step kt into ring stage `stage`; steps past the end reload the
+  // last step (in bounds, never read) so that every K step issues the same number of loads
   auto copy = [&](int kt, int stage, int c) {
     kt = kt < nk ? kt : nk - 1;
-    const uint32_t sbase = lds0 + uint32_t(stage) * STAGE6_BYTES;
-    if (c < 4) {
+    const uint32_t sbase = lds0 + uint32_t(stage) * STG;
+    if (c < APW) {
       const uint32_t piece = uint32_t(wave + 4 * c);
       if constexpr (GATHER_A)
         copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), offA[c], rA, kt * BK * 2);
@@ -676,8 +687,8 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
         copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), piece * 1024u + uint32_t(lane) * 16u, rA,
                     kt * 16384);
     } else {
-      const uint32_t q = uint32_t(wave + 4 * (c - 4));
-      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + A_STAGE_BYTES + q * 1024u), voffW[c - 4], rW, kt * 16384);
+      const uint32_t q = uint32_t(wave + 4 * (c - APW));
+      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + ABYTES + q * 1024u), voffW[c - APW], rW, kt * 16384);
     }
   };
   const int wm = wave >> 1, wn = wave & 1;
@@ -685,10 +696,10 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const int c = kk * 2 + (lane >> 5);
-    const int m = wm * 128 + (lane & 31);
+    const int m = wm * (TM / 2) + (lane & 31);
     aoff[kk] = uint32_t(m * 64 + ((c ^ pk_swz(m)) << 4));
     const int n = wn * 192 + (lane & 31);
-    boff[kk] = uint32_t(A_STAGE_BYTES + n * 64 + ((c ^ pk_swz(n)) << 4));
+    boff[kk] = uint32_t(ABYTES + n * 64 + ((c ^ pk_swz(n)) << 4));
   }
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
   // a0 / a1: A fragments of sub-steps 0 / 1; b[j]: the W^T fragment of column block j,
@@ -723,18 +734,21 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
       for (int r = 0; r < 16; ++r) accV[i][j][r] = 0.f;
   }
   asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // the zeroed VGPR accumulators settle
-  // prologue: steps 0..PK6_NS-1; wait for step 0 (10 loads per step)
+  // prologue: steps 0..PK6_NS-1; wait for step 0 (NCP loads per step)
 #pragma unroll
   for (int st = 0; st < PK6_NS; ++st)
 #pragma unroll
-    for (int c = 0; c < 10; ++c) copy(st, st, c);
-  asm volatile("s_waitcnt vmcnt(20)\n\ts_barrier" ::: "memory");
+    for (int c = 0; c < NCP; ++c) copy(st, st, c);
+  if constexpr (NCP == 10)
+    asm volatile("s_waitcnt vmcnt(20)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
   read_a(a0, smem, 0);
 #pragma unroll
   for (int j = 0; j < 6; ++j) read_b(smem, 0, j);
   int stage = 0;
   for (int it = 0; it < nk; ++it) {
-    const lds_u8* sp = smem + stage * STAGE6_BYTES;
+    const lds_u8* sp = smem + stage * STG;
     const int nstage = stage + 1 == PK6_NS ? 0 : stage + 1;
     // sub-step 0 on a0 / b; sub-step 1's fragments of this stage read behind the MFMAs
     read_a(a1, sp, 1);
@@ -746,15 +760,18 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
       read_b(sp, 1, j);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // every read of this stage has returned; after the barrier step it+1 is visible (the 10
+    // every read of this stage has returned; after the barrier step it+1 is visible (the NCP
     // loads of the step after it may be outstanding) and this stage takes step it+PK6_NS
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+    if constexpr (NCP == 10)
+      asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     // sub-step 1 on a1 / b; the next stage's sub-step 0 fragments and this stage's refill
     // between the MFMAs
-    const lds_u8* np = smem + nstage * STAGE6_BYTES;
+    const lds_u8* np = smem + nstage * STG;
     read_a(a0, np, 0);
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
@@ -762,7 +779,7 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
       for (int h = 0; h < 2; ++h) {
         mm(a1, 2 * h, j);
         mm(a1, 2 * h + 1, j);
-        if (2 * j + h < 10) {
+        if (2 * j + h < NCP) {
           __builtin_amdgcn_sched_barrier(0);
           copy(it + PK6_NS, stage, 2 * j + h);
           __builtin_amdgcn_sched_barrier(0);
@@ -785,12 +802,12 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
 // group of two column blocks, 32 rows x 64 columns are staged through LDS so that each lane
 // then owns 8 consecutive columns of one row (8 lanes per row, 8 rows per pass).
 // row_of(r) maps tile row r to its output row, or -1 where the tile runs past the rows.
-template <int EPI, typename RowOf>
+template <int EPI, int TM = 256, typename RowOf>
 __device__ __forceinline__ void tile_epilogue6(const f32x16_t (&accA)[4][4], const f32x16_t (&accV)[4][2],
                                                float* smem_f, const GemmArgs& p, int g, const bf16_t* bias_g,
-                                               int n0, int wave, int lane, RowOf row_of, int nib = 4) {
+                                               int n0, int wave, int lane, RowOf row_of, int nib = TM / 64) {
   const int M = p.M, N = p.N;
-  const int wrow0 = (wave >> 1) * 128, wcol0 = (wave & 1) * 192;
+  const int wrow0 = (wave >> 1) * (TM / 2), wcol0 = (wave & 1) * 192;
   float* st = smem_f + wave * 32 * LD6;
   const int col8 = (lane & 7) * 8;
   float bias[3][8];
@@ -802,7 +819,7 @@ __device__ __forceinline__ void tile_epilogue6(const f32x16_t (&accA)[4][4], con
     if (bias_g && n < N) load8(bias_g + n, bias[s]);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TM / 64; ++i) {
     if (i >= nib) break;  // row blocks past the rows (wave-uniform)
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
@@ -857,17 +874,17 @@ __device__ __forceinline__ void tile_epilogue6(const f32x16_t (&accA)[4][4], con
   }
 }
 
-// Dense per-token product on packed operands with 256 x 384 tiles: G * ceil(M/256) * N/384
+// Dense per-token product on packed operands with TM x 384 tiles: G * ceil(M/TM) * N/384
 // workgroups, N % 384 == 0; EPI_GELU or EPI_RESID.
-template <int EPI>
+template <int EPI, int TM>
 __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384(GemmArgs p) {
   static_assert(EPI == EPI_GELU || EPI == EPI_RESID, "256 x 384 tiles serve the inference epilogues");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[PK6_NS * STAGE6_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[PK6_NS * (TM * BK * 2 + BN6 * BK * 2)];
   lds_u8* const smem = (lds_u8*)smem_g;
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int M = p.M, N = p.N, K = p.K;
-  const int nMt = (M + BM - 1) / BM, nNt = N / BN6;
+  const int nMt = (M + TM - 1) / TM, nNt = N / BN6;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int g = id / (nMt * nNt);
   const int rem = id - g * nMt * nNt;
@@ -876,21 +893,25 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384(GemmArgs 
   const int in_band = rem - band * TILE_BAND * nNt;
   const int bm = min(TILE_BAND, nMt - band * TILE_BAND);
   const int nt = in_band / bm, mt = band * TILE_BAND + (in_band - (in_band / bm) * bm);
-  // the tile's A blocks (row block mt, K/32 x 16 KB) and the token's whole W^T (pk_rows(N)
-  // rows; slices < 2^31 bytes, checked at launch)
+  // the tile's A blocks (packed row block, K/32 x 16 KB; a 128-row tile starts at the first or
+  // second 8 KB half of each) and the token's whole W^T (pk_rows(N) rows; slices < 2^31
+  // bytes, checked at launch)
   const uint32_t blk = uint32_t(K / BK) * 16384u;
   const uint32_t wbytes = uint32_t(pk_rows(N) / 256) * blk;
+  const int nMb = (M + BM - 1) / BM;                    // packed 256-row blocks per token
+  const int mb = mt / (BM / TM), half = mt % (BM / TM);  // block and half of this tile
   const __amdgpu_buffer_rsrc_t rA =
-      make_rsrc(static_cast<const uint16_t*>(p.A) + (size_t(g) * nMt + mt) * (size_t(blk) / 2), blk);
+      make_rsrc(static_cast<const uint16_t*>(p.A) + (size_t(g) * nMb + mb) * (size_t(blk) / 2) + size_t(half) * 4096,
+                blk - uint32_t(half) * 8192u);
   const __amdgpu_buffer_rsrc_t rW =
       make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * (size_t(wbytes) / 2), wbytes);
   f32x16_t accA[4][4], accV[4][2];
   const uint32_t no_gather[4] = {0u, 0u, 0u, 0u};
-  mfma_tile_pk6<false, 4>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, no_gather);
+  mfma_tile_pk6<false, TM / 64, TM>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, no_gather);
   const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
-  const int m0 = mt * BM;
-  tile_epilogue6<EPI>(accA, accV, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN6, wave, lane,
-                      [&](int r) { return m0 + r < M ? m0 + r : -1; });
+  const int m0 = mt * TM;
+  tile_epilogue6<EPI, TM>(accA, accV, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN6, wave, lane,
+                          [&](int r) { return m0 + r < M ? m0 + r : -1; });
 }
 
 // Sparse-MoE grouped GEMM on prepared expert weights with 256 x 384 tiles: the persistent
@@ -1528,23 +1549,34 @@ hipError_t launch_gemm_moe(int epi, const GemmArgs& args, hipStream_t stream) {
 
 namespace {
 
-// 256 x 384 tiles where N allows them (their buffer descriptor spans a token's whole packed
-// W^T, which must stay below 2^31 bytes) and where they take fewer rounds of the whole
-// device: a 256 x 384 tile runs about 1.4x as long as a 256 x 256 one, so with rounds =
-// ceil(tiles / CUs) they win when 1.4 x rounds(384) < rounds(256).  (Measured at the 1B
-// shapes: B = 256, GEMM2 on 128 wide tiles for 256 CUs, 231 against 197 us.)  The
-// environment variable RMX_WIDE_TILES = "always" / "never" overrides the choice (tests and
-// tuning); both kernels give the same bits.
-bool wide_tiles_pay(const GemmArgs& a) {
+// Tile shape of a packed-operand product with the GELU or residual epilogue.  384-wide tiles
+// need N % 384 == 0 and a token's packed W^T below 2^31 bytes (their buffer descriptor spans
+// it).  Among the shapes allowed, the launch takes the fewest device rounds (ceil(tiles /
+// CUs)) weighted by the tile's duration, measured at the 1B shapes: a 256 x 384 tile runs
+// about 1.4x as long as a 256 x 256 one (B = 256, GEMM2 on 128 wide tiles for 256 CUs: 231
+// against 197 us), and a 128 x 384 tile, which copies as many bytes per K step as a
+// 256 x 256 one, 0.95x (B = 256, GEMM2 in one round of 256 such tiles: 188 against 198 us).
+// The environment variable RMX_WIDE_TILES = always / half / never forces 256 x 384,
+// 128 x 384 or 256 x 256 (tests and tuning; read at each launch); all give the same bits.
+enum TileShape { TILES_256 = 0, TILES_256x384 = 1, TILES_128x384 = 2 };
+
+TileShape pick_tiles(const GemmArgs& a) {
   const char* force = getenv("RMX_WIDE_TILES");
-  if (force && strcmp(force, "never") == 0) return false;
-  if (a.N % BN6 != 0 || uint64_t(pk_rows(a.N)) * uint64_t(a.K) * 2u >= (uint64_t(1) << 31)) return false;
-  if (force && strcmp(force, "always") == 0) return true;
+  if (force && strcmp(force, "never") == 0) return TILES_256;
+  if (a.N % BN6 != 0 || uint64_t(pk_rows(a.N)) * uint64_t(a.K) * 2u >= (uint64_t(1) << 31)) return TILES_256;
+  if (force && strcmp(force, "always") == 0) return TILES_256x384;
+  if (force && strcmp(force, "half") == 0) return TILES_128x384;
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const int64_t mt = (a.M + BM - 1) / BM;
+  auto rounds = [&](int64_t tiles) { return (tiles + cus - 1) / cus; };
+  const int64_t mt = (a.M + BM - 1) / BM, mh = (a.M + 127) / 128;
   const int64_t t6 = int64_t(a.G) * mt * (a.N / BN6), t4 = int64_t(a.G) * mt * ((a.N + BN - 1) / BN);
-  return 7 * ((t6 + cus - 1) / cus) < 5 * ((t4 + cus - 1) / cus);
+  const int64_t th = int64_t(a.G) * mh * (a.N / BN6);
+  // relative tile durations 20 : 28 : 19 (256 x 256 : 256 x 384 : 128 x 384; the first and
+  // last copy the same 32 KB per K step), times rounds
+  const int64_t c4 = 20 * rounds(t4), c6 = 28 * rounds(t6), ch = 19 * rounds(th);
+  if (ch < c6 && ch < c4) return TILES_128x384;
+  return c6 < c4 ? TILES_256x384 : TILES_256;
 }
 
 template <bool PK>
@@ -1559,12 +1591,21 @@ hipError_t launch_dense_mfma(int epi, const GemmArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_RESID, PK>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
     return hipGetLastError();
   }
-  if (PK && (epi == EPI_GELU || epi == EPI_RESID) && wide_tiles_pay(a)) {
+  const TileShape shape = PK && (epi == EPI_GELU || epi == EPI_RESID) ? pick_tiles(a) : TILES_256;
+  if (shape == TILES_256x384) {
     const int tiles6 = a.G * ((a.M + BM - 1) / BM) * (a.N / BN6);
     if (epi == EPI_GELU)
-      hipLaunchKernelGGL((gemm_bf16_mfma_n384<EPI_GELU>), dim3(tiles6), dim3(MFMA_THREADS), 0, stream, a);
+      hipLaunchKernelGGL((gemm_bf16_mfma_n384<EPI_GELU, 256>), dim3(tiles6), dim3(MFMA_THREADS), 0, stream, a);
     else
-      hipLaunchKernelGGL((gemm_bf16_mfma_n384<EPI_RESID>), dim3(tiles6), dim3(MFMA_THREADS), 0, stream, a);
+      hipLaunchKernelGGL((gemm_bf16_mfma_n384<EPI_RESID, 256>), dim3(tiles6), dim3(MFMA_THREADS), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (shape == TILES_128x384) {
+    const int tilesh = a.G * ((a.M + 127) / 128) * (a.N / BN6);
+    if (epi == EPI_GELU)
+      hipLaunchKernelGGL((gemm_bf16_mfma_n384<EPI_GELU, 128>), dim3(tilesh), dim3(MFMA_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_mfma_n384<EPI_RESID, 128>), dim3(tilesh), dim3(MFMA_THREADS), 0, stream, a);
     return hipGetLastError();
   }
   const int tiles = a.G * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);

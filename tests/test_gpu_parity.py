@@ -145,14 +145,15 @@ def test_small_batch_deterministic():
 def test_prepared_weights_bit_identical(B, T, D, k, L, monkeypatch):
     """Weights prepared by rmx_pack_weights (and the packed S and H they bring) give the
     same bits as the row-major path, and match the oracle; the same with the 256 x 384 tiles
-    forced where N % 384 == 0 (RMX_WIDE_TILES=always) and forbidden (=never), since at these
-    sizes the launch would pick by device occupancy."""
+    (RMX_WIDE_TILES=always) or the 128 x 384 tiles (=half) forced where N % 384 == 0, and
+    with both forbidden (=never), since at these sizes the launch would pick by device
+    occupancy."""
     cfg = synth.Config("pk", B=B, T=T, D=D, k=k, L=L, dtype="bf16", bias_std=0.02)
     inp = synth.make_inputs(cfg, seed=B + 3 * D)
     o1, xl1 = run_gpu(cfg, inp)
     o2, xl2 = run_gpu(cfg, inp, packed=True)
     assert np.array_equal(o1, o2) and np.array_equal(xl1, xl2)
-    for policy in ("always", "never"):
+    for policy in ("always", "half", "never"):
         monkeypatch.setenv("RMX_WIDE_TILES", policy)
         o3, xl3 = run_gpu(cfg, inp, packed=True)
         assert np.array_equal(o1, o3) and np.array_equal(xl1, xl3), policy
