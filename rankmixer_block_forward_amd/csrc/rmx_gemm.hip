@@ -1265,24 +1265,30 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_moe(GemmArgs p) {
 // K steps of 32 through a 4-stage ring of 20 KB (A 64 x 32, W 32 x 256), so two workgroups
 // share a CU and their copy streams overlap.  Same copy, swizzle and wait scheme as the
 // 256 x 256 kernel: 5 loads per wave per K step (1 of A, 4 of W).
+// SBN = 128 (packed operands only): 64 x 128 tiles, waves of 64 x 32, 3 loads per wave per
+// K step (the tile's W^T rows are one 8 KB half of each packed 256-row block), for launches
+// whose 64 x 256 tiles would load the CUs unevenly (see narrow_small_tiles).
 constexpr int SM_BM = 64;
 constexpr int SM_A_BYTES = SM_BM * BK * 2;                 // 4 KB, rows of 64 B
-constexpr int SM_STAGE_BYTES = SM_A_BYTES + BK * BN * 2;   // + 16 KB
-constexpr int SM_COPIES = 5;
 
-template <int EPI, bool PK>
+template <int EPI, bool PK, int SBN = 256>
 __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p) {
+  static_assert(SBN == 256 || (SBN == 128 && PK), "64 x 128 tiles need packed operands");
+  constexpr int SM_STAGE_BYTES = SM_A_BYTES + BK * SBN * 2;  // + 16 KB or 8 KB of W
+  constexpr int WPW = SBN / 64;                               // W pieces per wave and K step
+  constexpr int SM_COPIES = 1 + WPW;
+  constexpr int NJ = SBN / 128;                               // column blocks per wave
   __shared__ __attribute__((aligned(1024))) unsigned char smem_g[NS * SM_STAGE_BYTES];
   lds_u8* const smem = (lds_u8*)smem_g;
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int M = p.M, N = p.N, K = p.K;
-  const int nMt = (M + SM_BM - 1) / SM_BM, nNt = (N + BN - 1) / BN;
+  const int nMt = (M + SM_BM - 1) / SM_BM, nNt = (N + SBN - 1) / SBN;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int g = id / (nMt * nNt);
   const int rem = id - g * nMt * nNt;
   const int nt = rem / nMt, mt = rem - nt * nMt;
-  const int m0 = mt * SM_BM, n0 = nt * BN;
+  const int m0 = mt * SM_BM, n0 = nt * SBN;
   const int nk = K / BK;
 
   __amdgpu_buffer_rsrc_t rA, rW;
@@ -1294,11 +1300,14 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
   if constexpr (PK) {
     const uint32_t blk = uint32_t(nk) * 16384u;
     const int64_t row_blocks = pk_rows(M) / 256;
+    const int nNb = int(pk_rows(N) / 256);                         // packed W^T blocks
+    const int wb = nt / (256 / SBN), wh = nt % (256 / SBN);          // block, half of it
     rA = make_rsrc(static_cast<const uint16_t*>(p.A) + (size_t(g) * row_blocks + m0 / 256) * (size_t(blk) / 2), blk);
-    rW = make_rsrc(static_cast<const uint16_t*>(p.W) + (size_t(g) * nNt + nt) * (size_t(blk) / 2), blk);
+    rW = make_rsrc(static_cast<const uint16_t*>(p.W) + (size_t(g) * nNb + wb) * (size_t(blk) / 2) + size_t(wh) * 4096,
+                   blk - uint32_t(wh) * 8192u);
     offA = uint32_t(m0 % 256) * 64u + uint32_t(wave) * 1024u + uint32_t(lane) * 16u;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) offW[a] = uint32_t(4 * wave + a) * 1024u + uint32_t(lane) * 16u;
+    for (int a = 0; a < 4; ++a) offW[a] = uint32_t(WPW * wave + (a < WPW ? a : 0)) * 1024u + uint32_t(lane) * 16u;
   } else {
     const uint32_t lda = uint32_t(p.lda);
     const uint32_t bytesA = (uint32_t(M - 1) * lda + uint32_t(K)) * 2u, bytesW = uint32_t(K) * uint32_t(N) * 2u;
@@ -1321,7 +1330,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
       if (q == 0) {
         copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + uint32_t(wave) * 1024u), offA, rA, kt * 16384);
       } else {
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(sbase + SM_A_BYTES + uint32_t(4 * wave + q - 1) * 1024u);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(sbase + SM_A_BYTES + uint32_t(WPW * wave + q - 1) * 1024u);
         copy_to_lds(dst, offW[q - 1], rW, kt * 16384);
       }
     } else {
@@ -1344,7 +1353,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
       const int c = kk * 2 + (lane >> 5);
       aoff[kk][i] = uint32_t(m * 64 + ((c ^ swz_a(m)) << 4));
       if constexpr (PK) {
-        const int n = wave * 64 + i * 32 + (lane & 31);
+        const int n = wave * (SBN / 4) + i * 32 + (lane & 31);
         boff[kk][i] = uint32_t(SM_A_BYTES + n * 64 + ((c ^ pk_swz(n)) << 4));
       } else {
         const int kb = 8 * (lane >> 5) + ((lane & 15) >> 2);
@@ -1356,13 +1365,13 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
   typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
   struct SmFrags {
     u32x4_t a[2];
-    u32x4_t b[2];  // W columns of the 2 column blocks: 8 bf16 each
+    u32x4_t b[NJ];  // W columns of the NJ column blocks: 8 bf16 each
   };
   auto read_frags = [&](SmFrags& f, const lds_u8* sp, int kk) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) f.a[i] = *reinterpret_cast<const lds_u32x4*>(sp + aoff[kk][i]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       if constexpr (PK) {
         f.b[j] = *reinterpret_cast<const lds_u32x4*>(sp + boff[kk][j]);
       } else {
@@ -1373,19 +1382,19 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
       }
     }
   };
-  f32x16_t acc[2][2];
+  f32x16_t acc[2][NJ];
   auto mfma4 = [&](const SmFrags& f) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.b[j]),
                                                             __builtin_bit_cast(bf16x8_t, f.a[i]), acc[i][j], 0, 0, 0);
   };
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -1394,7 +1403,11 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
   for (int st = 0; st < NS; ++st)
 #pragma unroll
     for (int q = 0; q < SM_COPIES; ++q) copy(st, st, q);
-  asm volatile("s_waitcnt vmcnt(15)\n\ts_barrier" ::: "memory");
+  static_assert(NS == 4, "the wait counts below assume a 4-stage ring");
+  if constexpr (SM_COPIES == 5)
+    asm volatile("s_waitcnt vmcnt(15)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory");
   SmFrags f0, f1;
   read_frags(f0, smem, 0);
   int stage = 0;
@@ -1407,7 +1420,10 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
     // stage free for step it+NS
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+    if constexpr (SM_COPIES == 5)
+      asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     read_frags(f0, smem + nstage * SM_STAGE_BYTES, 0);
     mfma4(f1);
@@ -1420,8 +1436,8 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
-  tile_epilogue<EPI, 2, 2, PK>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, 0, wave * 64, wave, lane, g,
-                               [&](int m) { return m0 + m < M ? m0 + m : -1; });
+  tile_epilogue<EPI, 2, NJ, PK>(acc, reinterpret_cast<float*>(smem_g), p, bias_g, n0, 0, wave * (SBN / 4), wave,
+                                lane, g, [&](int m) { return m0 + m < M ? m0 + m : -1; });
 }
 
 // --------------------------------------------------------------- generic kernel
@@ -1579,9 +1595,34 @@ TileShape pick_tiles(const GemmArgs& a) {
   return c6 < c4 ? TILES_256x384 : TILES_256;
 }
 
+// 64-row tiles 128 columns wide (packed products) where the 256-wide ones number between
+// one and two per CU, so that some CUs would run two and others one: the narrow tiles then
+// spread evenly (measured at the 1B shapes, B = 128, GEMM2: 384 wide tiles 184 us, 768
+// narrow ones 169 us).  With fewer wide tiles than CUs the narrow ones are slower (B = 64,
+// GEMM2: 126 against 137 us): a workgroup streams its weight panel at a rate set by the
+// bytes its ring keeps in flight, which the narrow tile halves.  RMX_NARROW_TILES = always /
+// never forces the choice (tests and tuning; read at each launch); both give the same bits.
+bool narrow_small_tiles(const GemmArgs& a) {
+  const char* force = getenv("RMX_NARROW_TILES");
+  if (force && strcmp(force, "never") == 0) return false;
+  if (force && strcmp(force, "always") == 0) return true;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t tiles = int64_t(a.G) * ((a.M + SM_BM - 1) / SM_BM) * ((a.N + BN - 1) / BN);
+  return tiles >= int64_t(cus) && tiles < 2 * int64_t(cus);
+}
+
 template <bool PK>
 hipError_t launch_dense_mfma(int epi, const GemmArgs& a, hipStream_t stream) {
   if (a.M <= GEMM_SMALL_M) {
+    if (PK && (epi == EPI_GELU || epi == EPI_RESID) && narrow_small_tiles(a)) {
+      const int tiles = a.G * ((a.M + SM_BM - 1) / SM_BM) * ((a.N + 127) / 128);
+      if (epi == EPI_GELU)
+        hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_GELU, true, 128>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+      else
+        hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_RESID, true, 128>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+      return hipGetLastError();
+    }
     const int tiles = a.G * ((a.M + SM_BM - 1) / SM_BM) * ((a.N + BN - 1) / BN);
     if (epi == EPI_GELU)
       hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_GELU, PK>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);

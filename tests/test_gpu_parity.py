@@ -145,19 +145,20 @@ def test_small_batch_deterministic():
 def test_prepared_weights_bit_identical(B, T, D, k, L, monkeypatch):
     """Weights prepared by rmx_pack_weights (and the packed S and H they bring) give the
     same bits as the row-major path, and match the oracle; the same with the 256 x 384 tiles
-    (RMX_WIDE_TILES=always) or the 128 x 384 tiles (=half) forced where N % 384 == 0, and
-    with both forbidden (=never), since at these sizes the launch would pick by device
-    occupancy."""
+    (RMX_WIDE_TILES=always) or the 128 x 384 tiles (=half) forced where N % 384 == 0, with
+    both forbidden (=never), and, up to 128 rows per token, with the 64 x 128 tiles forced
+    or forbidden (RMX_NARROW_TILES), since at these sizes the launch picks by occupancy."""
     cfg = synth.Config("pk", B=B, T=T, D=D, k=k, L=L, dtype="bf16", bias_std=0.02)
     inp = synth.make_inputs(cfg, seed=B + 3 * D)
     o1, xl1 = run_gpu(cfg, inp)
     o2, xl2 = run_gpu(cfg, inp, packed=True)
     assert np.array_equal(o1, o2) and np.array_equal(xl1, xl2)
-    for policy in ("always", "half", "never"):
-        monkeypatch.setenv("RMX_WIDE_TILES", policy)
+    for var, policy in (("RMX_WIDE_TILES", "always"), ("RMX_WIDE_TILES", "half"), ("RMX_WIDE_TILES", "never"),
+                        ("RMX_NARROW_TILES", "always"), ("RMX_NARROW_TILES", "never")):
+        monkeypatch.setenv(var, policy)
         o3, xl3 = run_gpu(cfg, inp, packed=True)
-        assert np.array_equal(o1, o3) and np.array_equal(xl1, xl3), policy
-    monkeypatch.delenv("RMX_WIDE_TILES")
+        monkeypatch.delenv(var)
+        assert np.array_equal(o1, o3) and np.array_equal(xl1, xl3), (var, policy)
     rows = sample_rows(B, 32)
     o_ref, xl_ref = run_oracle(cfg, inp, rows)
     check(cfg, o2[rows], xl2[rows], o_ref, xl_ref, f"prepared {B}x{T}x{D} k{k} L{L}")
