@@ -1571,7 +1571,9 @@ namespace {
 // CUs)) weighted by the tile's duration, measured at the 1B shapes: a 256 x 384 tile runs
 // about 1.4x as long as a 256 x 256 one (B = 256, GEMM2 on 128 wide tiles for 256 CUs: 231
 // against 197 us), and a 128 x 384 tile, which copies as many bytes per K step as a
-// 256 x 256 one, 0.95x (B = 256, GEMM2 in one round of 256 such tiles: 188 against 198 us).
+// 256 x 256 one, 0.85x (B = 256, GEMM2 in one round of 256 such tiles: 188 against 198 us;
+// B = 384 GEMM1, 6 rounds of them against 4 of 256 x 384: 301 against 334 us; B = 640 and
+// 768 GEMM2, 3 rounds against 2: 454 against 486 us and 480 against 506 us).
 // The environment variable RMX_WIDE_TILES = always / half / never forces 256 x 384,
 // 128 x 384 or 256 x 256 (tests and tuning; read at each launch); all give the same bits.
 enum TileShape { TILES_256 = 0, TILES_256x384 = 1, TILES_128x384 = 2 };
@@ -1588,9 +1590,8 @@ TileShape pick_tiles(const GemmArgs& a) {
   const int64_t mt = (a.M + BM - 1) / BM, mh = (a.M + 127) / 128;
   const int64_t t6 = int64_t(a.G) * mt * (a.N / BN6), t4 = int64_t(a.G) * mt * ((a.N + BN - 1) / BN);
   const int64_t th = int64_t(a.G) * mh * (a.N / BN6);
-  // relative tile durations 20 : 28 : 19 (256 x 256 : 256 x 384 : 128 x 384; the first and
-  // last copy the same 32 KB per K step), times rounds
-  const int64_t c4 = 20 * rounds(t4), c6 = 28 * rounds(t6), ch = 19 * rounds(th);
+  // relative tile durations 20 : 28 : 17 (256 x 256 : 256 x 384 : 128 x 384), times rounds
+  const int64_t c4 = 20 * rounds(t4), c6 = 28 * rounds(t6), ch = 17 * rounds(th);
   if (ch < c6 && ch < c4) return TILES_128x384;
   return c6 < c4 ? TILES_256x384 : TILES_256;
 }
