@@ -1571,9 +1571,10 @@ namespace {
 // CUs)) weighted by the tile's duration, measured at the 1B shapes: a 256 x 384 tile runs
 // about 1.4x as long as a 256 x 256 one (B = 256, GEMM2 on 128 wide tiles for 256 CUs: 231
 // against 197 us), and a 128 x 384 tile, which copies as many bytes per K step as a
-// 256 x 256 one, 0.85x (B = 256, GEMM2 in one round of 256 such tiles: 188 against 198 us;
-// B = 384 GEMM1, 6 rounds of them against 4 of 256 x 384: 301 against 334 us; B = 640 and
-// 768 GEMM2, 3 rounds against 2: 454 against 486 us and 480 against 506 us).
+// 256 x 256 one, about 0.85x (fitted to B = 384 GEMM1, 6 rounds of them against 4 of
+// 256 x 384: 301 against 334 us, and B = 640 and 768 GEMM2, 3 rounds against 2: 454 against
+// 486 us and 480 against 506 us; at B = 256 GEMM2 one round of them takes 188 us against
+// 198 for one round of 256 x 256 tiles).
 // The environment variable RMX_WIDE_TILES = always / half / never forces 256 x 384,
 // 128 x 384 or 256 x 256 (tests and tuning; read at each launch); all give the same bits.
 enum TileShape { TILES_256 = 0, TILES_256x384 = 1, TILES_128x384 = 2 };
