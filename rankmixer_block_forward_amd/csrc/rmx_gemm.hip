@@ -622,7 +622,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
                                2 * mt + (wave >> 1));
 }
 
-// ------------------------------------------------------------- 256 x 384 tiles
+// ------------------------------------------------------- 256 x 384 and 128 x 384 tiles
 // Where N is a multiple of 384, the packed-operand products run 256 x 384 tiles: each wave
 // owns 128 x 192 outputs (4 x 6 blocks of 32 x 32), and the operand bytes copied into LDS per
 // FLOP drop by 17 % against 256 x 256 tiles (the copy rate of a CU bounds the K loop).  The
@@ -632,7 +632,8 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
 // wait states guard its VGPR hazards: after the VALU zeroes the accumulators, before a
 // fragment register an assembly MFMA has read is rewritten by an LDS read, and before the
 // epilogue reads the results.  Per block, the products are accumulated in the same order as
-// in the 256 x 256 kernel, so the two give the same bits.
+// in the 256 x 256 kernel, so the two give the same bits.  The same K loop and epilogue
+// also run 128 x 384 tiles (waves of 64 x 192; see mfma_tile_pk6).
 constexpr int BN6 = 384;
 constexpr int STAGE6_BYTES = A_STAGE_BYTES + BN6 * BK * 2;  // 16 KB of A + 24 KB of W^T
 constexpr int PK6_NS = 3;
@@ -796,7 +797,7 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
   __syncthreads();
 }
 
-// Epilogue of a 256 x 384 tile, the arithmetic of tile_epilogue: GELU (packed H out),
+// Epilogue of a TM x 384 tile, the arithmetic of tile_epilogue: GELU (packed H out),
 // residual (packed S in, fp32 Y out), or the Sparse-MoE ones (GELU to the compacted hidden
 // rows; gate times result to the compacted output rows).  Per row block i of the wave and
 // group of two column blocks, 32 rows x 64 columns are staged through LDS so that each lane
@@ -878,7 +879,7 @@ __device__ __forceinline__ void tile_epilogue6(const f32x16_t (&accA)[4][4], con
 // workgroups, N % 384 == 0; EPI_GELU or EPI_RESID.
 template <int EPI, int TM>
 __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384(GemmArgs p) {
-  static_assert(EPI == EPI_GELU || EPI == EPI_RESID, "256 x 384 tiles serve the inference epilogues");
+  static_assert(EPI == EPI_GELU || EPI == EPI_RESID, "TM x 384 tiles serve the inference epilogues");
   __shared__ __attribute__((aligned(1024))) unsigned char smem_g[PK6_NS * (TM * BK * 2 + BN6 * BK * 2)];
   lds_u8* const smem = (lds_u8*)smem_g;
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
