@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RMX_ABI_VERSION 5
+#define RMX_ABI_VERSION 6
 
 typedef struct rmx_handle rmx_handle; /* opaque, owned by the library */
 
@@ -156,6 +156,35 @@ rmx_status rmx_block_forward(rmx_handle* h, const void* X, int64_t B, const rmx_
 rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w,
                                 int32_t L, int32_t k, float* out, void* xl_out,
                                 float* gate_out, void* stream);
+
+/* The token -> expert row lists of a Sparse-MoE forward, every block: a diagnostic output
+ * (the integer routing step of the paper translation, section 3.4 eq (10): each token
+ * activates a variable number of its experts, those whose ReLU gate is positive).  With
+ * G = T*E groups, group gi = t*E + e lists the samples b whose gate g[b, t, e] > 0:
+ *   group_start [L, G + 1] int32  the list of group gi is rows[group_start[gi] ..
+ *                                 group_start[gi + 1]), group_start[0] = 0
+ *   rows        [L, G * B] int32  the lists, concatenated in group order; each entry is the
+ *                                 token row t*B + b, ascending in b within a group; entries
+ *                                 from group_start[G] on are left unspecified
+ *   row_gate    [L, G * B] fp32   the gate g[b, t, e] of each listed row (same positions)
+ *   pos         [L, G, B]  int32  inverse map: position of (t, e, b) in rows, or -1
+ *   tile_start  [L, G + 1] int32  cumulative count of 256-row product tiles over the groups
+ * Every member is a device pointer or NULL (not written).  The member arrays for block n
+ * start at n times the per-block size given above. */
+typedef struct {
+  int32_t* group_start;
+  int32_t* rows;
+  float* row_gate;
+  int32_t* pos;
+  int32_t* tile_start;
+} rmx_moe_lists;
+
+/* rmx_block_forward_ex that also copies the routing lists of every block to `lists`
+ * (Sparse-MoE handles only; INVALID_ARG for a dense handle or a NULL `lists`).  The
+ * forward's results are those of rmx_block_forward_ex. */
+rmx_status rmx_block_forward_moe_lists(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w,
+                                       int32_t L, int32_t k, float* out, void* xl_out, float* gate_out,
+                                       const rmx_moe_lists* lists, void* stream);
 
 /* Token Mixing alone (H = T): Y[b, h, t*q + r] = X[b, t, h*q + r], q = D/T, for every
  * sample; X and Y are device arrays [B, T, D] of `dtype` and must not overlap.  Uses

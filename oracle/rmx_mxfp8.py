@@ -30,7 +30,7 @@ import numpy as np
 
 from . import rmx_oracle as fwd
 
-__all__ = ["e4m3_round", "mx_scale_exponent", "mx_qdq", "forward_mxfp8"]
+__all__ = ["e4m3_round", "mx_scale_exponent", "mx_qdq", "quantize_weights", "forward_mxfp8"]
 
 E4M3_MAX = 448.0
 E4M3_EMAX = 8          # exponent of the largest E4M3 binade
@@ -72,12 +72,36 @@ def mx_qdq(x, axis: int = -1) -> np.ndarray:
     return np.moveaxis(q.reshape(x.shape), -1, axis)
 
 
-def forward_mxfp8(X, layers: list, eps: float = 1e-5):
+def quantize_weights(layers: list, workers: int = 1) -> list:
+    """mx_qdq of W1[t] and W2[t] along K (axis 0) for every block and token: a list over
+    blocks of lists over tokens of (w1, w2).  The matrices are independent; `workers` > 1
+    evaluates them on that many threads (the same function on the same values: the result
+    does not depend on it)."""
+    jobs = [(n, t) for n, p in enumerate(layers) for t in range(len(p["W1"]))]
+
+    def one(job):
+        n, t = job
+        return mx_qdq(layers[n]["W1"][t], axis=0), mx_qdq(layers[n]["W2"][t], axis=0)
+
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            done = list(ex.map(one, jobs))
+    else:
+        done = [one(j) for j in jobs]
+    out = [[None] * len(p["W1"]) for p in layers]
+    for (n, t), wq in zip(jobs, done):
+        out[n][t] = wq
+    return out
+
+
+def forward_mxfp8(X, layers: list, eps: float = 1e-5, wq: list | None = None):
     """The block stack and pool of ``rmx_oracle.forward`` with the products' operands
     quantized to MXFP8 as the module docstring states.  Dense blocks only.
-    Returns (o[B, D], X_L[B, T, D])."""
+    wq: the weights already passed through ``quantize_weights(layers)`` (optional; they are
+    quantized here otherwise).  Returns (o[B, D], X_L[B, T, D])."""
     X = np.asarray(X, dtype=np.float64)
-    for p in layers:
+    for n, p in enumerate(layers):
         if "Wg" in p:
             raise NotImplementedError("the MXFP8 variant covers the dense per-token FFN")
         S = fwd.layer_norm(fwd.token_mix(X) + X, p["ln1_g"], p["ln1_b"], eps)
@@ -85,8 +109,11 @@ def forward_mxfp8(X, layers: list, eps: float = 1e-5):
         B, T, D = S.shape
         V = np.empty_like(S)
         for t in range(T):
-            w1 = mx_qdq(p["W1"][t], axis=0)
-            w2 = mx_qdq(p["W2"][t], axis=0)
+            if wq is not None:
+                w1, w2 = wq[n][t]
+            else:
+                w1 = mx_qdq(p["W1"][t], axis=0)
+                w2 = mx_qdq(p["W2"][t], axis=0)
             H = fwd.gelu(Sq[:, t, :] @ w1 + np.asarray(p["b1"][t], dtype=np.float64))
             V[:, t, :] = mx_qdq(H, axis=-1) @ w2 + np.asarray(p["b2"][t], dtype=np.float64)
         X = fwd.layer_norm(V + S, p["ln2_g"], p["ln2_b"], eps)

@@ -21,7 +21,8 @@ KERNEL_COUNT = 16
 
 # Every symbol include/rmx.h declares.
 EXPORTS = (
-    "rmx_create", "rmx_destroy", "rmx_block_forward", "rmx_block_forward_ex", "rmx_token_mix",
+    "rmx_create", "rmx_destroy", "rmx_block_forward", "rmx_block_forward_ex", "rmx_block_forward_moe_lists",
+    "rmx_token_mix",
     "rmx_tokenize", "rmx_packed_weights_bytes", "rmx_pack_weights",
     "rmx_packed_weights_mxfp8_bytes", "rmx_pack_weights_mxfp8",
     "rmx_saved_bytes", "rmx_block_forward_train", "rmx_block_backward",
@@ -54,6 +55,13 @@ class rmx_weights(ctypes.Structure):
 GRAD_NAMES = ("W1", "b1", "W2", "b2", "ln1_g", "ln1_b", "ln2_g", "ln2_b")
 
 
+MOE_LIST_NAMES = ("group_start", "rows", "row_gate", "pos", "tile_start")
+
+
+class rmx_moe_lists(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in MOE_LIST_NAMES]
+
+
 class rmx_grads(ctypes.Structure):
     _fields_ = [("d" + n, ctypes.c_void_p) for n in GRAD_NAMES]
 
@@ -75,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rmx_block_forward.argtypes = [vp, vp, i64, ctypes.POINTER(rmx_weights), i32, i32, vp, vp]
     lib.rmx_block_forward_ex.argtypes = [vp, vp, i64, ctypes.POINTER(rmx_weights), i32, i32, vp,
                                          vp, vp, vp]
+    lib.rmx_block_forward_moe_lists.argtypes = [vp, vp, i64, ctypes.POINTER(rmx_weights), i32, i32, vp, vp, vp,
+                                                ctypes.POINTER(rmx_moe_lists), vp]
     lib.rmx_token_mix.argtypes = [vp, vp, i64, i32, i32, i32, vp]
     lib.rmx_tokenize.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, vp]
     lib.rmx_packed_weights_bytes.argtypes = [vp]
@@ -252,6 +262,35 @@ class Handle:
             _ptr(out, "out"), _ptr(xl_out, "xl_out"), _ptr(gate_out, "gate_out"), _stream(stream))
         _check(st, self._h)
         return out
+
+    def forward_moe_lists(self, X, weights: dict, out=None, xl_out=None, gate_out=None, stream=None):
+        """Sparse-MoE forward (rmx_block_forward_moe_lists) that also returns the routing lists
+        of every block: a dict of device tensors group_start [L, G+1], rows [L, G*B],
+        row_gate [L, G*B], pos [L, G, B], tile_start [L, G+1] (G = T*E groups)."""
+        import torch
+        c = self.cfg
+        B = X.shape[0]
+        _ptr(X, "X", self.dtype, (B, c.T, c.D))
+        if out is None:
+            out = torch.empty((B, c.D), dtype=torch.float32, device=X.device)
+        _ptr(out, "out", torch.float32, (B, c.D))
+        _ptr(xl_out, "xl_out", self.dtype, (B, c.T, c.D))
+        if gate_out is not None:
+            _ptr(gate_out, "gate_out", torch.float32, (c.L, B, c.T, c.moe_experts))
+        G = c.T * c.moe_experts
+        i32 = dict(dtype=torch.int32, device=X.device)
+        lists = {"group_start": torch.full((c.L, G + 1), -7, **i32),
+                 "rows": torch.full((c.L, G * B), -7, **i32),
+                 "row_gate": torch.full((c.L, G * B), float("nan"), dtype=torch.float32, device=X.device),
+                 "pos": torch.full((c.L, G, B), -7, **i32),
+                 "tile_start": torch.full((c.L, G + 1), -7, **i32)}
+        ls = rmx_moe_lists(*[lists[n].data_ptr() for n in MOE_LIST_NAMES])
+        ws = self._weights(weights)
+        st = self._lib.rmx_block_forward_moe_lists(
+            self._h, _ptr(X, "X"), B, ctypes.byref(ws), c.L, c.k, _ptr(out, "out"), _ptr(xl_out, "xl_out"),
+            _ptr(gate_out, "gate_out"), ctypes.byref(ls), _stream(stream))
+        _check(st, self._h)
+        return out, lists
 
     # ---- training
     def saved_bytes(self, B: int) -> int:

@@ -477,7 +477,7 @@ rmx_status rmx_destroy(rmx_handle* h) {
 // every block there instead of in the workspace.
 static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w, int32_t L,
                                int32_t k, float* out, void* xl_out, float* gate_out, void* saved,
-                               size_t saved_bytes, void* stream) {
+                               size_t saved_bytes, void* stream, const rmx_moe_lists* lists = nullptr) {
   if (!h) return fail(nullptr, RMX_ERR_INVALID_ARG, "handle is NULL");
   clear_error(h);
   const rmx_config& c = h->cfg;
@@ -495,6 +495,7 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
   if (!attn && (w->Wq || w->Wk || w->Wv))
     return fail(h, RMX_ERR_INVALID_ARG, "Wq / Wk / Wv given to a Token Mixing handle");
   if (gate_out && !moe) return fail(h, RMX_ERR_INVALID_ARG, "gate_out must be NULL for a dense handle");
+  if (lists && !moe) return fail(h, RMX_ERR_INVALID_ARG, "routing lists exist for Sparse-MoE handles only");
   if (train && moe) return fail(h, RMX_ERR_UNSUPPORTED, "training needs a dense handle");
   if (train && w->packed) return fail(h, RMX_ERR_INVALID_ARG, "training reads W1 and W2: packed must be NULL");
   if (train && saved_bytes < rmx_saved_bytes(h, B))
@@ -530,6 +531,15 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
     if ((st = check_dev_opt(h, w->be1, Ls * T * E * hid * esz, dev, "be1")) != RMX_OK) return st;
     if ((st = check_dev_opt(h, w->be2, Ls * T * E * D * esz, dev, "be2")) != RMX_OK) return st;
     if ((st = check_dev_opt(h, gate_out, Ls * size_t(B) * T * E * 4, dev, "gate_out")) != RMX_OK) return st;
+    if (lists) {
+      const size_t G = T * E;
+      if ((st = check_dev_opt(h, lists->group_start, Ls * (G + 1) * 4, dev, "lists.group_start")) != RMX_OK ||
+          (st = check_dev_opt(h, lists->rows, Ls * G * size_t(B) * 4, dev, "lists.rows")) != RMX_OK ||
+          (st = check_dev_opt(h, lists->row_gate, Ls * G * size_t(B) * 4, dev, "lists.row_gate")) != RMX_OK ||
+          (st = check_dev_opt(h, lists->pos, Ls * G * size_t(B) * 4, dev, "lists.pos")) != RMX_OK ||
+          (st = check_dev_opt(h, lists->tile_start, Ls * (G + 1) * 4, dev, "lists.tile_start")) != RMX_OK)
+        return st;
+    }
   } else if (w->packed) {
     if (!h->pk_capable)
       return fail(h, RMX_ERR_UNSUPPORTED, "prepared weights need a dense bf16 handle with D and k*D multiples of 32");
@@ -693,6 +703,20 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
       ma.E = c.moe_experts;
       ma.nchunk = (Bi + 63) / 64;
       if ((e = run_moe_route(h, s, ma)) != hipSuccess) break;
+      if (lists) {
+        // diagnostic copies of this block's routing lists (device to device, on the stream)
+        const size_t G = T * E, GB = G * size_t(B);
+        auto cp = [&](void* dst, const void* src, size_t bytes) {
+          if (dst && e == hipSuccess) e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+        };
+        cp(lists->group_start ? lists->group_start + size_t(n) * (G + 1) : nullptr, h->moe_group_start,
+           (G + 1) * 4);
+        cp(lists->rows ? lists->rows + size_t(n) * GB : nullptr, h->moe_src_row, GB * 4);
+        cp(lists->row_gate ? lists->row_gate + size_t(n) * GB : nullptr, h->moe_row_gate, GB * 4);
+        cp(lists->pos ? lists->pos + size_t(n) * GB : nullptr, h->moe_pos, GB * 4);
+        cp(lists->tile_start ? lists->tile_start + size_t(n) * (G + 1) : nullptr, h->moe_tile_start, (G + 1) * 4);
+        if (e != hipSuccess) break;
+      }
       const uint16_t* pkw = moe_pk ? static_cast<const uint16_t*>(w->packed) + size_t(n) * (pk_we1 + pk_we2) : nullptr;
       GemmArgs m1{};
       m1.A = h->S;
@@ -804,6 +828,16 @@ rmx_status rmx_block_forward_ex(rmx_handle* h, const void* X, int64_t B, const r
                                 int32_t L, int32_t k, float* out, void* xl_out, float* gate_out,
                                 void* stream) {
   return forward_impl(h, X, B, w, L, k, out, xl_out, gate_out, nullptr, 0, stream);
+}
+
+rmx_status rmx_block_forward_moe_lists(rmx_handle* h, const void* X, int64_t B, const rmx_weights* w,
+                                       int32_t L, int32_t k, float* out, void* xl_out, float* gate_out,
+                                       const rmx_moe_lists* lists, void* stream) {
+  if (!lists) {
+    if (h) clear_error(h);
+    return fail(h, RMX_ERR_INVALID_ARG, "lists is NULL");
+  }
+  return forward_impl(h, X, B, w, L, k, out, xl_out, gate_out, nullptr, 0, stream, lists);
 }
 
 size_t rmx_saved_bytes(const rmx_handle* h, int64_t B) {

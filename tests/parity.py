@@ -81,3 +81,51 @@ def check(cfg, o, xl, o_ref, xl_ref, label=""):
             assert err["xl_rel_l2"] <= BF16_REL_L2 and err["xl_max_abs"] <= BF16_MAX_ABS, f"{label}: {err}"
     print(f"{label}: {err}", flush=True)
     return err
+
+
+def sample_tiles(B, per_tile, tile=256, seed=0):
+    """Sample indices stratified over the 256-row tiles of the products: the first and last
+    row of every tile (the ragged edges) plus per_tile - 2 seeded rows inside it."""
+    rng = np.random.default_rng(seed)
+    picks = []
+    for t0 in range(0, B, tile):
+        t1 = min(B, t0 + tile)
+        picks += [t0, t1 - 1]
+        inner = np.arange(t0 + 1, t1 - 1)
+        if len(inner):
+            picks += rng.choice(inner, size=min(len(inner), max(0, per_tile - 2)), replace=False).tolist()
+    return np.unique(np.array(picks, dtype=np.int64))
+
+
+def check_moe_lists(lists, gates, tile=256):
+    """Bit-exact check of the Sparse-MoE routing lists of every block against the gate values
+    the same forward wrote: group gi = t*E + e lists exactly the samples b with
+    gates[n, b, t, e] > 0, as token rows t*B + b in ascending b; the lists are concatenated in
+    group order; row_gate holds the same fp32 gate bits; pos is the inverse map (-1 when
+    inactive); tile_start counts the 256-row tiles of the groups cumulatively.
+    lists: dict of numpy arrays as Handle.forward_moe_lists returns them; gates [L, B, T, E].
+    Returns the per-block active fraction."""
+    L, B, T, E = gates.shape
+    G = T * E
+    frac = []
+    for n in range(L):
+        gs, rows, rg = lists["group_start"][n], lists["rows"][n], lists["row_gate"][n]
+        pos, ts = lists["pos"][n].reshape(G, B), lists["tile_start"][n]
+        g = gates[n].transpose(1, 2, 0).reshape(G, B)           # [t*E + e, b]
+        act = g > 0
+        counts = act.sum(axis=1)
+        assert gs[0] == 0 and np.array_equal(np.diff(gs), counts), f"block {n}: group offsets"
+        want_ts = np.concatenate([[0], np.cumsum((counts + tile - 1) // tile)])
+        assert np.array_equal(ts, want_ts), f"block {n}: tile table"
+        for gi in range(G):
+            b = np.nonzero(act[gi])[0]
+            lo, hi = gs[gi], gs[gi + 1]
+            t = gi // E
+            assert np.array_equal(rows[lo:hi], t * B + b), f"block {n} group {gi}: row list"
+            assert np.array_equal(rg[lo:hi].view(np.uint32), g[gi, b].astype(np.float32).view(np.uint32)), \
+                f"block {n} group {gi}: gate values"
+            want_pos = np.full(B, -1, dtype=np.int64)
+            want_pos[b] = lo + np.arange(len(b))
+            assert np.array_equal(pos[gi], want_pos), f"block {n} group {gi}: inverse map"
+        frac.append(float(counts.sum()) / (G * B))
+    return frac

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = rmx.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.rmx_abi_version() == 5
+    assert lib.rmx_abi_version() == 6
 
 
 def test_status_strings_and_kernel_names():

@@ -23,7 +23,7 @@ import pytest
 
 import oracle
 from rankmixer_block_forward_amd import synth
-from tests.parity import rel_l2, max_abs, sample_rows, to_np
+from tests.parity import rel_l2, max_abs, sample_rows, sample_tiles, to_np
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -116,12 +116,18 @@ def test_mxfp8_100m_full_size_sampled_rows():
 @pytest.mark.slow
 def test_mxfp8_1b_full_size_sampled_rows():
     """RankMixer-1B at B = 2048 (the benchmark workload) through the MXFP8 path, against the
-    unquantized oracle on 6 sampled samples (the quantized oracle needs minutes of CPU here
-    to quantize 2.4 G weights; it is exercised at the 100M size above)."""
+    quantized oracle (its 128 weight matrices quantized on the host's threads) on 32 samples
+    stratified over the row tiles, and against the unquantized oracle on the same samples."""
+    import os
     cfg = synth.B1
     inp = synth.make_inputs(cfg, seed=0)
+    print("case MXFP8 1B B=2048", flush=True)
     o, xl = _run(cfg, inp)
-    rows = sample_rows(cfg.B, 6, seed=24)
+    rows = sample_tiles(cfg.B, 4, seed=24)
+    wq = oracle.quantize_weights(inp.layers(), workers=min(16, os.cpu_count() or 1))
+    print("weights quantized by the oracle", flush=True)
+    qo, qxl = oracle.forward_mxfp8(inp.X[rows], inp.layers(), cfg.eps, wq=wq)
+    _check("1B vs quantized oracle", o[rows], xl[rows], qo, qxl, *q_bar(cfg.L))
     uo, uxl, _ = oracle.forward(inp.X[rows], inp.layers(), cfg.eps)
     _check("1B vs unquantized oracle", o[rows], xl[rows], uo, uxl, U_REL, U_ABS)
 

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from rankmixer_block_forward_amd import synth
-from tests.parity import check, run_gpu, run_oracle, sample_rows, to_np
+from tests.parity import check, run_gpu, run_oracle, sample_rows, sample_tiles, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -164,17 +164,6 @@ def test_prepared_weights_bit_identical(B, T, D, k, L, monkeypatch):
     check(cfg, o2[rows], xl2[rows], o_ref, xl_ref, f"prepared {B}x{T}x{D} k{k} L{L}")
 
 
-def test_prepared_weights_1b_full_size():
-    cfg = synth.B1
-    inp = synth.make_inputs(cfg, seed=0)
-    o1, _ = run_gpu(cfg, inp, with_xl=False)
-    o2, xl2 = run_gpu(cfg, inp, packed=True)
-    assert np.array_equal(o1, o2)
-    rows = sample_rows(cfg.B, 4)
-    o_ref, xl_ref = run_oracle(cfg, inp, rows)
-    check(cfg, o2[rows], xl2[rows], o_ref, xl_ref, "prepared 1B B=2048")
-
-
 def test_prepared_weights_rejected_where_unsupported():
     rmx = _rmx()
     from rankmixer_block_forward_amd import binding
@@ -189,29 +178,11 @@ def test_rankmixer_100m_full_size():
     cfg = synth.M100
     inp = synth.make_inputs(cfg, seed=0)
     o, xl = run_gpu(cfg, inp)
-    rows = sample_rows(cfg.B, 24)
+    o_pk, xl_pk = run_gpu(cfg, inp, packed=True)
+    assert np.array_equal(o, o_pk) and np.array_equal(xl, xl_pk)
+    rows = sample_tiles(cfg.B, 32)
     o_ref, xl_ref = run_oracle(cfg, inp, rows)
-    check(cfg, o[rows], xl[rows], o_ref, xl_ref, "100M B=512")
-
-
-def test_rankmixer_1b_full_size():
-    cfg = synth.B1
-    inp = synth.make_inputs(cfg, seed=0)
-    o, xl = run_gpu(cfg, inp)
-    assert np.isfinite(o).all()
-    rows = sample_rows(cfg.B, 6)
-    o_ref, xl_ref = run_oracle(cfg, inp, rows)
-    check(cfg, o[rows], xl[rows], o_ref, xl_ref, "1B B=2048")
-
-
-@pytest.mark.parametrize("B", [64, 16384])
-def test_rankmixer_1b_sweep_sizes(B):
-    cfg = synth.SWEEP.with_(B=B)
-    inp = synth.make_inputs(cfg, seed=0)
-    o, xl = run_gpu(cfg, inp, with_xl=(B <= 4096))
-    rows = sample_rows(B, 4)
-    o_ref, xl_ref = run_oracle(cfg, inp, rows)
-    check(cfg, o[rows], None if xl is None else xl[rows], o_ref, xl_ref, f"1B sweep B={B}")
+    check(cfg, o[rows], xl[rows], o_ref, xl_ref, f"100M B=512 ({len(rows)} samples)")
 
 
 # ------------------------------------------------------------ boundary cases
@@ -381,19 +352,3 @@ def test_moe_zero_router_is_ffn_free_block():
     assert not g.any()
     o_ref, xl_ref, _ = oracle.forward(inp.X, inp.layers(), cfg.eps)
     check(cfg, o, xl, o_ref, xl_ref, "moe zero router")
-
-
-def test_rankmixer_1b_moe_full_size():
-    cfg = synth.MOE
-    inp = synth.make_inputs(cfg, seed=0)
-    o, _, g = _run_moe(cfg, inp, with_xl=False)
-    assert np.isfinite(o).all()
-    rows = sample_rows(cfg.B, 4)
-    sub = synth.Inputs(cfg, inp.X[rows], inp.W1, inp.b1, inp.W2, inp.b2, inp.ln1_g, inp.ln1_b,
-                       inp.ln2_g, inp.ln2_b, inp.moe)
-    o_ref, _, g_ref = oracle.forward(sub.X, sub.layers(), cfg.eps)
-    check(cfg, o[rows], None, o_ref, None, "1B MoE B=2048")
-    _check_gates(g[:, rows], g_ref, "1B MoE B=2048")
-    # the benchmark's launch: prepared expert weights, same bits
-    o2, _, g2 = _run_moe(cfg, inp, with_xl=False, packed=True)
-    assert np.array_equal(g, g2) and np.array_equal(o, o2)

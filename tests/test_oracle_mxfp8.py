@@ -177,3 +177,17 @@ def test_forward_mxfp8_is_forward_when_every_operand_is_representable():
         mx.mx_qdq = saved
     o_ref, XL_ref, _ = oracle.forward(X, [p], EPS)
     np.testing.assert_allclose(XL, XL_ref, rtol=1e-13, atol=1e-13)
+
+
+def test_prequantized_weights_give_the_same_bits():
+    """forward_mxfp8 with the weights quantized beforehand (on threads) returns exactly what
+    it returns when it quantizes them itself: the same function of the same values."""
+    from rankmixer_block_forward_amd import synth
+    cfg = synth.Config("mx-pre", B=6, T=4, D=64, k=2, L=2, bias_std=0.05)
+    inp = synth.make_inputs(cfg, seed=4)
+    a = oracle.forward_mxfp8(inp.X, inp.layers(), EPS)
+    wq = oracle.quantize_weights(inp.layers(), workers=4)
+    b = oracle.forward_mxfp8(inp.X, inp.layers(), EPS, wq=wq)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    assert np.array_equal(wq[1][3][0], oracle.mx_qdq(inp.layers()[1]["W1"][3], axis=0))
