@@ -334,6 +334,30 @@ const char* rmx_status_string(rmx_status s);
  * none. */
 const char* rmx_last_error(const rmx_handle* h);
 
+/* Forward pass that allocates nothing, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * It is rmx_block_forward for a dense Token Mixing configuration (moe_experts == 0,
+ * routing == RMX_ROUTING_MIX), with no handle: `cfg` is validated as rmx_create would
+ * (max_batch is ignored), and `w` holds W1/W2 or `packed` from rmx_pack_weights (on a
+ * handle of the same configuration; packed_mxfp8 is refused).  The results are those of
+ * rmx_block_forward with the same arguments, bit for bit.
+ * Workspace: the library keeps one array of RMX_NOALLOC_SCRATCH_BYTES of device memory per
+ * device it runs on (held from the first use on that device until the process ends) and
+ * lays the workspace of a handle with max_batch = B into it:
+ *   round256(P*D*s) + round256(P*k*D*s) + T*B*D*4 bytes,  s = sizeof(dtype),
+ *   P = T * (B rounded up to a multiple of 256) for bf16 configurations with D and k*D
+ *   multiples of 32, else P = T * B.
+ * Beyond the limit the call returns RMX_ERR_UNSUPPORTED (at the RankMixer-1B shape,
+ * T=32, D=1536, k=4, bf16: B <= 256; at T=16, D=768, k=4: B <= 1024).  Every call on one
+ * device uses that device's array, so calls on one device whose executions overlap (on
+ * different streams, or from different threads) race and must be ordered by the caller.
+ * The first call on a device sets the device up (architecture check, the array's address);
+ * no call allocates device memory.  Errors as rmx_block_forward; the detail is in
+ * rmx_last_error(NULL). */
+#define RMX_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+rmx_status rmx_block_forward_noalloc(const rmx_config* cfg, const void* X, int64_t B, const rmx_weights* w,
+                                     float* out, void* stream);
+
 /* RMX_ABI_VERSION of the built library. */
 int32_t rmx_abi_version(void);
 

@@ -6,4 +6,5 @@
 
 The library is built in-tree with ``python -m rankmixer_block_forward_amd.build``.
 """
-from .binding import (EXPORTS, Handle, RmxError, load_library, token_mix, tokenize, upload)  # noqa: F401
+from .binding import (EXPORTS, Handle, RmxError, forward_noalloc, load_library, token_mix, tokenize,  # noqa: F401
+                      upload)

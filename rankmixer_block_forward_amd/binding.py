@@ -27,7 +27,7 @@ EXPORTS = (
     "rmx_packed_weights_mxfp8_bytes", "rmx_pack_weights_mxfp8",
     "rmx_saved_bytes", "rmx_block_forward_train", "rmx_block_backward",
     "rmx_profile_enable", "rmx_profile_read", "rmx_profile_reset", "rmx_kernel_name",
-    "rmx_status_string", "rmx_last_error", "rmx_abi_version",
+    "rmx_status_string", "rmx_last_error", "rmx_abi_version", "rmx_block_forward_noalloc",
 )
 
 
@@ -85,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          vp, vp, vp]
     lib.rmx_block_forward_moe_lists.argtypes = [vp, vp, i64, ctypes.POINTER(rmx_weights), i32, i32, vp, vp, vp,
                                                 ctypes.POINTER(rmx_moe_lists), vp]
+    lib.rmx_block_forward_noalloc.argtypes = [ctypes.POINTER(rmx_config), vp, i64, ctypes.POINTER(rmx_weights),
+                                              vp, vp]
     lib.rmx_token_mix.argtypes = [vp, vp, i64, i32, i32, i32, vp]
     lib.rmx_tokenize.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, vp]
     lib.rmx_packed_weights_bytes.argtypes = [vp]
@@ -161,6 +163,35 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _weights_struct(w: dict, dtype) -> rmx_weights:
+    import torch
+    s = rmx_weights()
+    for n in WEIGHT_NAMES:
+        t = w.get(n)
+        setattr(s, n, _ptr(t, n, torch.uint8 if n == "packed_mxfp8" else dtype))
+    return s
+
+
+def forward_noalloc(X, weights: dict, T: int, D: int, k: int, L: int, dtype="bf16", ln_eps: float = 1e-5,
+                    out=None, stream=None):
+    """rmx_block_forward_noalloc: the dense forward with the library's fixed device
+    workspace (no handle, no device allocation by the library).  `out` may be given so
+    that the call allocates nothing on the Python side either."""
+    import torch
+    lib = load_library()
+    code = _dtype_code(dtype)
+    B = X.shape[0]
+    _ptr(X, "X", _torch_dtype(code), (B, T, D))
+    if out is None:
+        out = torch.empty((B, D), dtype=torch.float32, device=X.device)
+    _ptr(out, "out", torch.float32, (B, D))
+    cfg = rmx_config(T, D, k, L, code, ln_eps, B, 0, 0, RMX_ROUTING_MIX)
+    ws = _weights_struct(weights, _torch_dtype(code))
+    _check(lib.rmx_block_forward_noalloc(ctypes.byref(cfg), _ptr(X, "X"), B, ctypes.byref(ws), _ptr(out, "out"),
+                                         _stream(stream)))
+    return out
+
+
 class Handle:
     """One rmx_handle: a model configuration and its workspace on the current device."""
 
@@ -200,12 +231,7 @@ class Handle:
         self.close()
 
     def _weights(self, w: dict) -> rmx_weights:
-        import torch
-        s = rmx_weights()
-        for n in WEIGHT_NAMES:
-            t = w.get(n)
-            setattr(s, n, _ptr(t, n, torch.uint8 if n == "packed_mxfp8" else self.dtype))
-        return s
+        return _weights_struct(w, self.dtype)
 
     def packed_weights_bytes(self) -> int:
         """Bytes of the prepared copy of W1 and W2 (0 when this handle has no such path)."""

@@ -16,6 +16,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
+#include <mutex>
 #include <new>
 #include <type_traits>
 #include <string>
@@ -352,6 +354,8 @@ hipError_t run_moe_combine(rmx_handle* h, hipStream_t s, const MoeArgs& a) {
 
 }  // namespace
 
+static void set_capabilities(rmx_handle* h);
+
 extern "C" {
 
 int32_t rmx_abi_version(void) { return RMX_ABI_VERSION; }
@@ -413,13 +417,7 @@ rmx_status rmx_create(const rmx_config* cfg, rmx_handle** out_handle) {
     *ptr = static_cast<std::remove_pointer_t<std::remove_reference_t<decltype(*ptr)>>*>(q);
     total += bytes;
   };
-  h->pk_capable = cfg->moe_experts == 0 && cfg->dtype == RMX_BF16 && cfg->D % 32 == 0 &&
-                  (int64_t(cfg->k) * cfg->D) % 32 == 0;
-  h->mx_capable = h->pk_capable && cfg->D % 64 == 0 && (int64_t(cfg->k) * cfg->D) % 64 == 0;
-  h->moe_pk_capable = cfg->moe_experts > 0 && cfg->dtype == RMX_BF16 && cfg->D % 384 == 0 &&
-                      cfg->moe_hidden % 384 == 0 &&
-                      gemm_moe_supported(cfg->moe_hidden, cfg->D, int64_t(cfg->T) * cfg->max_batch, true) &&
-                      gemm_moe_supported(cfg->D, cfg->moe_hidden, cfg->max_batch, true);
+  set_capabilities(h);
   const size_t prow = h->pk_capable ? size_t(cfg->T) * size_t(pk_rows(cfg->max_batch)) : rows;
   if (rows > 0) {
     alloc(&h->S, prow * cfg->D * esz);
@@ -471,6 +469,18 @@ rmx_status rmx_destroy(rmx_handle* h) {
   for (auto e : h->free_events) (void)hipEventDestroy(e);
   delete h;
   return RMX_OK;
+}
+
+// Which prepared-operand paths a handle's configuration can run.
+static void set_capabilities(rmx_handle* h) {
+  const rmx_config* cfg = &h->cfg;
+  h->pk_capable = cfg->moe_experts == 0 && cfg->dtype == RMX_BF16 && cfg->D % 32 == 0 &&
+                  (int64_t(cfg->k) * cfg->D) % 32 == 0;
+  h->mx_capable = h->pk_capable && cfg->D % 64 == 0 && (int64_t(cfg->k) * cfg->D) % 64 == 0;
+  h->moe_pk_capable = cfg->moe_experts > 0 && cfg->dtype == RMX_BF16 && cfg->D % 384 == 0 &&
+                      cfg->moe_hidden % 384 == 0 &&
+                      gemm_moe_supported(cfg->moe_hidden, cfg->D, int64_t(cfg->T) * cfg->max_batch, true) &&
+                      gemm_moe_supported(cfg->D, cfg->moe_hidden, cfg->max_batch, true);
 }
 
 // The forward pass; with `saved` (training) it also keeps S, U, H and the pre-LN2 rows of
@@ -1321,3 +1331,88 @@ rmx_status rmx_profile_reset(rmx_handle* h) {
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ no-allocation forward
+// rmx_block_forward_noalloc runs the dense forward with its workspace (S, the hidden H and
+// the pre-LN2 rows Y, sized and laid out as a handle's for max_batch = B) carved out of
+// `scratch`, a fixed array in device memory that the code object carries, so that the call
+// allocates nothing.  Each device holds its own copy of the array; host code reaches it only
+// through the device address hipGetSymbolAddress returns, taken once per device.
+static __device__ __align__(256) unsigned char scratch[RMX_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_noalloc_mutex;
+std::atomic<unsigned char*> g_noalloc_ptr[NOALLOC_MAX_DEVICES];
+
+// Once per device (the device current): the architecture check, the kernels' launch
+// attributes and the device address of `scratch`.
+rmx_status noalloc_device_scratch(int dev, unsigned char** out) {
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+    return fail(nullptr, RMX_ERR_UNSUPPORTED, "device %d: the no-allocation path serves devices 0..%d", dev,
+                NOALLOC_MAX_DEVICES - 1);
+  unsigned char* p = g_noalloc_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+    p = g_noalloc_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int d = -1;
+      rmx_status st = check_device_arch(nullptr, &d);
+      if (st != RMX_OK) return st;
+      hipError_t e;
+      if ((e = rows_init()) != hipSuccess || (e = gemm_init()) != hipSuccess)
+        return fail(nullptr, RMX_ERR_HIP, "kernel set-up failed: %s", hipGetErrorString(e));
+      void* q = nullptr;
+      if ((e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch))) != hipSuccess || !q) {
+        (void)hipGetLastError();
+        return fail(nullptr, RMX_ERR_HIP, "device address of the scratch array: %s", hipGetErrorString(e));
+      }
+      p = static_cast<unsigned char*>(q);
+      g_noalloc_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return RMX_OK;
+}
+
+}  // namespace
+
+extern "C" rmx_status rmx_block_forward_noalloc(const rmx_config* cfg, const void* X, int64_t B,
+                                                 const rmx_weights* w, float* out, void* stream) {
+  clear_error(nullptr);
+  rmx_status st = validate_config(cfg);
+  if (st != RMX_OK) return st;
+  if (cfg->moe_experts != 0 || cfg->routing != RMX_ROUTING_MIX)
+    return fail(nullptr, RMX_ERR_UNSUPPORTED, "the no-allocation forward runs the dense Token Mixing block");
+  if (!w) return fail(nullptr, RMX_ERR_INVALID_ARG, "weights is NULL");
+  if (w->packed_mxfp8) return fail(nullptr, RMX_ERR_UNSUPPORTED, "the no-allocation forward runs bf16 or fp32 weights");
+  if (B < 0) return fail(nullptr, RMX_ERR_INVALID_ARG, "B=%lld < 0", (long long)B);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(nullptr, RMX_ERR_UNSUPPORTED, "no HIP device");
+  }
+  unsigned char* base = nullptr;
+  if ((st = noalloc_device_scratch(dev, &base)) != RMX_OK) return st;
+
+  // the workspace of a handle created for max_batch = B
+  rmx_handle tmp;
+  tmp.cfg = *cfg;
+  tmp.cfg.max_batch = B;
+  tmp.device = dev;
+  set_capabilities(&tmp);
+  const size_t esz = dtype_size(cfg->dtype), T = cfg->T, D = cfg->D, kD = size_t(cfg->k) * cfg->D;
+  const size_t prow = tmp.pk_capable ? T * size_t(pk_rows(B)) : T * size_t(B);
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t offH = up(prow * D * esz), offY = offH + up(prow * kD * esz), need = offY + T * size_t(B) * D * 4;
+  if (need > RMX_NOALLOC_SCRATCH_BYTES)
+    return fail(nullptr, RMX_ERR_UNSUPPORTED, "B=%lld needs %zu bytes of workspace; the no-allocation limit is %zu",
+                (long long)B, need, size_t(RMX_NOALLOC_SCRATCH_BYTES));
+  tmp.S = base;
+  tmp.H = base + offH;
+  tmp.Y = reinterpret_cast<float*>(base + offY);
+  st = forward_impl(&tmp, X, B, w, cfg->L, cfg->k, out, nullptr, nullptr, nullptr, 0, stream);
+  if (st != RMX_OK) g_thread_error = tmp.last_error;
+  return st;
+}
