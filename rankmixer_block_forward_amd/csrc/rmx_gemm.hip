@@ -915,6 +915,217 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384(GemmArgs 
                           [&](int r) { return m0 + r < M ? m0 + r : -1; });
 }
 
+// ------------------------------------------------- 256 x 192 tiles, two workgroups per CU
+// A 256 x 384 tile holds 384 fp32 accumulators per lane and fills a SIMD's registers with one
+// wave, so its epilogue (bias, GELU, bf16 stores: about a quarter of the GELU product's time
+// at the 1B shape) leaves the matrix cores idle.  A 256 x 192 tile needs 192 accumulators
+// (AGPRs) and fits in 256 registers per lane with a 2-stage ring of 28 KB stages, so two
+// workgroups share a CU and one's epilogue runs beside the other's K loop.  It copies 40 %
+// more operand bytes per FLOP than the 256 x 384 tile; measured at the 1B shape, B = 2048:
+// GELU product 1.17 against 1.21 ms, residual product level (1.035 against 1.03 ms), so the
+// launch takes it for the GELU epilogue.  Waves 2 x 2 of 128 x 96 (4 x 3 blocks); per block
+// the same MFMAs in the same K order as the other tile shapes, so the bits are the same.
+// W^T rows of a tile: 192 nt .. 192 nt + 191, which may straddle two 256-row packed blocks;
+// each 16-row piece of a stage lies inside one block (the swizzle depends on row % 8).
+constexpr int BN3 = 192;
+constexpr int ST3_A = BM * BK * 2;                 // 16 KB of A per stage
+constexpr int ST3 = ST3_A + BN3 * BK * 2;          // + 12 KB of W^T
+constexpr int LD3 = 32 + 4;                        // epilogue staging rows: one 32-column block
+
+__device__ __forceinline__ void mfma_tile_pk3(f32x16_t (&acc)[4][3], __amdgpu_buffer_rsrc_t rA,
+                                              __amdgpu_buffer_rsrc_t rW, lds_u8* smem, uint32_t lds0, int K, int nt,
+                                              int wave, int lane) {
+  const int nk = K / BK;
+  uint32_t voffW[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const int row = BN3 * nt + 16 * (wave + 4 * c);  // first W^T row of the piece
+    voffW[c] = uint32_t(row >> 8) * uint32_t(nk) * 16384u + uint32_t(row & 255) * 64u + uint32_t(lane) * 16u;
+  }
+  // copy c (0..6) of K step kt into stage `stage`: pieces wave + 4 c of A (c < 4) and
+  // wave + 4 (c - 4) of W^T; steps past the end reload the last (in bounds, never read)
+  auto copy = [&](int kt, int stage, int c) {
+    kt = kt < nk ? kt : nk - 1;
+    const uint32_t sbase = lds0 + uint32_t(stage) * ST3;
+    if (c < 4) {
+      const uint32_t piece = uint32_t(wave + 4 * c);
+      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), piece * 1024u + uint32_t(lane) * 16u, rA,
+                  kt * 16384);
+    } else {
+      const uint32_t q = uint32_t(wave + 4 * (c - 4));
+      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + ST3_A + q * 1024u), voffW[c - 4], rW, kt * 16384);
+    }
+  };
+  const int wm = wave >> 1, wn = wave & 1;
+  uint32_t aoff[2], boff[2];  // row block i / column block j at + 2048 i / + 2048 j
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int c = kk * 2 + (lane >> 5);
+    const int m = wm * 128 + (lane & 31);
+    aoff[kk] = uint32_t(m * 64 + ((c ^ pk_swz(m)) << 4));
+    const int n = wn * 96 + (lane & 31);
+    boff[kk] = uint32_t(ST3_A + n * 64 + ((c ^ pk_swz(n)) << 4));
+  }
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  u32x4_t a0[4], a1[4], b[3];
+  auto read_a = [&](u32x4_t (&a)[4], const lds_u8* sp, int kk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const lds_u32x4*>(sp + aoff[kk] + i * 2048);
+  };
+  auto read_b = [&](const lds_u8* sp, int kk, int j) {
+    b[j] = *reinterpret_cast<const lds_u32x4*>(sp + boff[kk] + j * 2048);
+  };
+  auto mm = [&](const u32x4_t (&a)[4], int i, int j) {
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[j]),
+                                                        __builtin_bit_cast(bf16x8_t, a[i]), acc[i][j], 0, 0, 0);
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // prologue: steps 0 and 1; wait for step 0 (7 loads per step)
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int c = 0; c < 7; ++c) copy(st, st, c);
+  asm volatile("s_waitcnt vmcnt(7)\n\ts_barrier" ::: "memory");
+  read_a(a0, smem, 0);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) read_b(smem, 0, j);
+  int stage = 0;
+  for (int it = 0; it < nk; ++it) {
+    const lds_u8* sp = smem + stage * ST3;
+    const int nstage = stage ^ 1;
+    // sub-step 0 on a0 / b; sub-step 1's fragments read behind the MFMAs that free them
+    read_a(a1, sp, 1);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mm(a0, i, j);
+      __builtin_amdgcn_sched_barrier(0);
+      read_b(sp, 1, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // every read of this stage has returned; after the barrier step it+1 is visible and this
+    // stage takes step it+2
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // sub-step 1 on a1 / b; the refill of this stage spread over its 12 MFMAs
+    const lds_u8* np = smem + nstage * ST3;
+    read_a(a0, np, 0);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mm(a1, i, j);
+        const int q = 4 * j + i;
+        if (q == 0 || q == 2 || q == 4 || q == 6 || q == 8 || q == 9 || q == 10) {
+          __builtin_amdgcn_sched_barrier(0);
+          copy(it + 2, stage, q <= 6 ? q / 2 : q - 4);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      read_b(np, 0, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    stage = nstage;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// Epilogue of a 256 x 192 tile (the arithmetic of tile_epilogue6): per 32 x 32 block, the
+// accumulators are staged through LDS so that each lane owns 8 consecutive columns of one row
+// (4 lanes per row, 16 rows per pass).  Rows past M are not stored.
+template <int EPI>
+__device__ __forceinline__ void tile_epilogue3(const f32x16_t (&acc)[4][3], float* smem_f, const GemmArgs& p, int g,
+                                               const bf16_t* bias_g, int n0, int m0, int wave, int lane) {
+  const int M = p.M, N = p.N;
+  const int wrow0 = (wave >> 1) * 128, wcol0 = (wave & 1) * 96;
+  float* st = smem_f + wave * 32 * LD3;
+  const int col8 = (lane & 3) * 8;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int n = n0 + wcol0 + j * 32 + col8;
+    float bias[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bias[e] = 0.f;
+    if (bias_g) load8(bias_g + n, bias);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(st + (lane & 31) * LD3 + 8 * g4 + 4 * (lane >> 5)) =
+            make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]);
+      // the staging rows are private to this wave, whose LDS operations complete in order
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int row = pass * 16 + (lane >> 2);
+        const int m = m0 + wrow0 + i * 32 + row;
+        float v[8];
+        const float4 x0 = *reinterpret_cast<const float4*>(st + row * LD3 + col8);
+        const float4 x1 = *reinterpret_cast<const float4*>(st + row * LD3 + col8 + 4);
+        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+        if (m < M) {
+          const size_t pko = size_t(g) * size_t(pk_rows(M)) * N + pk_off(m, n, N);
+          if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[e]);
+            store8(static_cast<bf16_t*>(p.C) + pko, v);
+          } else {
+            float rr[8];
+            load8(static_cast<const bf16_t*>(p.R) + pko, rr);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = v[e] + bias[e] + rr[e];
+            store8(static_cast<float*>(p.C) + size_t(g) * size_t(p.sc) + size_t(m) * size_t(p.ldc) + n, v);
+          }
+        }
+      }
+      asm volatile("" ::: "memory");
+    }
+  }
+}
+
+// Dense per-token product on packed operands with 256 x 192 tiles, two workgroups per CU:
+// G * ceil(M/256) * N/192 workgroups, N % 192 == 0; EPI_GELU or EPI_RESID.
+template <int EPI>
+__global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_n192(GemmArgs p) {
+  static_assert(EPI == EPI_GELU || EPI == EPI_RESID, "256 x 192 tiles serve the inference epilogues");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[2 * ST3];
+  lds_u8* const smem = (lds_u8*)smem_g;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nMt = (M + BM - 1) / BM, nNt = N / BN3;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = id / (nMt * nNt);
+  const int rem = id - g * nMt * nNt;
+  // bands of TILE_BAND row tiles, M-fastest inside a band (as in the 256 x 256 kernel)
+  const int band = rem / (TILE_BAND * nNt);
+  const int in_band = rem - band * TILE_BAND * nNt;
+  const int bm = min(TILE_BAND, nMt - band * TILE_BAND);
+  const int nt = in_band / bm, mt = band * TILE_BAND + (in_band - (in_band / bm) * bm);
+  // the tile's A blocks (packed row block mt, K/32 x 16 KB) and the token's whole W^T
+  // (pk_rows(N) rows; slices < 2^31 bytes, checked at launch)
+  const uint32_t blk = uint32_t(K / BK) * 16384u;
+  const uint32_t wbytes = uint32_t(pk_rows(N) / 256) * blk;
+  const __amdgpu_buffer_rsrc_t rA =
+      make_rsrc(static_cast<const uint16_t*>(p.A) + (size_t(g) * nMt + mt) * (size_t(blk) / 2), blk);
+  const __amdgpu_buffer_rsrc_t rW =
+      make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * (size_t(wbytes) / 2), wbytes);
+  f32x16_t acc[4][3];
+  mfma_tile_pk3(acc, rA, rW, smem, lds0, K, nt, wave, lane);
+  const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
+  tile_epilogue3<EPI>(acc, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN3, mt * BM, wave, lane);
+}
+
 // Sparse-MoE grouped GEMM on prepared expert weights with 256 x 384 tiles: the persistent
 // tile walk of gemm_bf16_moe (same device-built tile table, each XCD a contiguous range of
 // tiles, row tiles fastest inside a group), the K loop of gemm_bf16_mfma_n384 with A gathered
@@ -1576,14 +1787,19 @@ namespace {
 // 256 x 384: 301 against 334 us, and B = 640 and 768 GEMM2, 3 rounds against 2: 454 against
 // 486 us and 480 against 506 us; at B = 256 GEMM2 one round of them takes 188 us against
 // 198 for one round of 256 x 256 tiles).
-// The environment variable RMX_WIDE_TILES = always / half / never forces 256 x 384,
-// 128 x 384 or 256 x 256 (tests and tuning; read at each launch); all give the same bits.
-enum TileShape { TILES_256 = 0, TILES_256x384 = 1, TILES_128x384 = 2 };
+// The environment variable RMX_WIDE_TILES = always / half / pair / never forces 256 x 384,
+// 128 x 384, 256 x 192 (two workgroups per CU) or 256 x 256 (tests and tuning; read at each
+// launch); all give the same bits.  Unforced, the GELU product takes 256 x 192 tiles where
+// the choice above gives 256 x 384 and N % 192 == 0 (measured at the 1B shape: the same
+// number of rounds of twice as many tiles, 1.17 against 1.21 ms at B = 2048).
+enum TileShape { TILES_256 = 0, TILES_256x384 = 1, TILES_128x384 = 2, TILES_256x192 = 3 };
 
-TileShape pick_tiles(const GemmArgs& a) {
+TileShape pick_tiles(const GemmArgs& a, int epi) {
   const char* force = getenv("RMX_WIDE_TILES");
   if (force && strcmp(force, "never") == 0) return TILES_256;
-  if (a.N % BN6 != 0 || uint64_t(pk_rows(a.N)) * uint64_t(a.K) * 2u >= (uint64_t(1) << 31)) return TILES_256;
+  const bool w_ok = uint64_t(pk_rows(a.N)) * uint64_t(a.K) * 2u < (uint64_t(1) << 31);
+  if (force && strcmp(force, "pair") == 0) return (w_ok && a.N % BN3 == 0) ? TILES_256x192 : TILES_256;
+  if (a.N % BN6 != 0 || !w_ok) return TILES_256;
   if (force && strcmp(force, "always") == 0) return TILES_256x384;
   if (force && strcmp(force, "half") == 0) return TILES_128x384;
   int dev = 0, cus = 256;
@@ -1595,7 +1811,8 @@ TileShape pick_tiles(const GemmArgs& a) {
   // relative tile durations 20 : 28 : 17 (256 x 256 : 256 x 384 : 128 x 384), times rounds
   const int64_t c4 = 20 * rounds(t4), c6 = 28 * rounds(t6), ch = 17 * rounds(th);
   if (ch < c6 && ch < c4) return TILES_128x384;
-  return c6 < c4 ? TILES_256x384 : TILES_256;
+  if (c6 >= c4) return TILES_256;
+  return epi == EPI_GELU ? TILES_256x192 : TILES_256x384;
 }
 
 // 64-row tiles 128 columns wide (packed products) where the 256-wide ones number between
@@ -1635,7 +1852,15 @@ hipError_t launch_dense_mfma(int epi, const GemmArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((gemm_bf16_mfma_m64<EPI_RESID, PK>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
     return hipGetLastError();
   }
-  const TileShape shape = PK && (epi == EPI_GELU || epi == EPI_RESID) ? pick_tiles(a) : TILES_256;
+  const TileShape shape = PK && (epi == EPI_GELU || epi == EPI_RESID) ? pick_tiles(a, epi) : TILES_256;
+  if (shape == TILES_256x192) {
+    const int tiles3 = a.G * ((a.M + BM - 1) / BM) * (a.N / BN3);
+    if (epi == EPI_GELU)
+      hipLaunchKernelGGL((gemm_bf16_mfma_n192<EPI_GELU>), dim3(tiles3), dim3(MFMA_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_mfma_n192<EPI_RESID>), dim3(tiles3), dim3(MFMA_THREADS), 0, stream, a);
+    return hipGetLastError();
+  }
   if (shape == TILES_256x384) {
     const int tiles6 = a.G * ((a.M + BM - 1) / BM) * (a.N / BN6);
     if (epi == EPI_GELU)
