@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--sweep", action="store_true", help="one line per serving batch size")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-samples", type=int, default=1152)
+    p.add_argument("--cpu-samples", type=int, default=768)
     p.add_argument("--routing-comparison", action="store_true",
                    help="Token Mixing versus the self-attention comparator at the 100M and 1B shapes")
     p.add_argument("--mxfp8", action="store_true",
@@ -55,22 +55,25 @@ def parse():
                    help="also time the same forward captured once in a HIP graph and replayed "
                         "(torch.cuda.CUDAGraph on the caller's stream): adds a hip_graph object")
     p.add_argument("--calibrate-copy", action="store_true",
-                   help="after the timed region, run the library's token-mixing kernel (a pure "
-                        "permutation copy of the input, bytes known) three times: the reference "
-                        "dispatches for scaling HBM byte counters")
+                   help="after the timed region, run a plain streaming kernel (torch.neg over 1 GiB "
+                        "of fp32) three times on cold sources: reference dispatches of known bytes "
+                        "for the memory-traffic counters")
     return p.parse_args()
 
 
-def gemm_counts(cfg, B):
+def gemm_counts(cfg, B, mxfp8=False):
     """Algorithmic FLOPs and HBM bytes of one launch of each grouped GEMM.
 
     GEMM1: S[T,B,D] x W1[T,D,kD] -> H[T,B,kD];  GEMM2: H x W2[T,kD,D] + S -> Y[T,B,D] fp32.
-    Bytes: weights once + activations read once + output written once (bf16 = 2 B)."""
+    Bytes: weights once + activations read once + output written once.  Operands of the
+    products take 2 B per value in bf16; in MXFP8 1 B per code plus one scale byte per 32
+    values (33/32 B), while the residual S stays bf16 and Y fp32."""
     T, D, kD = cfg.T, cfg.D, cfg.kD
+    op = 33.0 / 32.0 if mxfp8 else 2.0
     flops = 2.0 * B * T * D * kD
-    w = 2.0 * T * D * kD
-    g1 = w + 2.0 * B * T * D + 2.0 * B * T * kD
-    g2 = w + 2.0 * B * T * kD + 2.0 * B * T * D + 4.0 * B * T * D
+    w = op * T * D * kD
+    g1 = w + op * B * T * D + op * B * T * kD
+    g2 = w + op * B * T * kD + 2.0 * B * T * D + 4.0 * B * T * D
     return {"gemm1_gelu": (flops, g1), "gemm2_residual": (flops, g2)}
 
 
@@ -128,31 +131,40 @@ def time_forward(cfg, B, steps, warmup, calibrate_copy=False, mxfp8=False, prepa
     moe = moe_active_flops(h, X, w, cfg, B) if cfg.E > 0 else None
     calib = []
     if calibrate_copy:
-        # three 1 GiB sources, written now and cold (out of L2 and the memory-side cache)
-        # by the time they are copied after the timed region
-        Bc = max(1, (1 << 30) // (cfg.T * cfg.D * X.element_size()))
-        calib = [(torch.zeros((Bc, cfg.T, cfg.D), dtype=X.dtype, device="cuda"),
-                  torch.empty((Bc, cfg.T, cfg.D), dtype=X.dtype, device="cuda")) for _ in range(3)]
+        # three 1 GiB fp32 sources, written now and cold (out of the L2 and the memory-side
+        # cache) by the time a plain streaming kernel (torch.neg) reads each once and writes
+        # 1 GiB after the timed region: reference dispatches of known bytes for the counters
+        n = (1 << 30) // 4
+        calib = [(torch.zeros(n, dtype=torch.float32, device="cuda"),
+                  torch.empty(n, dtype=torch.float32, device="cuda")) for _ in range(3)]
     for _ in range(warmup):
         h.forward(X, w, out=out)
     torch.cuda.synchronize()
-    h.profile_reset()
-    h.profile_enable(True)
-    torch.cuda.synchronize()
+    # the timed region: the production launch sequence, nothing recorded between launches
     t0 = time.perf_counter()
     for _ in range(steps):
         h.forward(X, w, out=out)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # then the same steps again with a pair of HIP events around every launch (on the stream
+    # the kernels run on): the per-kernel durations of the roofline and the breakdown
+    h.profile_reset()
+    h.profile_enable(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        h.forward(X, w, out=out)
+    torch.cuda.synchronize()
+    prof_elapsed = time.perf_counter() - t1
     h.profile_enable(False)
     prof = h.profile_read()
+    prof["_profiled_ms_per_step"] = prof_elapsed / steps * 1e3
     assert torch.isfinite(out).all().item(), "non-finite output"
     if calib:
         for src, dst in calib:
-            rmx.token_mix(src, dst)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        src = calib[0][0]
-        print(f"[bench] calibration copies: 3 x token mix of {src.numel() * src.element_size()} bytes "
+        print(f"[bench] calibration copies: 3 x streaming negation of {calib[0][0].numel() * 4} bytes "
               f"read and written, cold sources", file=sys.stderr, flush=True)
         del calib
     h.close()
@@ -199,7 +211,7 @@ def time_graph(cfg, B, steps, warmup, mxfp8=False):
 
 
 def roofline(cfg, B, prof, peak_tflops=PEAK_BF16_TFLOPS):
-    counts = gemm_counts(cfg, B)
+    counts = gemm_counts(cfg, B, mxfp8=peak_tflops == PEAK_FP8_TFLOPS)
     ridge = peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9)
     # dominant kernel: the grouped GEMM with the larger total time
     kern = max(counts, key=lambda k: prof.get(k, {}).get("total_ms", 0.0))
@@ -256,26 +268,29 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(cfg, n, single_thread=True):
+def cpu_baseline(cfg, n, single_thread=True, repeats=3):
     """The fp64 oracle, as it stands, on n samples of the same workload with the BLAS
-    threads the host gives it; with single_thread, also on n/16 samples with one thread."""
+    threads the host gives it, the median of `repeats` timed runs over the same inputs; with
+    single_thread, also on n/16 samples with one thread (median of as many runs)."""
     import numpy as np
     import oracle
     from rankmixer_block_forward_amd import synth
     threads = blas_threads()
+    inp = synth.make_inputs(cfg.with_(B=n), seed=0)
+    layers = inp.layers()
 
     def run(m):
-        inp = synth.make_inputs(cfg.with_(B=m), seed=0)
         t0 = time.perf_counter()
-        o, _, _ = oracle.forward(inp.X, inp.layers(), cfg.eps)
+        o, _, _ = oracle.forward(inp.X[:m], layers, cfg.eps)
         el = time.perf_counter() - t0
         assert np.isfinite(o).all()
         return el
 
-    el = run(n)
+    els = sorted(run(n) for _ in range(repeats))
+    el = els[len(els) // 2]
     res = {"value": round(n / el, 3), "unit": "samples/s", "cores": int(threads), "kind": "oracle",
            "sample": f"{n} samples of {cfg.name} (T={cfg.T}, D={cfg.D}, k={cfg.k}, L={cfg.L}), "
-                     f"fp64 NumPy, {el:.1f} s",
+                     f"fp64 NumPy, median of {repeats} runs: " + ", ".join(f"{e:.1f}" for e in els) + " s",
            "cpu_model": cpu_model(), "logical_cpus": os.cpu_count()}
     if single_thread:
         try:
@@ -284,9 +299,11 @@ def cpu_baseline(cfg, n, single_thread=True):
             return res
         n1 = max(1, n // 16)
         with threadpool_limits(limits=1, user_api="blas"):
-            el1 = run(n1)
+            els1 = sorted(run(n1) for _ in range(repeats))
+        el1 = els1[len(els1) // 2]
         res["single_thread"] = {"value": round(n1 / el1, 3), "unit": "samples/s",
-                                "sample": f"{n1} samples, one BLAS thread, {el1:.1f} s"}
+                                "sample": f"{n1} samples, one BLAS thread, median of {repeats} runs: "
+                                          + ", ".join(f"{e:.1f}" for e in els1) + " s"}
     return res
 
 
@@ -425,7 +442,7 @@ def bench_backward(cfg, B, steps, warmup, cpu_samples):
                    "L": cfg.L, "parallelism": "single GPU"},
         "tflops": round(flops / (ms / 1e3) / 1e12, 2),
         "frac_bf16_peak": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "kernels_ms_per_step": {k: round(v["total_ms"] / steps, 4) for k, v in prof.items() if k != "_dropped"},
+        "kernels_ms_per_step": {k: round(v["total_ms"] / steps, 4) for k, v in prof.items() if not k.startswith("_")},
         "roofline": roof,
     }
     if cpu_samples:
@@ -468,11 +485,11 @@ def bench_routing(steps, warmup):
             "mix": {"samples_per_s": round(mix.B / (ms_mix / 1e3), 1), "ms_per_step": round(ms_mix, 4),
                     "flops_per_sample": f_mix, "ffn_params": p_mix,
                     "kernels_ms_per_step": {n: round(v["total_ms"] / steps, 4) for n, v in prof_mix.items()
-                                            if n != "_dropped"}},
+                                            if not n.startswith("_")}},
             "attention": {"samples_per_s": round(mix.B / (ms_att / 1e3), 1), "ms_per_step": round(ms_att, 4),
                           "flops_per_sample": f_att, "params": p_att,
                           "kernels_ms_per_step": {n: round(v["total_ms"] / steps, 4) for n, v in prof_att.items()
-                                                  if n != "_dropped"}},
+                                                  if not n.startswith("_")}},
             "flops_ratio": round(f_att / f_mix, 4), "param_ratio": round(p_att / p_mix, 4),
             "time_ratio": round(ms_att / ms_mix, 4)}), flush=True)
 
@@ -527,7 +544,8 @@ def main():
             "tflops": round(tflops, 2),
             "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
             "kernels_ms_per_step": {k: round(v["total_ms"] / args.steps, 4) for k, v in prof.items()
-                                    if k != "_dropped"},
+                                    if not k.startswith("_")},
+            "profiled_ms_per_step": round(prof["_profiled_ms_per_step"], 4),
             "roofline": (moe_roofline(cfg, B, prof, moe) if moe is not None else
                          roofline(cfg, B, prof, PEAK_FP8_TFLOPS if args.mxfp8 else PEAK_BF16_TFLOPS)),
         }

@@ -1,15 +1,33 @@
-"""HBM traffic per kernel launch from rocprofv3 counter runs.
+"""Memory traffic per kernel launch from rocprofv3 counter runs.
 
-Two counter passes of the same bench command (rocprofv3 --pmc FETCH_SIZE, then
---pmc WRITE_SIZE, both with --output-format csv) give per-dispatch KiB read from and
-written to HBM through the L2.  The bench's --calibrate-copy dispatches of the token-mixing
-kernel move a known number of bytes each way; what the counters read for them gives the
-scale factor from counter KiB to bytes, applied to every other kernel.  The record is
-keyed by the hash of the sources the GEMM kernels are compiled from, so the bench reports
-it only while they are unchanged.
+The traffic record counts the requests the L2 (TCC) sends to memory, by size.  One counter
+pass of a bench command with TCC_EA0_RDREQ_sum, TCC_EA0_RDREQ_32B_sum,
+TCC_EA0_RDREQ_64B_sum and TCC_EA0_RDREQ_128B_sum (--output-format csv), and one with
+TCC_EA0_WRREQ_sum and TCC_EA0_WRREQ_64B_sum, give per dispatch
+    read bytes  = 32 n32 + 64 n64 + 128 n128
+    write bytes = 64 n64w + 32 (n_w - n64w).
+These are the bytes that leave the L2 towards the memory fabric (the 256 MB memory-side
+cache and HBM behind it; the counters cannot tell which of the two served a request).
+No scale factor enters.  The derived FETCH_SIZE counter of this part prices 128-byte reads
+through TCC_BUBBLE, which reads 0 on gfx950, and so reports half of every 128-byte read.
+
+    python -m rankmixer_block_forward_amd.counters --reads R.csv --writes W.csv \\
+        --workload "rankmixer-1b B=2048" --out profiles/traffic_counters.json
+
+FETCH_SIZE / WRITE_SIZE passes scaled by a plain streaming copy of known size (the bench's
+--calibrate-copy dispatches) give the same figures for kernels whose reads are all 128-byte
+requests:
 
     python -m rankmixer_block_forward_amd.counters --fetch F.csv --write W.csv \\
-        --workload "rankmixer-1b B=2048" --copy-bytes N --out profiles/traffic_counters.json
+        --workload "rankmixer-1b B=2048" --copy-bytes N
+
+The record is keyed by the hash of the sources the GEMM kernels are compiled from, so the
+bench reports it only while they are unchanged.
+
+Per-kernel durations of a kernel-trace run (rocprofv3 --kernel-trace --stats; the results
+database):
+
+    python -m rankmixer_block_forward_amd.counters --stats run_results.db
 
 A pass of SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and SQ_INSTS_VALU_MFMA_MOPS_BF16 gives the
 matrix cores' utilisation and the clock they ran at, per kernel:
@@ -33,11 +51,14 @@ GEMM_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("rmx_gemm.hip", "rmx_devi
 
 # kernel-name patterns -> the names the library's profiling uses
 KERNELS = [
-    (re.compile(r"gemm_bf16_mfma(_n384)?<0[,>]"), "gemm1_gelu"),
-    (re.compile(r"gemm_bf16_mfma(_n384)?<1[,>]"), "gemm2_residual"),
-    (re.compile(r"gemm_bf16_moe<2>"), "moe_ffn1"),
-    (re.compile(r"gemm_bf16_moe<3>"), "moe_ffn2"),
-    (re.compile(r"token_mix_kernel"), "copy"),
+    (re.compile(r"gemm_bf16_mfma(_n384|_n192|_m64)?<0[,>]"), "gemm1_gelu"),
+    (re.compile(r"gemm_bf16_mfma(_n384|_n192|_m64)?<1[,>]"), "gemm2_residual"),
+    (re.compile(r"gemm_bf16_moe(_n384)?<2>"), "moe_ffn1"),
+    (re.compile(r"gemm_bf16_moe(_n384)?<3>"), "moe_ffn2"),
+    (re.compile(r"rows_kernel<[^>]*, 0>"), "rows_first"),
+    (re.compile(r"rows_kernel<[^>]*, 1>"), "rows_ln2_mix_ln1"),
+    (re.compile(r"rows_kernel<[^>]*, 2>"), "rows_ln2_pool"),
+    (re.compile(r"vectorized_elementwise_kernel<\d+, at::native::neg_kernel"), "copy"),
 ]
 
 
@@ -49,7 +70,7 @@ def classify(name):
 
 
 def per_dispatch_kib(path, counter):
-    """Mean counter value (KiB) per dispatch, by kernel class."""
+    """Mean counter value per dispatch, by kernel class: {class: (mean, dispatches)}."""
     vals = defaultdict(list)
     with open(path, newline="") as f:
         for row in csv.DictReader(f):
@@ -59,6 +80,59 @@ def per_dispatch_kib(path, counter):
             if k is not None:
                 vals[k].append(float(row["Counter_Value"]))
     return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+
+def request_bytes(reads_csv, writes_csv):
+    """Bytes read and written per dispatch, by kernel class, from the request counts by size:
+    {class: {"read": bytes, "write": bytes, "dispatches": n, "read_requests": {...}}}."""
+    n32 = per_dispatch_kib(reads_csv, "TCC_EA0_RDREQ_32B_sum")
+    n64 = per_dispatch_kib(reads_csv, "TCC_EA0_RDREQ_64B_sum")
+    n128 = per_dispatch_kib(reads_csv, "TCC_EA0_RDREQ_128B_sum")
+    ntot = per_dispatch_kib(reads_csv, "TCC_EA0_RDREQ_sum")
+    w_all = per_dispatch_kib(writes_csv, "TCC_EA0_WRREQ_sum")
+    w64 = per_dispatch_kib(writes_csv, "TCC_EA0_WRREQ_64B_sum")
+    out = {}
+    for k in sorted(set(n128) & set(w_all)):
+        a, b, c = n32.get(k, (0.0, 0))[0], n64.get(k, (0.0, 0))[0], n128[k][0]
+        wa, wb = w_all[k][0], w64.get(k, (0.0, 0))[0]
+        out[k] = {"read": 32.0 * a + 64.0 * b + 128.0 * c, "write": 64.0 * wb + 32.0 * (wa - wb),
+                  "dispatches": [n128[k][1], w_all[k][1]],
+                  "read_requests": {"32B": a, "64B": b, "128B": c, "all": ntot.get(k, (0.0, 0))[0]}}
+    return out
+
+
+def build_request_record(reads_csv, writes_csv, workload):
+    """The traffic record (bytes per launch by kernel class) from the request-size passes."""
+    kernels = {}
+    for k, e in request_bytes(reads_csv, writes_csv).items():
+        if k == "copy":
+            continue
+        kernels[k] = {"workload": workload, "bytes_per_launch": round(e["read"] + e["write"]),
+                      "read_bytes": round(e["read"]), "write_bytes": round(e["write"]),
+                      "dispatches": e["dispatches"]}
+    return {"gemm_source_sha256_16": gemm_hash(),
+            "method": "L2-to-memory requests by size (TCC_EA0_RDREQ_32B/64B/128B, TCC_EA0_WRREQ/_64B)",
+            "kernels": kernels}
+
+
+def kernel_stats(db_path):
+    """Per-kernel totals of a rocprofv3 kernel-trace results database: a list of
+    (kernel name, calls, total us, average us, percentage, min us, max us), longest total
+    first (min and max from the per-dispatch durations, in ns in the database)."""
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    try:
+        rows = con.execute("select name, total_calls, total_duration, average, percentage from top_kernels "
+                           "order by total_duration desc").fetchall()
+        ext = {}
+        try:
+            for name, lo, hi in con.execute("select name, min(duration), max(duration) from kernels group by name"):
+                ext[name] = (lo / 1e3, hi / 1e3)
+        except sqlite3.Error:
+            pass
+    finally:
+        con.close()
+    return [tuple(r) + ext.get(r[0], (float("nan"), float("nan"))) for r in rows]
 
 
 def gemm_hash():
@@ -136,11 +210,14 @@ def mfma_utilisation(counter_csv, agent_csv):
 
 def main():
     p = argparse.ArgumentParser()
+    p.add_argument("--reads", help="counter file of the read-request pass")
+    p.add_argument("--writes", help="counter file of the write-request pass")
     p.add_argument("--fetch")
     p.add_argument("--write")
     p.add_argument("--workload")
     p.add_argument("--copy-bytes", type=int)
     p.add_argument("--out")
+    p.add_argument("--stats", help="rocprofv3 kernel-trace results database: print the kernel table instead")
     p.add_argument("--mfma", help="counter file of an MFMA utilisation pass: print the table instead")
     p.add_argument("--agents", help="the agent-info file of the same pass (with --mfma)")
     a = p.parse_args()
@@ -153,12 +230,29 @@ def main():
             print(f"| {k} | {e['dispatches']} | {e['ms']:.4f} | {e['clock_ghz']:.3f} | "
                   f"{100 * e['mfma_busy']:.1f}% | {e['tflops']:.1f} |")
         return
-    if not (a.fetch and a.write and a.workload and a.copy_bytes and a.out):
-        p.error("the traffic record needs --fetch, --write, --workload, --copy-bytes and --out")
+    if a.stats:
+        print("| kernel | calls | average (us) | min (us) | max (us) | total (ms) | share |")
+        print("|---|---|---|---|---|---|---|")
+        for name, calls, total, avg, pct, lo, hi in kernel_stats(a.stats):
+            short = re.sub(r"^void |\(.*$|rmx::\(anonymous namespace\)::", "", name)
+            print(f"| `{short}` | {calls} | {avg:.1f} | {lo:.1f} | {hi:.1f} | {total / 1e3:.3f} | {pct:.1f}% |")
+        return
+    if a.reads and a.writes and a.workload:
+        rec = build_request_record(a.reads, a.writes, a.workload)
+        if a.out:
+            with open(a.out, "w") as f:
+                json.dump(rec, f, indent=1)
+                f.write("\n")
+        print(json.dumps(rec, indent=1))
+        return
+    if not (a.fetch and a.write and a.workload and a.copy_bytes):
+        p.error("give --reads, --writes and --workload (request counts), or --fetch, --write, --workload "
+                "and --copy-bytes (scaled FETCH_SIZE / WRITE_SIZE)")
     rec = build_record(a.fetch, a.write, a.workload, a.copy_bytes)
-    with open(a.out, "w") as f:
-        json.dump(rec, f, indent=1)
-        f.write("\n")
+    if a.out:
+        with open(a.out, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
     print(json.dumps(rec, indent=1))
 
 

@@ -17,7 +17,7 @@ def _write(path, rows):
 def test_record_scales_by_copy_calibration(tmp_path):
     g1 = "void rmx::(anonymous namespace)::gemm_bf16_mfma<0>(rmx::GemmArgs)"
     g2 = "void rmx::(anonymous namespace)::gemm_bf16_mfma_n384<1>(rmx::GemmArgs)"
-    cp = "void rmx::(anonymous namespace)::token_mix_kernel<rmx::bf16_t, 8>(rmx::bf16_t const*, ...)"
+    cp = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)::{lambda(float)#1}>(...)"
     other = "void at::native::vectorized_elementwise_kernel<4>(...)"
     copy_bytes = 1 << 30
     # the fetch counter reads 5/6 of the copy, the write counter all of it
@@ -45,10 +45,11 @@ def test_committed_record_is_well_formed():
                         "traffic_counters.json")
     with open(path) as f:
         rec = json.load(f)
-    assert rec["calibration"]["copy_bytes_each_way"] > 0
+    assert "request" in rec["method"]
+    assert {"gemm1_gelu", "gemm2_residual"} <= set(rec["kernels"])
     for k, e in rec["kernels"].items():
-        assert e["bytes_per_launch"] == e["fetch_bytes"] + e["write_bytes"] or \
-            abs(e["bytes_per_launch"] - e["fetch_bytes"] - e["write_bytes"]) <= 1
+        assert abs(e["bytes_per_launch"] - e["read_bytes"] - e["write_bytes"]) <= 1
+        assert e["read_bytes"] > 0 and e["write_bytes"] > 0
 
 
 def test_mfma_utilisation_arithmetic(tmp_path):
@@ -81,3 +82,46 @@ def test_mfma_utilisation_arithmetic(tmp_path):
     assert abs(e["mfma_busy"] - (0.5 + 0.125) / 2) < 1e-12
     assert abs(e["ms"] - (500 + 1000) / 2 / 1e6) < 1e-15
     assert abs(e["tflops"] - (512000 / 500 + 512000 / 1000) / 2 / 1e3) < 1e-9
+
+
+def test_request_record_prices_each_request_by_its_size(tmp_path):
+    """Bytes per dispatch are 32, 64 and 128 per read request of that size and 64 per 64-byte
+    write, 32 per other write; no scale factor enters."""
+    g1 = "void rmx::(anonymous namespace)::gemm_bf16_mfma_n192<0>(rmx::GemmArgs)"
+    g2 = "void rmx::(anonymous namespace)::gemm_bf16_mfma_m64<1, true, 256>(rmx::GemmArgs)"
+    rows = "void rmx::(anonymous namespace)::rows_kernel<rmx::bf16_t, 8, 3, 1>(rmx::RowsArgs)"
+    rd = []
+    for k, (a, b, c) in ((g1, (10.0, 20.0, 1000.0)), (g1, (30.0, 40.0, 3000.0)), (g2, (0.0, 0.0, 500.0)),
+                         (rows, (0.0, 2.0, 64.0))):
+        rd += [(k, "TCC_EA0_RDREQ_32B_sum", a), (k, "TCC_EA0_RDREQ_64B_sum", b), (k, "TCC_EA0_RDREQ_128B_sum", c),
+               (k, "TCC_EA0_RDREQ_sum", a + b + c)]
+    wr = []
+    for k, (n, n64) in ((g1, (300.0, 200.0)), (g1, (300.0, 200.0)), (g2, (50.0, 50.0)), (rows, (8.0, 8.0))):
+        wr += [(k, "TCC_EA0_WRREQ_sum", n), (k, "TCC_EA0_WRREQ_64B_sum", n64)]
+    _write(tmp_path / "r.csv", rd)
+    _write(tmp_path / "w.csv", wr)
+    rec = counters.build_request_record(str(tmp_path / "r.csv"), str(tmp_path / "w.csv"), "w B=2")
+    k1 = rec["kernels"]["gemm1_gelu"]
+    assert k1["read_bytes"] == 32 * 20 + 64 * 30 + 128 * 2000      # means of the two dispatches
+    assert k1["write_bytes"] == 64 * 200 + 32 * 100
+    assert k1["bytes_per_launch"] == k1["read_bytes"] + k1["write_bytes"] and k1["dispatches"] == [2, 2]
+    assert rec["kernels"]["gemm2_residual"]["read_bytes"] == 128 * 500
+    assert rec["kernels"]["rows_ln2_mix_ln1"]["read_bytes"] == 64 * 2 + 128 * 64
+    assert rec["gemm_source_sha256_16"] == counters.gemm_hash()
+
+
+def test_kernel_stats_table_from_a_results_database(tmp_path):
+    import sqlite3
+    db = tmp_path / "run_results.db"
+    con = sqlite3.connect(db)
+    con.execute("create table top_kernels (name text, total_calls int, total_duration real, average real, "
+                "percentage real)")
+    con.executemany("insert into top_kernels values (?, ?, ?, ?, ?)",
+                    [("a", 2, 100.0, 50.0, 10.0), ("b", 4, 900.0, 225.0, 90.0)])
+    con.execute("create table kernels (name text, duration real)")
+    con.executemany("insert into kernels values (?, ?)", [("a", 40e3), ("a", 60e3), ("b", 200e3), ("b", 250e3)])
+    con.commit()
+    con.close()
+    rows = counters.kernel_stats(str(db))
+    assert [r[0] for r in rows] == ["b", "a"] and rows[0][3] == 225.0
+    assert rows[1][5:] == (40.0, 60.0) and rows[0][5:] == (200.0, 250.0)
