@@ -915,7 +915,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384(GemmArgs 
                           [&](int r) { return m0 + r < M ? m0 + r : -1; });
 }
 
-// ------------------------------------------------- 256 x 192 tiles, two workgroups per CU
+// ------------------------------------------ TM x 192 tiles (TM = 256 or 128), two per CU
 // A 256 x 384 tile holds 384 fp32 accumulators per lane and fills a SIMD's registers with one
 // wave, so its epilogue (bias, GELU, bf16 stores: about a quarter of the GELU product's time
 // at the 1B shape) leaves the matrix cores idle.  A 256 x 192 tile needs 192 accumulators
@@ -923,18 +923,33 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384(GemmArgs 
 // workgroups share a CU and one's epilogue runs beside the other's K loop.  It copies 40 %
 // more operand bytes per FLOP than the 256 x 384 tile; measured at the 1B shape, B = 2048:
 // GELU product 1.17 against 1.21 ms, residual product level (1.035 against 1.03 ms), so the
-// launch takes it for the GELU epilogue.  Waves 2 x 2 of 128 x 96 (4 x 3 blocks); per block
-// the same MFMAs in the same K order as the other tile shapes, so the bits are the same.
+// launch takes it for the GELU epilogue.  Waves 2 x 2 of (TM / 2) x 96 (TM / 64 x 3 blocks);
+// per block the same MFMAs in the same K order as the other tile shapes, so the bits are the
+// same.  TM = 128 (waves of 64 x 96, 3-stage ring of 20 KB stages; the A part of a stage is
+// the first or second 8 KB half of a packed 256-row block) serves launches with few tiles,
+// where a CU's copy rate, not the matrix cores, sets the time: it spreads a product over
+// twice as many workgroups as the 128 x 384 tile.
 // W^T rows of a tile: 192 nt .. 192 nt + 191, which may straddle two 256-row packed blocks;
 // each 16-row piece of a stage lies inside one block (the swizzle depends on row % 8).
 constexpr int BN3 = 192;
-constexpr int ST3_A = BM * BK * 2;                 // 16 KB of A per stage
-constexpr int ST3 = ST3_A + BN3 * BK * 2;          // + 12 KB of W^T
 constexpr int LD3 = 32 + 4;                        // epilogue staging rows: one 32-column block
 
-__device__ __forceinline__ void mfma_tile_pk3(f32x16_t (&acc)[4][3], __amdgpu_buffer_rsrc_t rA,
+template <int TM> struct Pk3 {
+  static constexpr int NI = TM / 64;               // row blocks per wave
+  static constexpr int APW = TM / 64;              // A pieces per wave and K step
+  static constexpr int NCP = APW + 3;              // copies per wave and K step
+  static constexpr int SA = TM * BK * 2;           // A part of a stage
+  static constexpr int SG = SA + BN3 * BK * 2;     // stage bytes
+  static constexpr int NS = TM == 256 ? 2 : 3;     // ring stages
+};
+
+template <int TM>
+__device__ __forceinline__ void mfma_tile_pk3(f32x16_t (&acc)[TM / 64][3], __amdgpu_buffer_rsrc_t rA,
                                               __amdgpu_buffer_rsrc_t rW, lds_u8* smem, uint32_t lds0, int K, int nt,
                                               int wave, int lane) {
+  using C = Pk3<TM>;
+  constexpr int NI = C::NI, APW = C::APW, NCP = C::NCP, SA = C::SA, SG = C::SG, NS = C::NS;
+  static_assert(NCP <= 2 * 3 * NI, "the refill copies fit between the MFMAs of a sub-step");
   const int nk = K / BK;
   uint32_t voffW[3];
 #pragma unroll
@@ -942,18 +957,18 @@ __device__ __forceinline__ void mfma_tile_pk3(f32x16_t (&acc)[4][3], __amdgpu_bu
     const int row = BN3 * nt + 16 * (wave + 4 * c);  // first W^T row of the piece
     voffW[c] = uint32_t(row >> 8) * uint32_t(nk) * 16384u + uint32_t(row & 255) * 64u + uint32_t(lane) * 16u;
   }
-  // copy c (0..6) of K step kt into stage `stage`: pieces wave + 4 c of A (c < 4) and
-  // wave + 4 (c - 4) of W^T; steps past the end reload the last (in bounds, never read)
+  // copy c (0..NCP-1) of K step kt into stage `stage`: pieces wave + 4 c of A (c < APW) and
+  // wave + 4 (c - APW) of W^T; steps past the end reload the last (in bounds, never read)
   auto copy = [&](int kt, int stage, int c) {
     kt = kt < nk ? kt : nk - 1;
-    const uint32_t sbase = lds0 + uint32_t(stage) * ST3;
-    if (c < 4) {
+    const uint32_t sbase = lds0 + uint32_t(stage) * SG;
+    if (c < APW) {
       const uint32_t piece = uint32_t(wave + 4 * c);
       copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), piece * 1024u + uint32_t(lane) * 16u, rA,
                   kt * 16384);
     } else {
-      const uint32_t q = uint32_t(wave + 4 * (c - 4));
-      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + ST3_A + q * 1024u), voffW[c - 4], rW, kt * 16384);
+      const uint32_t q = uint32_t(wave + 4 * (c - APW));
+      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + SA + q * 1024u), voffW[c - APW], rW, kt * 16384);
     }
   };
   const int wm = wave >> 1, wn = wave & 1;
@@ -961,71 +976,79 @@ __device__ __forceinline__ void mfma_tile_pk3(f32x16_t (&acc)[4][3], __amdgpu_bu
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const int c = kk * 2 + (lane >> 5);
-    const int m = wm * 128 + (lane & 31);
+    const int m = wm * (TM / 2) + (lane & 31);
     aoff[kk] = uint32_t(m * 64 + ((c ^ pk_swz(m)) << 4));
     const int n = wn * 96 + (lane & 31);
-    boff[kk] = uint32_t(ST3_A + n * 64 + ((c ^ pk_swz(n)) << 4));
+    boff[kk] = uint32_t(SA + n * 64 + ((c ^ pk_swz(n)) << 4));
   }
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
-  u32x4_t a0[4], a1[4], b[3];
-  auto read_a = [&](u32x4_t (&a)[4], const lds_u8* sp, int kk) {
+  u32x4_t a0[NI], a1[NI], b[3];
+  auto read_a = [&](u32x4_t (&a)[NI], const lds_u8* sp, int kk) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const lds_u32x4*>(sp + aoff[kk] + i * 2048);
+    for (int i = 0; i < NI; ++i) a[i] = *reinterpret_cast<const lds_u32x4*>(sp + aoff[kk] + i * 2048);
   };
   auto read_b = [&](const lds_u8* sp, int kk, int j) {
     b[j] = *reinterpret_cast<const lds_u32x4*>(sp + boff[kk] + j * 2048);
   };
-  auto mm = [&](const u32x4_t (&a)[4], int i, int j) {
+  auto mm = [&](const u32x4_t (&a)[NI], int i, int j) {
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[j]),
                                                         __builtin_bit_cast(bf16x8_t, a[i]), acc[i][j], 0, 0, 0);
   };
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 3; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  // prologue: steps 0 and 1; wait for step 0 (7 loads per step)
+  // prologue: steps 0 .. NS-1; wait for step 0 (NCP loads per step)
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
+  for (int st = 0; st < NS; ++st)
 #pragma unroll
-    for (int c = 0; c < 7; ++c) copy(st, st, c);
-  asm volatile("s_waitcnt vmcnt(7)\n\ts_barrier" ::: "memory");
+    for (int c = 0; c < NCP; ++c) copy(st, st, c);
+  if constexpr (TM == 256)
+    asm volatile("s_waitcnt vmcnt(7)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
   read_a(a0, smem, 0);
 #pragma unroll
   for (int j = 0; j < 3; ++j) read_b(smem, 0, j);
   int stage = 0;
   for (int it = 0; it < nk; ++it) {
-    const lds_u8* sp = smem + stage * ST3;
-    const int nstage = stage ^ 1;
+    const lds_u8* sp = smem + stage * SG;
+    const int nstage = stage + 1 == NS ? 0 : stage + 1;
     // sub-step 0 on a0 / b; sub-step 1's fragments read behind the MFMAs that free them
     read_a(a1, sp, 1);
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mm(a0, i, j);
+      for (int i = 0; i < NI; ++i) mm(a0, i, j);
       __builtin_amdgcn_sched_barrier(0);
       read_b(sp, 1, j);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // every read of this stage has returned; after the barrier step it+1 is visible and this
-    // stage takes step it+2
+    // every read of this stage has returned; after the barrier step it+1 is visible (with 3
+    // stages the NCP loads of step it+2 may be outstanding) and this stage takes step it+NS
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (TM == 256)
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    // sub-step 1 on a1 / b; the refill of this stage spread over its 12 MFMAs
-    const lds_u8* np = smem + nstage * ST3;
+    // sub-step 1 on a1 / b; the refill of this stage spread over its MFMAs
+    const lds_u8* np = smem + nstage * SG;
     read_a(a0, np, 0);
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NI; ++i) {
         mm(a1, i, j);
-        const int q = 4 * j + i;
-        if (q == 0 || q == 2 || q == 4 || q == 6 || q == 8 || q == 9 || q == 10) {
+        // TM = 256: copies after MFMAs 0, 2, 4, 6, 8, 9, 10 of 12; TM = 128: after 0 .. 4 of 6
+        const int q = NI * j + i;
+        const int c = TM == 256 ? (q <= 6 ? ((q & 1) ? -1 : q / 2) : (q <= 10 ? q - 4 : -1)) : (q < 5 ? q : -1);
+        if (c >= 0) {
           __builtin_amdgcn_sched_barrier(0);
-          copy(it + 2, stage, q <= 6 ? q / 2 : q - 4);
+          copy(it + NS, stage, c);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -1039,14 +1062,15 @@ __device__ __forceinline__ void mfma_tile_pk3(f32x16_t (&acc)[4][3], __amdgpu_bu
   __syncthreads();
 }
 
-// Epilogue of a 256 x 192 tile (the arithmetic of tile_epilogue6): per 32 x 32 block, the
+// Epilogue of a TM x 192 tile (the arithmetic of tile_epilogue6): per 32 x 32 block, the
 // accumulators are staged through LDS so that each lane owns 8 consecutive columns of one row
 // (4 lanes per row, 16 rows per pass).  Rows past M are not stored.
-template <int EPI>
-__device__ __forceinline__ void tile_epilogue3(const f32x16_t (&acc)[4][3], float* smem_f, const GemmArgs& p, int g,
-                                               const bf16_t* bias_g, int n0, int m0, int wave, int lane) {
+template <int EPI, int TM>
+__device__ __forceinline__ void tile_epilogue3(const f32x16_t (&acc)[TM / 64][3], float* smem_f, const GemmArgs& p,
+                                               int g, const bf16_t* bias_g, int n0, int m0, int wave, int lane) {
+  constexpr int NI = TM / 64;
   const int M = p.M, N = p.N;
-  const int wrow0 = (wave >> 1) * 128, wcol0 = (wave & 1) * 96;
+  const int wrow0 = (wave >> 1) * (TM / 2), wcol0 = (wave & 1) * 96;
   float* st = smem_f + wave * 32 * LD3;
   const int col8 = (lane & 3) * 8;
 #pragma unroll
@@ -1057,7 +1081,7 @@ __device__ __forceinline__ void tile_epilogue3(const f32x16_t (&acc)[4][3], floa
     for (int e = 0; e < 8; ++e) bias[e] = 0.f;
     if (bias_g) load8(bias_g + n, bias);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NI; ++i) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
         *reinterpret_cast<float4*>(st + (lane & 31) * LD3 + 8 * g4 + 4 * (lane >> 5)) =
@@ -1093,17 +1117,19 @@ __device__ __forceinline__ void tile_epilogue3(const f32x16_t (&acc)[4][3], floa
   }
 }
 
-// Dense per-token product on packed operands with 256 x 192 tiles, two workgroups per CU:
-// G * ceil(M/256) * N/192 workgroups, N % 192 == 0; EPI_GELU or EPI_RESID.
-template <int EPI>
+// Dense per-token product on packed operands with TM x 192 tiles, two workgroups per CU:
+// G * ceil(M/TM) * N/192 workgroups, N % 192 == 0; EPI_GELU or EPI_RESID.
+template <int EPI, int TM>
 __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_n192(GemmArgs p) {
-  static_assert(EPI == EPI_GELU || EPI == EPI_RESID, "256 x 192 tiles serve the inference epilogues");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[2 * ST3];
+  static_assert(EPI == EPI_GELU || EPI == EPI_RESID, "TM x 192 tiles serve the inference epilogues");
+  static_assert(TM == 256 || TM == 128, "256- or 128-row tiles");
+  using C = Pk3<TM>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[C::NS * C::SG];
   lds_u8* const smem = (lds_u8*)smem_g;
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int M = p.M, N = p.N, K = p.K;
-  const int nMt = (M + BM - 1) / BM, nNt = N / BN3;
+  const int nMt = (M + TM - 1) / TM, nNt = N / BN3;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int g = id / (nMt * nNt);
   const int rem = id - g * nMt * nNt;
@@ -1112,18 +1138,22 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_n192(GemmArgs 
   const int in_band = rem - band * TILE_BAND * nNt;
   const int bm = min(TILE_BAND, nMt - band * TILE_BAND);
   const int nt = in_band / bm, mt = band * TILE_BAND + (in_band - (in_band / bm) * bm);
-  // the tile's A blocks (packed row block mt, K/32 x 16 KB) and the token's whole W^T
-  // (pk_rows(N) rows; slices < 2^31 bytes, checked at launch)
+  // the tile's A blocks (packed row block, K/32 x 16 KB; a 128-row tile starts at the first or
+  // second 8 KB half of each) and the token's whole W^T (pk_rows(N) rows; slices < 2^31
+  // bytes, checked at launch)
   const uint32_t blk = uint32_t(K / BK) * 16384u;
   const uint32_t wbytes = uint32_t(pk_rows(N) / 256) * blk;
+  const int nMb = (M + BM - 1) / BM;                    // packed 256-row blocks per token
+  const int mb = mt / (BM / TM), half = mt % (BM / TM);  // block and half of this tile
   const __amdgpu_buffer_rsrc_t rA =
-      make_rsrc(static_cast<const uint16_t*>(p.A) + (size_t(g) * nMt + mt) * (size_t(blk) / 2), blk);
+      make_rsrc(static_cast<const uint16_t*>(p.A) + (size_t(g) * nMb + mb) * (size_t(blk) / 2) + size_t(half) * 4096,
+                blk - uint32_t(half) * 8192u);
   const __amdgpu_buffer_rsrc_t rW =
       make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * (size_t(wbytes) / 2), wbytes);
-  f32x16_t acc[4][3];
-  mfma_tile_pk3(acc, rA, rW, smem, lds0, K, nt, wave, lane);
+  f32x16_t acc[TM / 64][3];
+  mfma_tile_pk3<TM>(acc, rA, rW, smem, lds0, K, nt, wave, lane);
   const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
-  tile_epilogue3<EPI>(acc, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN3, mt * BM, wave, lane);
+  tile_epilogue3<EPI, TM>(acc, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN3, mt * TM, wave, lane);
 }
 
 // Sparse-MoE grouped GEMM on prepared expert weights with 256 x 384 tiles: the persistent
@@ -1777,42 +1807,58 @@ hipError_t launch_gemm_moe(int epi, const GemmArgs& args, hipStream_t stream) {
 
 namespace {
 
-// Tile shape of a packed-operand product with the GELU or residual epilogue.  384-wide tiles
-// need N % 384 == 0 and a token's packed W^T below 2^31 bytes (their buffer descriptor spans
-// it).  Among the shapes allowed, the launch takes the fewest device rounds (ceil(tiles /
-// CUs)) weighted by the tile's duration, measured at the 1B shapes: a 256 x 384 tile runs
-// about 1.4x as long as a 256 x 256 one (B = 256, GEMM2 on 128 wide tiles for 256 CUs: 231
-// against 197 us), and a 128 x 384 tile, which copies as many bytes per K step as a
-// 256 x 256 one, about 0.85x (fitted to B = 384 GEMM1, 6 rounds of them against 4 of
-// 256 x 384: 301 against 334 us, and B = 640 and 768 GEMM2, 3 rounds against 2: 454 against
-// 486 us and 480 against 506 us; at B = 256 GEMM2 one round of them takes 188 us against
-// 198 for one round of 256 x 256 tiles).
-// The environment variable RMX_WIDE_TILES = always / half / pair / never forces 256 x 384,
-// 128 x 384, 256 x 192 (two workgroups per CU) or 256 x 256 (tests and tuning; read at each
-// launch); all give the same bits.  Unforced, the GELU product takes 256 x 192 tiles where
-// the choice above gives 256 x 384 and N % 192 == 0 (measured at the 1B shape: the same
-// number of rounds of twice as many tiles, 1.17 against 1.21 ms at B = 2048).
-enum TileShape { TILES_256 = 0, TILES_256x384 = 1, TILES_128x384 = 2, TILES_256x192 = 3 };
+// Tile shape of a packed-operand product with the GELU or residual epilogue.  Each shape's
+// cost is its number of rounds times the measured duration of one round of its tiles on the
+// whole chip, relative to the others (1B shapes, K = 1536 and 6144; durations in units of
+// about 2.8 us at K = 1536):
+//   256 x 256: 20 per round of CUs tiles          256 x 384: 28 per round of CUs tiles
+//   128 x 384: 17 per round of CUs tiles          (N % 384 == 0 for both)
+//   256 x 192, two per CU: 27 per round of 2 CUs tiles (the GELU product only: for the
+//       residual product at B = 2048 it is level with 256 x 384, 1.04 against 1.03 ms)
+//   128 x 192, two per CU: 17 per round of 2 CUs tiles, 12 when the launch holds at most
+//       one tile per CU (RankMixer-100M GEMM2, B = 512: 256 tiles, 56 us against 77 us for
+//       its 128 x 384 tiles, which leave half of the CUs idle)
+// The fewest units win; ties go to the shape listed first.  384-wide tiles need
+// N % 384 == 0, 192-wide ones N % 192 == 0, all of them a token's packed W^T below 2^31
+// bytes (their buffer descriptor spans it).
+// The environment variable RMX_WIDE_TILES = always / half / pair / pairhalf / never forces
+// 256 x 384, 128 x 384, 256 x 192, 128 x 192 or 256 x 256 (tests and tuning; read at each
+// launch; a shape N does not divide falls back to 256 x 256); all give the same bits.
+enum TileShape { TILES_256 = 0, TILES_256x384 = 1, TILES_128x384 = 2, TILES_256x192 = 3, TILES_128x192 = 4 };
 
 TileShape pick_tiles(const GemmArgs& a, int epi) {
   const char* force = getenv("RMX_WIDE_TILES");
-  if (force && strcmp(force, "never") == 0) return TILES_256;
   const bool w_ok = uint64_t(pk_rows(a.N)) * uint64_t(a.K) * 2u < (uint64_t(1) << 31);
-  if (force && strcmp(force, "pair") == 0) return (w_ok && a.N % BN3 == 0) ? TILES_256x192 : TILES_256;
-  if (a.N % BN6 != 0 || !w_ok) return TILES_256;
-  if (force && strcmp(force, "always") == 0) return TILES_256x384;
-  if (force && strcmp(force, "half") == 0) return TILES_128x384;
+  const bool n384 = w_ok && a.N % BN6 == 0, n192 = w_ok && a.N % BN3 == 0;
+  if (force) {
+    if (strcmp(force, "never") == 0) return TILES_256;
+    if (strcmp(force, "always") == 0) return n384 ? TILES_256x384 : TILES_256;
+    if (strcmp(force, "half") == 0) return n384 ? TILES_128x384 : TILES_256;
+    if (strcmp(force, "pair") == 0) return n192 ? TILES_256x192 : TILES_256;
+    if (strcmp(force, "pairhalf") == 0) return n192 ? TILES_128x192 : TILES_256;
+  }
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  auto rounds = [&](int64_t tiles) { return (tiles + cus - 1) / cus; };
-  const int64_t mt = (a.M + BM - 1) / BM, mh = (a.M + 127) / 128;
-  const int64_t t6 = int64_t(a.G) * mt * (a.N / BN6), t4 = int64_t(a.G) * mt * ((a.N + BN - 1) / BN);
-  const int64_t th = int64_t(a.G) * mh * (a.N / BN6);
-  // relative tile durations 20 : 28 : 17 (256 x 256 : 256 x 384 : 128 x 384), times rounds
-  const int64_t c4 = 20 * rounds(t4), c6 = 28 * rounds(t6), ch = 17 * rounds(th);
-  if (ch < c6 && ch < c4) return TILES_128x384;
-  if (c6 >= c4) return TILES_256;
-  return epi == EPI_GELU ? TILES_256x192 : TILES_256x384;
+  const int64_t G = a.G, m256 = (a.M + BM - 1) / BM, m128 = (a.M + 127) / 128;
+  auto rounds = [&](int64_t tiles, int64_t slots) { return (tiles + slots - 1) / slots; };
+  TileShape best = TILES_256;
+  int64_t best_cost = 20 * rounds(G * m256 * ((a.N + BN - 1) / BN), cus);
+  auto consider = [&](TileShape s, int64_t cost) {
+    if (cost < best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  };
+  if (n384) {
+    consider(TILES_256x384, 28 * rounds(G * m256 * (a.N / BN6), cus));
+    consider(TILES_128x384, 17 * rounds(G * m128 * (a.N / BN6), cus));
+  }
+  if (n192) {
+    if (epi == EPI_GELU) consider(TILES_256x192, 27 * rounds(G * m256 * (a.N / BN3), 2 * int64_t(cus)));
+    const int64_t t = G * m128 * (a.N / BN3);
+    consider(TILES_128x192, t <= cus ? 12 : 17 * rounds(t, 2 * int64_t(cus)));
+  }
+  return best;
 }
 
 // 64-row tiles 128 columns wide (packed products) where the 256-wide ones number between
@@ -1856,9 +1902,17 @@ hipError_t launch_dense_mfma(int epi, const GemmArgs& a, hipStream_t stream) {
   if (shape == TILES_256x192) {
     const int tiles3 = a.G * ((a.M + BM - 1) / BM) * (a.N / BN3);
     if (epi == EPI_GELU)
-      hipLaunchKernelGGL((gemm_bf16_mfma_n192<EPI_GELU>), dim3(tiles3), dim3(MFMA_THREADS), 0, stream, a);
+      hipLaunchKernelGGL((gemm_bf16_mfma_n192<EPI_GELU, 256>), dim3(tiles3), dim3(MFMA_THREADS), 0, stream, a);
     else
-      hipLaunchKernelGGL((gemm_bf16_mfma_n192<EPI_RESID>), dim3(tiles3), dim3(MFMA_THREADS), 0, stream, a);
+      hipLaunchKernelGGL((gemm_bf16_mfma_n192<EPI_RESID, 256>), dim3(tiles3), dim3(MFMA_THREADS), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (shape == TILES_128x192) {
+    const int tiles3 = a.G * ((a.M + 127) / 128) * (a.N / BN3);
+    if (epi == EPI_GELU)
+      hipLaunchKernelGGL((gemm_bf16_mfma_n192<EPI_GELU, 128>), dim3(tiles3), dim3(MFMA_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_mfma_n192<EPI_RESID, 128>), dim3(tiles3), dim3(MFMA_THREADS), 0, stream, a);
     return hipGetLastError();
   }
   if (shape == TILES_256x384) {
