@@ -403,6 +403,11 @@ def bench_backward(cfg, B, steps, warmup, cpu_samples):
     print(f"[bench] inputs {cfg.name} B={B} generated and resident in {time.time() - t0:.1f}s",
           file=sys.stderr, flush=True)
     h = rmx.Handle.for_config(cfg, max_batch=B)
+    if h.packed_weights_bytes() > 0:
+        # weights prepared once (model-load work): the training forward's products read them,
+        # the backward reads W1 and W2
+        w["packed"] = h.pack_weights(w)
+        torch.cuda.synchronize()
     out, saved = h.forward_train(X, w)
     dX, grads = h.backward(X, w, saved, g)
     for _ in range(warmup):

@@ -252,7 +252,10 @@ rmx_status rmx_tokenize(const void* E, const void* Wp, const void* bp, void* X, 
 
 /* Training: the forward pass that keeps the activations the backward pass needs, and the
  * backward pass ("RankMixer 详解（1）：特征分组与完整计算流程", section 5.2).  Dense handles
- * (moe_experts == 0) only; the weights are read from W1 and W2 (w->packed must be NULL).
+ * (moe_experts == 0) only.  Both calls need W1 and W2.  rmx_block_forward_train may also be
+ * given w->packed (rmx_pack_weights for this handle): its products then read W1 and W2 from
+ * the prepared copy where their shapes allow (N a multiple of 384), with the same results
+ * bit for bit; rmx_block_backward reads W1 and W2 and ignores w->packed.
  *
  * rmx_saved_bytes: bytes of the saved activations for B samples (0 for a Sparse-MoE handle,
  * a NULL handle or B < 0).  Per block: S [T, B, D] (dtype); GELU'(U) at the

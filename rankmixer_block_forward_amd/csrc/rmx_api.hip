@@ -507,7 +507,8 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
   if (gate_out && !moe) return fail(h, RMX_ERR_INVALID_ARG, "gate_out must be NULL for a dense handle");
   if (lists && !moe) return fail(h, RMX_ERR_INVALID_ARG, "routing lists exist for Sparse-MoE handles only");
   if (train && moe) return fail(h, RMX_ERR_UNSUPPORTED, "training needs a dense handle");
-  if (train && w->packed) return fail(h, RMX_ERR_INVALID_ARG, "training reads W1 and W2: packed must be NULL");
+  if (train && w->packed && !(w->W1 && w->W2))
+    return fail(h, RMX_ERR_INVALID_ARG, "training needs W1 and W2 (the backward reads them) beside packed");
   if (train && saved_bytes < rmx_saved_bytes(h, B))
     return fail(h, RMX_ERR_INVALID_ARG, "saved buffer of %zu bytes, %zu needed", saved_bytes,
                 rmx_saved_bytes(h, B));
@@ -554,6 +555,10 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
     if (!h->pk_capable)
       return fail(h, RMX_ERR_UNSUPPORTED, "prepared weights need a dense bf16 handle with D and k*D multiples of 32");
     if ((st = check_dev(h, w->packed, rmx_packed_weights_bytes(h), dev, "packed")) != RMX_OK) return st;
+    if (train) {
+      if ((st = check_dev(h, w->W1, Ls * T * D * kD * esz, dev, "W1")) != RMX_OK) return st;
+      if ((st = check_dev(h, w->W2, Ls * T * kD * D * esz, dev, "W2")) != RMX_OK) return st;
+    }
   } else if (w->packed_mxfp8) {
     if (!h->mx_capable)
       return fail(h, RMX_ERR_UNSUPPORTED, "MXFP8 weights need a dense bf16 handle with D and k*D multiples of 64");
@@ -610,7 +615,11 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
   };
   hipError_t e = hipSuccess;
   const int Bi = int(B);
-  const bool pk = !moe && w->packed != nullptr;
+  const bool pk = !moe && !train && w->packed != nullptr;
+  // training on prepared weights: the products read W from the prepared copy and S, H
+  // row-major (the saved activations), where their shapes allow 384-wide tiles; the same bits
+  const bool pk_train1 = train && !moe && w->packed != nullptr && gemm_packed_w_supported(B, int64_t(kD), int64_t(D));
+  const bool pk_train2 = train && !moe && w->packed != nullptr && gemm_packed_w_supported(B, int64_t(D), int64_t(kD));
   const bool moe_pk = moe && w->packed != nullptr;
   // prepared expert weights of block n: the T*E groups' We1^T, then their We2^T (elements)
   const size_t pk_we1 = T * E * size_t(pk_rows(int64_t(hid))) * D, pk_we2 = T * E * size_t(pk_rows(int64_t(D))) * hid;
@@ -792,8 +801,8 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
 
     GemmArgs g1{};
     g1.A = S_of(n);
-    g1.W = pk ? at(w->packed, size_t(n) * (pk_w1 + pk_w2)) : at(w->W1, size_t(n) * T * D * kD);
-    g1.packed = pk ? 1 : 0;
+    g1.W = (pk || pk_train1) ? at(w->packed, size_t(n) * (pk_w1 + pk_w2)) : at(w->W1, size_t(n) * T * D * kD);
+    g1.packed = pk ? 1 : (pk_train1 ? GEMM_PACKED_W : 0);
     g1.bias = at(w->b1, size_t(n) * T * kD);
     g1.C = H_of(n);
     g1.U = train ? blk(n, lay.U) : nullptr;
@@ -806,8 +815,8 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
 
     GemmArgs g2{};
     g2.A = H_of(n);
-    g2.W = pk ? at(w->packed, size_t(n) * (pk_w1 + pk_w2) + pk_w1) : at(w->W2, size_t(n) * T * kD * D);
-    g2.packed = pk ? 1 : 0;
+    g2.W = (pk || pk_train2) ? at(w->packed, size_t(n) * (pk_w1 + pk_w2) + pk_w1) : at(w->W2, size_t(n) * T * kD * D);
+    g2.packed = pk ? 1 : (pk_train2 ? GEMM_PACKED_W : 0);
     g2.bias = at(w->b2, size_t(n) * T * D);
     g2.R = S_of(n);
     g2.C = Y_of(n);
@@ -917,7 +926,7 @@ rmx_status rmx_block_backward(rmx_handle* h, const void* X, int64_t B, const rmx
     return fail(h, RMX_ERR_INVALID_ARG, "B=%lld outside [0, max_batch=%lld]", (long long)B,
                 (long long)c.max_batch);
   if (c.moe_experts > 0) return fail(h, RMX_ERR_UNSUPPORTED, "the backward needs a dense handle");
-  if (w->packed) return fail(h, RMX_ERR_INVALID_ARG, "the backward reads W1 and W2: packed must be NULL");
+  // the backward reads W1 and W2 (w->packed, if set, is the forward's prepared copy: unused)
   if (!rows_bwd_supported(c.dtype, c.T, c.D))
     return fail(h, RMX_ERR_UNSUPPORTED, "the backward row kernel takes D <= %d (D %% 8 == 0, (D/T) %% 8 == 0) or "
                 "D <= %d, and T*D*sizeof(dtype) within its LDS", ROWS_BWD_MAX_D, ROWS_BWD_MAX_D_SCALAR);

@@ -682,11 +682,8 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
     const uint32_t sbase = lds0 + uint32_t(stage) * STG;
     if (c < APW) {
       const uint32_t piece = uint32_t(wave + 4 * c);
-      if constexpr (GATHER_A)
-        copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), offA[c], rA, kt * BK * 2);
-      else
-        copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), piece * 1024u + uint32_t(lane) * 16u, rA,
-                    kt * 16384);
+      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), piece * 1024u + uint32_t(lane) * 16u, rA,
+                  kt * 16384);
     } else {
       const uint32_t q = uint32_t(wave + 4 * (c - APW));
       copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + ABYTES + q * 1024u), voffW[c - APW], rW, kt * 16384);
@@ -803,7 +800,9 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
 // group of two column blocks, 32 rows x 64 columns are staged through LDS so that each lane
 // then owns 8 consecutive columns of one row (8 lanes per row, 8 rows per pass).
 // row_of(r) maps tile row r to its output row, or -1 where the tile runs past the rows.
-template <int EPI, int TM = 256, typename RowOf>
+// RM: the dense operands are row-major (the training forward): EPI_GELU_SAVE writes H and
+// GELU' to C and U, EPI_RESID reads R, all [G][M][N] with the strides of p.
+template <int EPI, int TM = 256, bool RM = false, typename RowOf>
 __device__ __forceinline__ void tile_epilogue6(const f32x16_t (&accA)[4][4], const f32x16_t (&accV)[4][2],
                                                float* smem_f, const GemmArgs& p, int g, const bf16_t* bias_g,
                                                int n0, int wave, int lane, RowOf row_of, int nib = TM / 64) {
@@ -846,18 +845,26 @@ __device__ __forceinline__ void tile_epilogue6(const f32x16_t (&accA)[4][4], con
         v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
         v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
         if (m >= 0 && n < N) {
+          const size_t rmo = size_t(g) * size_t(p.sc) + size_t(m) * size_t(p.ldc) + n;  // row-major
           if constexpr (EPI == EPI_GELU) {
             const size_t pko = size_t(g) * size_t(pk_rows(M)) * N + pk_off(m, n, N);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[s][e]);
             store8(static_cast<bf16_t*>(p.C) + pko, v);
+          } else if constexpr (EPI == EPI_GELU_SAVE) {
+            static_assert(RM, "the training epilogue writes row-major H and GELU'");
+            float gd[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = gelu_erf_and_grad(v[e] + bias[s][e], &gd[e]);
+            store8(static_cast<bf16_t*>(p.U) + rmo, gd);
+            store8(static_cast<bf16_t*>(p.C) + rmo, v);
           } else if constexpr (EPI == EPI_RESID) {
-            const size_t pko = size_t(g) * size_t(pk_rows(M)) * N + pk_off(m, n, N);
+            const size_t pko = RM ? rmo : size_t(g) * size_t(pk_rows(M)) * N + pk_off(m, n, N);
             float rr[8];
             load8(static_cast<const bf16_t*>(p.R) + pko, rr);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = v[e] + bias[s][e] + rr[e];
-            store8(static_cast<float*>(p.C) + size_t(g) * size_t(p.sc) + size_t(m) * size_t(p.ldc) + n, v);
+            store8(static_cast<float*>(p.C) + rmo, v);
           } else if constexpr (EPI == EPI_MOE1) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[s][e]);
@@ -1154,6 +1161,53 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_n192(GemmArgs 
   mfma_tile_pk3<TM>(acc, rA, rW, smem, lds0, K, nt, wave, lane);
   const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
   tile_epilogue3<EPI, TM>(acc, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN3, mt * TM, wave, lane);
+}
+
+// Dense per-token product with row-major A (the training forward's saved S and H) and
+// prepared W^T, 256 x 384 tiles: A rows are gathered straight into the packed LDS layout (the
+// K loop of the Sparse-MoE kernel), the epilogue writes row-major outputs.  Per block the
+// same MFMAs in the same K order as the row-major kernels, so the outputs are the same bits.
+// G * ceil(M/256) * N/384 workgroups, N % 384 == 0, M * K * 2 < 2^31; EPI_GELU_SAVE or
+// EPI_RESID.
+template <int EPI>
+__global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384g(GemmArgs p) {
+  static_assert(EPI == EPI_GELU_SAVE || EPI == EPI_RESID, "the training forward's epilogues");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[PK6_NS * STAGE6_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_g;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nMt = (M + BM - 1) / BM, nNt = N / BN6;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = id / (nMt * nNt);
+  const int rem = id - g * nMt * nNt;
+  // bands of TILE_BAND row tiles, M-fastest inside a band (as in the 256 x 256 kernel)
+  const int band = rem / (TILE_BAND * nNt);
+  const int in_band = rem - band * TILE_BAND * nNt;
+  const int bm = min(TILE_BAND, nMt - band * TILE_BAND);
+  const int nt = in_band / bm, mt = band * TILE_BAND + (in_band - (in_band / bm) * bm);
+  const int m0 = mt * BM;
+  const uint32_t blk = uint32_t(K / BK) * 16384u;
+  const uint32_t wbytes = uint32_t(pk_rows(N) / 256) * blk;
+  const __amdgpu_buffer_rsrc_t rW =
+      make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * (size_t(wbytes) / 2), wbytes);
+  // A: the token's rows [M x K]; rows past M read as zeros (offset past the descriptor's end)
+  const uint32_t row_bytes = uint32_t(K) * 2u, bytesA = uint32_t(M) * row_bytes;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(g) * size_t(p.sa), bytesA);
+  uint32_t offA[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    // piece wave + 4 c is tile rows 16 (wave + 4 c) .. + 15; lane l fills slot l % 4 of row
+    // l / 4, which holds 16-byte chunk (l % 4) ^ pk_swz(row) of that row's 64-byte K step
+    const int r = 16 * (wave + 4 * c) + (lane >> 2);
+    const uint32_t chunk16 = uint32_t((lane & 3) ^ pk_swz(r)) * 16u;
+    offA[c] = m0 + r < M ? uint32_t(m0 + r) * row_bytes + chunk16 : bytesA;
+  }
+  f32x16_t accA[4][4], accV[4][2];
+  mfma_tile_pk6<true, 4>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA);
+  const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
+  tile_epilogue6<EPI, 256, true>(accA, accV, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN6, wave, lane,
+                                 [&](int r) { return m0 + r < M ? m0 + r : -1; });
 }
 
 // Sparse-MoE grouped GEMM on prepared expert weights with 256 x 384 tiles: the persistent
@@ -1775,6 +1829,12 @@ bool gemm_uses_mfma(int dtype, int M, int N, int K, int64_t lda, int at, int bt)
 
 hipError_t gemm_init() { return hipSuccess; }
 
+bool gemm_packed_w_supported(int64_t M, int64_t N, int64_t K) {
+  const uint64_t lim = uint64_t(1) << 31;
+  return M > 0 && N > 0 && K > 0 && N % BN6 == 0 && K % BK == 0 && uint64_t(M) * uint64_t(K) * 2u < lim &&
+         uint64_t(pk_rows(N)) * uint64_t(K) * 2u < lim;
+}
+
 bool gemm_moe_supported(int N, int K, int64_t a_rows, bool packed) {
   const uint64_t lim = uint64_t(1) << 31;
   if (packed && (N % BN6 != 0 || uint64_t(pk_rows(N)) * K * 2 >= lim)) return false;
@@ -2104,6 +2164,18 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& args, hipStream_t str
   GemmArgs a = normalized(args);
   const bool bwd_epi = epi == EPI_GELU_BWD || epi == EPI_RESID32 || epi == EPI_STORE32;
   if ((a.at || a.bt) && !bwd_epi) return hipErrorInvalidValue;
+  if (a.packed == GEMM_PACKED_W) {
+    // prepared W^T with row-major A and outputs: the training forward's products
+    if (dtype != DT_BF16 || (epi != EPI_GELU_SAVE && epi != EPI_RESID) || !gemm_packed_w_supported(a.M, a.N, a.K) ||
+        a.lda != a.K || a.ldc != a.N || a.sa != int64_t(a.M) * a.K || a.sc != int64_t(a.M) * a.N)
+      return hipErrorInvalidValue;
+    const int tiles = a.G * ((a.M + BM - 1) / BM) * (a.N / BN6);
+    if (epi == EPI_GELU_SAVE)
+      hipLaunchKernelGGL((gemm_bf16_mfma_n384g<EPI_GELU_SAVE>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_mfma_n384g<EPI_RESID>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+    return hipGetLastError();
+  }
   if (a.packed) {
     // packed operands exist only for the MFMA kernels, and only for the inference epilogues
     if (!gemm_uses_mfma(dtype, a.M, a.N, a.K) || (epi != EPI_GELU && epi != EPI_RESID)) return hipErrorInvalidValue;

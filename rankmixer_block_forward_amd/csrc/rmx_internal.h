@@ -183,6 +183,8 @@ enum Epilogue {
   EPI_GELU_BWD = 5, EPI_RESID32 = 6, EPI_STORE32 = 7, EPI_GELU_SAVE = 8, EPI_GELU_MX = 9
 };
 
+constexpr int GEMM_PACKED_W = 2;  // GemmArgs::packed: prepared W^T, row-major A
+
 struct GemmArgs {
   const void* A;
   const void* W;
@@ -200,7 +202,8 @@ struct GemmArgs {
   int64_t lda, ldc, sa, sc;
   // Dense kernels only: A [G][pk_rows(M) x K] and W^T [G][pk_rows(N) x K] in the packed
   // operand layout; EPI_GELU then writes C packed ([G][pk_rows(M) x N]) and EPI_RESID reads
-  // R packed, C stays row-major.  Strides are ignored.
+  // R packed, C stays row-major.  Strides are ignored.  GEMM_PACKED_W: only W^T is packed, A,
+  // C, R and U are contiguous row-major (EPI_GELU_SAVE, EPI_RESID; gemm_packed_w_supported).
   int packed;
   // Dense kernels only, operands stored transposed (the backward products):
   //   at: A is [G][K][M], element (m, k) at A + g * sa + k * lda + m (lda = 0: M, sa = 0: K * M)
@@ -226,6 +229,9 @@ bool gemm_uses_mfma(int dtype, int M, int N, int K, int64_t lda = 0, int at = 0,
 hipError_t launch_gemm_moe(int epi, const GemmArgs& a, hipStream_t stream);
 // packed: W is the groups' W^T in the packed operand layout (256 x 384 tiles, N % 384 == 0).
 bool gemm_moe_supported(int N, int K, int64_t a_rows, bool packed);
+// The products of prepared W^T with row-major A (GEMM_PACKED_W): N % 384 == 0, K % 32 == 0,
+// A's M x K and the packed W^T below 2^31 bytes.
+bool gemm_packed_w_supported(int64_t M, int64_t N, int64_t K);
 hipError_t gemm_init();
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t stream);
 // True when launch_gemm(dtype, epi, a) runs a matrix-core kernel that writes a.colsum.

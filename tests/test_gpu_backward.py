@@ -113,6 +113,36 @@ def test_forward_train_output_is_the_forward_output(cfg):
         assert torch.equal(out, ref)
 
 
+@pytest.mark.parametrize("B,T,D,k,L", [
+    (300, 4, 384, 4, 2),   # both products on 256 x 384 tiles from the prepared copy, ragged rows
+    (129, 8, 384, 2, 1),   # one row past a tile
+    (300, 4, 256, 3, 2),   # only GEMM1 (N = kD = 768) reads the prepared copy; GEMM2 (N = 256) W2
+    (1, 2, 768, 4, 1),     # one sample
+])
+def test_forward_train_on_prepared_weights_same_bits(B, T, D, k, L):
+    """The training forward given the prepared copy (its products read W^T packed and the saved
+    S and H row-major, gathered into the packed LDS layout) writes the same out and the same
+    saved activations, bit for bit, as on W1 and W2; the backward from either is the same."""
+    rmx = _rmx()
+    cfg = synth.Config("train-pk", B=B, T=T, D=D, k=k, L=L, dtype="bf16", bias_std=0.02)
+    inp = synth.make_inputs(cfg, seed=B + D)
+    X, w = rmx.upload(inp)
+    g = torch.from_numpy(synth.make_grad_out(B, D, seed=B)).cuda()
+    with rmx.Handle.for_config(cfg) as h:
+        o1, s1 = h.forward_train(X, w)
+        wp = dict(w, packed=h.pack_weights(w))
+        o2, s2 = h.forward_train(X, wp)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(s1, s2)
+        dX1, g1 = h.backward(X, w, s1, g)
+        dX2, g2 = h.backward(X, wp, s2, g)
+        torch.cuda.synchronize()
+        assert torch.equal(dX1, dX2) and all(torch.equal(g1[n], g2[n]) for n in g1)
+        o3 = h.forward(X, wp)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o3)   # the inference forward on the prepared copy: the same bits
+
+
 def test_backward_twice_is_deterministic_and_reuses_the_workspace():
     cfg = CASES[3]
     rmx = _rmx()
@@ -168,8 +198,15 @@ def test_backward_1b_full_size_sampled():
     X, w = rmx.upload(inp)
     toks = [0, 7, 20, 31]
     with rmx.Handle.for_config(cfg) as h:
-        out, saved = h.forward_train(X, w)
-        dX, grads = h.backward(X, w, saved, torch.from_numpy(g_out).cuda())
+        # the training forward on the prepared copy (the benchmark's launch), which must give
+        # the bits of the forward on W1 and W2
+        wp = dict(w, packed=h.pack_weights(w))
+        out, saved = h.forward_train(X, wp)
+        out_rm, saved_rm = h.forward_train(X, w)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_rm) and torch.equal(saved, saved_rm)
+        del saved_rm
+        dX, grads = h.backward(X, wp, saved, torch.from_numpy(g_out).cuda())
         torch.cuda.synchronize()
         got = {n: to_np(t).astype(np.float64) for n, t in grads.items() if n not in ("W1", "W2")}
         got["W1"] = to_np(grads["W1"][:, toks]).astype(np.float64)
@@ -232,8 +269,8 @@ def test_backward_argument_errors():
         with pytest.raises(RmxError) as ei:       # saved buffer too small
             h.backward(X, w, saved[: saved.numel() // 2], g)
         assert ei.value.status == RMX_ERR_INVALID_ARG
-        with pytest.raises(RmxError) as ei:       # prepared weights are not read by training
-            h.forward_train(X, dict(w, packed=h.pack_weights(w)))
+        with pytest.raises(RmxError) as ei:       # training needs W1 and W2 beside prepared weights
+            h.forward_train(X, dict(w, packed=h.pack_weights(w), W1=None))
         assert ei.value.status == RMX_ERR_INVALID_ARG
         dX = torch.empty((cfg.B, cfg.T, cfg.D), dtype=torch.float32, device="cuda")
         grads = {n: torch.empty(1, device="cuda") for n in NAMES}
