@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rmx_layout.h"
+
 namespace rmx {
 
 struct bf16_t {
@@ -63,37 +65,9 @@ __device__ __forceinline__ float load1(const bf16_t* p) { return bf16_to_f32(p->
 __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store1(bf16_t* p, float v) { p->bits = f32_to_bf16(v); }
 
-// ---- Packed operand layout of a bf16 matrix [rows, K], K % 32 == 0: blocks of 256 rows x
-// 32 columns (16 KB), ordered [row block][K step]; inside a block row r holds its four
-// 16-byte chunks, chunk c at position c ^ pk_swz(r).  A K step of a 256-row block is then
-// one contiguous 16 KB that lands in LDS as is, already swizzled for conflict-free 16-byte
-// fragment reads.  Rows are padded to a multiple of 256 (pk_rows, rmx_internal.h).
-__device__ __forceinline__ int pk_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-// element offset of (row, col) with col % 8 == 0: the start of a 16-byte chunk
-__device__ __forceinline__ size_t pk_off(int row, int col, int K) {
-  const int rb = row >> 8, r = row & 255, kt = col >> 5, c = (col >> 3) & 3;
-  return ((size_t(rb) * size_t(K >> 5) + size_t(kt)) << 13) + size_t(r << 5) + size_t((c ^ pk_swz(r)) << 3);
-}
+// The packed bf16 and MXFP8 operand layouts (pk_off, mx_off, mx_scale_off, ...) are in
+// rmx_layout.h.
 
-// ---- MXFP8 operands (OCP Microscaling Formats (MX) Specification v1.0, FP8 E4M3 elements,
-// one E8M0 power-of-two scale per 32 consecutive values along K).  A matrix [rows, K]
-// (K % 64 == 0, rows padded to a multiple of 256) is stored as blocks of 256 rows x 64 K
-// (16 KB), ordered [row block][K step]; inside a block row r holds four 16-byte chunks of
-// 16 consecutive k, chunk c at position c ^ pk_swz(r).  Its scales are 512 bytes per block,
-// laid out so that lane l of the wave that owns rows 128 h .. 128 h + 127 of the block finds
-// the scales of rows 128 h + 32 i + (l % 32), i = 0..3, for the 32-value half l / 32 of the
-// K step in one 32-bit word, byte i: the scale operand of the MFMA.
-// byte offset of (row, k), k % 16 == 0 (the start of a chunk; + 8 for its second half)
-__device__ __forceinline__ size_t mx_off(int row, int k, int K) {
-  const int rb = row >> 8, r = row & 255, kt = k >> 6, c = (k >> 4) & 3;
-  return ((size_t(rb) * size_t(K >> 6) + size_t(kt)) << 14) + size_t(r << 6) + size_t((c ^ pk_swz(r)) << 4);
-}
-// byte offset of the scale of (row, 32-value block kb)
-__device__ __forceinline__ size_t mx_scale_off(int row, int kb, int K) {
-  const int rb = row >> 8, r = row & 255;
-  return ((size_t(rb) * size_t(K >> 6) + size_t(kb >> 1)) << 9) + size_t((r >> 7) << 8) +
-         size_t((((kb & 1) << 5) | (r & 31)) << 2) + size_t((r >> 5) & 3);
-}
 // Biased E8M0 scale of a block whose largest magnitude is amax: 2^(floor(log2 amax) - 8),
 // 8 the top exponent of E4M3, clamped below at 2^-127 (an all-zero block takes 2^-127).
 // From the fp32 exponent field e: floor(log2 amax) - 8 + 127 = e - 8.

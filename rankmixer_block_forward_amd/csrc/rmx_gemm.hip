@@ -51,8 +51,6 @@ constexpr int BM = 256, BN = 256, BK = 32, NS = 4;
 constexpr int A_STAGE_BYTES = BM * BK * 2;                 // 16 KB, rows of 64 B
 constexpr int STAGE_BYTES = A_STAGE_BYTES + BK * BN * 2;   // + 16 KB, rows of 512 B
 constexpr int MFMA_THREADS = 256;
-constexpr int NUM_XCD = 8;         // MI355X: 8 accelerator complex dies, each with its own L2
-constexpr int TILE_BAND = 8;       // row tiles per band of the dense tile order
 
 
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
@@ -62,16 +60,6 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-
-// Workgroups are dealt to the XCDs round-robin.  Remap so that each XCD receives a
-// contiguous range of tile indices, and order tiles M-fastest within bands of row tiles of
-// a token so that the tiles resident on one XCD at a time share their weight panels and A
-// rows in its L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  const int xcd = bid % NUM_XCD, pos = bid / NUM_XCD;
-  const int base = nblocks / NUM_XCD, extra = nblocks % NUM_XCD;
-  return xcd * base + (xcd < extra ? xcd : extra) + pos;
-}
 
 // Chunk swizzles.  A rows hold 4 chunks (64 B): 16 consecutive rows read one chunk each.
 // W rows hold 32 chunks (512 B): a transposing read takes 4 consecutive k rows x 32 B.
@@ -490,9 +478,9 @@ __device__ __forceinline__ void mfma_tile_pk(f32x16_t (&acc)[4][4], __amdgpu_buf
     for (int i = 0; i < 4; ++i) {
       const int c = kk * 2 + (lane >> 5);
       const int m = wm * 128 + i * 32 + (lane & 31);
-      aoff[kk][i] = uint32_t(m * 64 + ((c ^ pk_swz(m)) << 4));
+      aoff[kk][i] = pk_lds_off(m, c);
       const int n = wn * 128 + i * 32 + (lane & 31);
-      boff[kk][i] = uint32_t(A_STAGE_BYTES + n * 64 + ((c ^ pk_swz(n)) << 4));
+      boff[kk][i] = uint32_t(A_STAGE_BYTES) + pk_lds_off(n, c);
     }
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
   struct PkFrags {
@@ -576,10 +564,8 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma(GemmArgs p) {
   // Within a token, tiles run over bands of TILE_BAND row tiles: M-fastest inside a band,
   // then N, then the next band, so the tiles resident on one XCD at a time form a compact
   // block whatever the batch size.
-  const int band = rem / (TILE_BAND * nNt);
-  const int in_band = rem - band * TILE_BAND * nNt;
-  const int bm = min(TILE_BAND, nMt - band * TILE_BAND);
-  const int nt = in_band / bm, mt = band * TILE_BAND + (in_band - (in_band / bm) * bm);
+  int mt, nt;
+  band_tile(rem, nMt, nNt, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
 
   f32x16_t acc[4][4];
@@ -695,9 +681,9 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
   for (int kk = 0; kk < 2; ++kk) {
     const int c = kk * 2 + (lane >> 5);
     const int m = wm * (TM / 2) + (lane & 31);
-    aoff[kk] = uint32_t(m * 64 + ((c ^ pk_swz(m)) << 4));
+    aoff[kk] = pk_lds_off(m, c);
     const int n = wn * 192 + (lane & 31);
-    boff[kk] = uint32_t(ABYTES + n * 64 + ((c ^ pk_swz(n)) << 4));
+    boff[kk] = uint32_t(ABYTES) + pk_lds_off(n, c);
   }
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
   // a0 / a1: A fragments of sub-steps 0 / 1; b[j]: the W^T fragment of column block j,
@@ -897,10 +883,8 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384(GemmArgs 
   const int g = id / (nMt * nNt);
   const int rem = id - g * nMt * nNt;
   // bands of TILE_BAND row tiles, M-fastest inside a band (as in the 256 x 256 kernel)
-  const int band = rem / (TILE_BAND * nNt);
-  const int in_band = rem - band * TILE_BAND * nNt;
-  const int bm = min(TILE_BAND, nMt - band * TILE_BAND);
-  const int nt = in_band / bm, mt = band * TILE_BAND + (in_band - (in_band / bm) * bm);
+  int mt, nt;
+  band_tile(rem, nMt, nNt, mt, nt);
   // the tile's A blocks (packed row block, K/32 x 16 KB; a 128-row tile starts at the first or
   // second 8 KB half of each) and the token's whole W^T (pk_rows(N) rows; slices < 2^31
   // bytes, checked at launch)
@@ -984,9 +968,9 @@ __device__ __forceinline__ void mfma_tile_pk3(f32x16_t (&acc)[TM / 64][3], __amd
   for (int kk = 0; kk < 2; ++kk) {
     const int c = kk * 2 + (lane >> 5);
     const int m = wm * (TM / 2) + (lane & 31);
-    aoff[kk] = uint32_t(m * 64 + ((c ^ pk_swz(m)) << 4));
+    aoff[kk] = pk_lds_off(m, c);
     const int n = wn * 96 + (lane & 31);
-    boff[kk] = uint32_t(SA + n * 64 + ((c ^ pk_swz(n)) << 4));
+    boff[kk] = uint32_t(SA) + pk_lds_off(n, c);
   }
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
   u32x4_t a0[NI], a1[NI], b[3];
@@ -1141,10 +1125,8 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_n192(GemmArgs 
   const int g = id / (nMt * nNt);
   const int rem = id - g * nMt * nNt;
   // bands of TILE_BAND row tiles, M-fastest inside a band (as in the 256 x 256 kernel)
-  const int band = rem / (TILE_BAND * nNt);
-  const int in_band = rem - band * TILE_BAND * nNt;
-  const int bm = min(TILE_BAND, nMt - band * TILE_BAND);
-  const int nt = in_band / bm, mt = band * TILE_BAND + (in_band - (in_band / bm) * bm);
+  int mt, nt;
+  band_tile(rem, nMt, nNt, mt, nt);
   // the tile's A blocks (packed row block, K/32 x 16 KB; a 128-row tile starts at the first or
   // second 8 KB half of each) and the token's whole W^T (pk_rows(N) rows; slices < 2^31
   // bytes, checked at launch)
@@ -1182,10 +1164,8 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384g(GemmArgs
   const int g = id / (nMt * nNt);
   const int rem = id - g * nMt * nNt;
   // bands of TILE_BAND row tiles, M-fastest inside a band (as in the 256 x 256 kernel)
-  const int band = rem / (TILE_BAND * nNt);
-  const int in_band = rem - band * TILE_BAND * nNt;
-  const int bm = min(TILE_BAND, nMt - band * TILE_BAND);
-  const int nt = in_band / bm, mt = band * TILE_BAND + (in_band - (in_band / bm) * bm);
+  int mt, nt;
+  band_tile(rem, nMt, nNt, mt, nt);
   const int m0 = mt * BM;
   const uint32_t blk = uint32_t(K / BK) * 16384u;
   const uint32_t wbytes = uint32_t(pk_rows(N) / 256) * blk;
@@ -1197,10 +1177,9 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384g(GemmArgs
   uint32_t offA[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    // piece wave + 4 c is tile rows 16 (wave + 4 c) .. + 15; lane l fills slot l % 4 of row
-    // l / 4, which holds 16-byte chunk (l % 4) ^ pk_swz(row) of that row's 64-byte K step
-    const int r = 16 * (wave + 4 * c) + (lane >> 2);
-    const uint32_t chunk16 = uint32_t((lane & 3) ^ pk_swz(r)) * 16u;
+    // piece wave + 4 c of the K step: tile row r, chunk pk_gather_chunk of its 64 bytes
+    const int r = pk_gather_row(wave + 4 * c, lane);
+    const uint32_t chunk16 = uint32_t(pk_gather_chunk(r, lane)) * 16u;
     offA[c] = m0 + r < M ? uint32_t(m0 + r) * row_bytes + chunk16 : bytesA;
   }
   f32x16_t accA[4][4], accV[4][2];
@@ -1228,22 +1207,14 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_moe_n384(GemmArgs p
   const int total = p.tile_start[G] * nNt;
   const int per_xcd = int(gridDim.x) / NUM_XCD;  // gridDim.x is a multiple of NUM_XCD
   const int xcd = int(blockIdx.x) % NUM_XCD, slot = int(blockIdx.x) / NUM_XCD;
-  const int chunk = (total + NUM_XCD - 1) / NUM_XCD;
-  const int lo = xcd * chunk, hi = min(total, lo + chunk);
+  int lo, hi;
+  moe_xcd_span(total, xcd, NUM_XCD, lo, hi);
   const uint32_t blk = uint32_t(K / BK) * 16384u;
   const uint32_t wbytes = uint32_t(pk_rows(N) / 256) * blk;
 
   for (int tile = lo + slot; tile < hi; tile += per_xcd) {
-    // group of this tile: the last g with tile_start[g] * nNt <= tile
-    int glo = 0, ghi = G;  // invariant: tile_start[glo]*nNt <= tile < tile_start[ghi]*nNt
-    while (ghi - glo > 1) {
-      const int mid = (glo + ghi) >> 1;
-      if (p.tile_start[mid] * nNt <= tile) glo = mid; else ghi = mid;
-    }
-    const int g = glo;
-    const int mtiles = p.tile_start[g + 1] - p.tile_start[g];
-    const int local = tile - p.tile_start[g] * nNt;
-    const int nt = local / mtiles, mt = local - nt * mtiles;
+    int g, mt, nt;
+    moe_tile_locate(p.tile_start, G, nNt, tile, g, mt, nt);
     const int row0 = p.group_start[g], rows = p.group_start[g + 1] - row0;
     const int m0 = mt * BM;
     const __amdgpu_buffer_rsrc_t rW =
@@ -1258,10 +1229,9 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_moe_n384(GemmArgs p
     uint32_t offA[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      // piece wave + 4 c is tile rows 16 (wave + 4 c) .. + 15; lane l fills slot l % 4 of row
-      // l / 4, which holds 16-byte chunk (l % 4) ^ pk_swz(row) of that row's 64-byte K step
-      const int r = 16 * (wave + 4 * c) + (lane >> 2);
-      const uint32_t chunk16 = uint32_t((lane & 3) ^ pk_swz(r)) * 16u;
+      // piece wave + 4 c of the K step: tile row r, chunk pk_gather_chunk of its 64 bytes
+      const int r = pk_gather_row(wave + 4 * c, lane);
+      const uint32_t chunk16 = uint32_t(pk_gather_chunk(r, lane)) * 16u;
       if (m0 + r < rows) {
         const uint32_t src = EPI == EPI_MOE1 ? uint32_t(p.src_row[row0 + m0 + r]) : uint32_t(m0 + r);
         offA[c] = src * row_bytes + chunk16;
@@ -1369,9 +1339,9 @@ __device__ __forceinline__ void mfma_tile_mx(f32x16_t (&acc)[4][4], __amdgpu_buf
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int m = wm * 128 + i * 32 + (lane & 31);
-      aoff[i][c] = uint32_t(m * 64 + (((hk + 2 * c) ^ pk_swz(m)) << 4));
+      aoff[i][c] = pk_lds_off(m, hk + 2 * c);
       const int n = wn * 128 + i * 32 + (lane & 31);
-      boff[i][c] = uint32_t(MX_CODE_BYTES + n * 64 + (((hk + 2 * c) ^ pk_swz(n)) << 4));
+      boff[i][c] = uint32_t(MX_CODE_BYTES) + pk_lds_off(n, hk + 2 * c);
     }
   const uint32_t sa_off = uint32_t(2 * MX_CODE_BYTES + wm * 256 + lane * 4);
   const uint32_t sw_off = uint32_t(2 * MX_CODE_BYTES + 512 + wn * 256 + lane * 4);
@@ -1470,10 +1440,8 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_mx_mfma(GemmArgs p) {
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int g = id / (nMt * nNt);
   const int rem = id - g * nMt * nNt;
-  const int band = rem / (TILE_BAND * nNt);
-  const int in_band = rem - band * TILE_BAND * nNt;
-  const int bm = min(TILE_BAND, nMt - band * TILE_BAND);
-  const int nt = in_band / bm, mt = band * TILE_BAND + (in_band - (in_band / bm) * bm);
+  int mt, nt;
+  band_tile(rem, nMt, nNt, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
   const uint32_t nk = uint32_t(K / MX_BK);
   const uint8_t* A = static_cast<const uint8_t*>(p.A) + (size_t(g) * nMt + mt) * (size_t(nk) * MX_CODE_BYTES);
@@ -1505,21 +1473,13 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_moe(GemmArgs p) {
   const int total = p.tile_start[G] * nNt;
   const int per_xcd = int(gridDim.x) / NUM_XCD;  // gridDim.x is a multiple of NUM_XCD
   const int xcd = int(blockIdx.x) % NUM_XCD, slot = int(blockIdx.x) / NUM_XCD;
-  const int chunk = (total + NUM_XCD - 1) / NUM_XCD;
-  const int lo = xcd * chunk, hi = min(total, lo + chunk);
+  int lo, hi;
+  moe_xcd_span(total, xcd, NUM_XCD, lo, hi);
   const uint32_t bytesW = uint32_t(K) * uint32_t(N) * 2u;
 
   for (int tile = lo + slot; tile < hi; tile += per_xcd) {
-    // group of this tile: the last g with tile_start[g] * nNt <= tile
-    int glo = 0, ghi = G;  // invariant: tile_start[glo]*nNt <= tile < tile_start[ghi]*nNt
-    while (ghi - glo > 1) {
-      const int mid = (glo + ghi) >> 1;
-      if (p.tile_start[mid] * nNt <= tile) glo = mid; else ghi = mid;
-    }
-    const int g = glo;
-    const int mtiles = p.tile_start[g + 1] - p.tile_start[g];
-    const int local = tile - p.tile_start[g] * nNt;
-    const int nt = local / mtiles, mt = local - nt * mtiles;
+    int g, mt, nt;
+    moe_tile_locate(p.tile_start, G, nNt, tile, g, mt, nt);
     const int row0 = p.group_start[g], rows = p.group_start[g + 1] - row0;
     const int m0 = mt * BM, n0 = nt * BN;
 
@@ -1650,7 +1610,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_m64(GemmArgs p
       aoff[kk][i] = uint32_t(m * 64 + ((c ^ swz_a(m)) << 4));
       if constexpr (PK) {
         const int n = wave * (SBN / 4) + i * 32 + (lane & 31);
-        boff[kk][i] = uint32_t(SM_A_BYTES + n * 64 + ((c ^ pk_swz(n)) << 4));
+        boff[kk][i] = uint32_t(SM_A_BYTES) + pk_lds_off(n, c);
       } else {
         const int kb = 8 * (lane >> 5) + ((lane & 15) >> 2);
         const int n = wave * 64 + i * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);

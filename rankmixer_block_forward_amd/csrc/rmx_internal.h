@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rmx_layout.h"
+
 namespace rmx {
 
 enum Dtype { DT_FP32 = 0, DT_BF16 = 1 };
@@ -19,8 +21,6 @@ inline int dtype_size(int dt) { return dt == DT_BF16 ? 2 : 4; }
 // S is written token-major [T, B, D] (dtype), the layout the grouped GEMMs read.
 enum RowsMode { ROWS_FIRST = 0, ROWS_MID = 1, ROWS_FINAL = 2 };
 
-// Rows of one group of a matrix in the packed operand layout (blocks of 256 rows).
-__host__ __device__ inline int64_t pk_rows(int64_t rows) { return (rows + 255) / 256 * 256; }
 
 struct RowsArgs {
   const void* in;
