@@ -668,8 +668,11 @@ __device__ __forceinline__ void mfma_tile_pk6(f32x16_t (&accA)[4][4], f32x16_t (
     const uint32_t sbase = lds0 + uint32_t(stage) * STG;
     if (c < APW) {
       const uint32_t piece = uint32_t(wave + 4 * c);
-      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), piece * 1024u + uint32_t(lane) * 16u, rA,
-                  kt * 16384);
+      if constexpr (GATHER_A)
+        copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), offA[c], rA, kt * BK * 2);
+      else
+        copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), piece * 1024u + uint32_t(lane) * 16u, rA,
+                    kt * 16384);
     } else {
       const uint32_t q = uint32_t(wave + 4 * (c - APW));
       copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + ABYTES + q * 1024u), voffW[c - APW], rW, kt * 16384);
