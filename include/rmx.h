@@ -313,7 +313,8 @@ typedef enum {
   RMX_KERNEL_MOE_GATE = 4, /* router + token -> expert lists */
   RMX_KERNEL_MOE_FFN1 = 5, /* expert first layer (gathered rows) + GELU */
   RMX_KERNEL_MOE_FFN2 = 6, /* expert second layer, gate-weighted */
-  RMX_KERNEL_MOE_COMBINE = 7, /* sum of expert outputs + S -> pre-LN2 rows */
+  RMX_KERNEL_MOE_COMBINE = 7, /* not launched: the sum of the expert rows + S is formed in the
+                                 next row pass (RMX_KERNEL_ROWS / RMX_KERNEL_POOL) */
   RMX_KERNEL_BWD_ROWS = 8, /* backward: LayerNorm backward, mixing transpose, residuals */
   RMX_KERNEL_BWD_DU = 9,   /* backward: per-token gY W2^T * GELU'(U) -> gU */
   RMX_KERNEL_BWD_DS = 10,  /* backward: per-token gU W1^T + gY -> gradient of S */

@@ -68,8 +68,8 @@ struct rmx_handle {
   int* moe_src_row = nullptr;    // [R]
   float* moe_row_gate = nullptr; // [R]
   int* moe_pos = nullptr;        // [G, max_batch]
-  void* moe_hidden = nullptr;    // [R, h]  bf16
-  float* moe_out = nullptr;      // [R, D]  fp32
+  void* moe_hidden = nullptr;    // [R, h] bf16, or packed on tile-aligned group blocks
+  void* moe_out = nullptr;       // [R, D]  bf16 gate-scaled expert rows
   // Self-attention routing (routing == RMX_ROUTING_ATTENTION): Q, K, V and the block input
   // of blocks 2..L, each [max_batch, T, D] dtype, and a scratch for the unused pool of the
   // launch that forms that input
@@ -344,14 +344,6 @@ hipError_t run_moe_gemm(rmx_handle* h, hipStream_t s, int epi, const GemmArgs& a
   return e;
 }
 
-hipError_t run_moe_combine(rmx_handle* h, hipStream_t s, const MoeArgs& a) {
-  ProfPair pp;
-  prof_begin(h, s, &pp, RMX_KERNEL_MOE_COMBINE);
-  hipError_t e = launch_moe_combine(a, s);
-  prof_end(h, s, &pp);
-  return e;
-}
-
 }  // namespace
 
 static void set_capabilities(rmx_handle* h);
@@ -444,8 +436,10 @@ rmx_status rmx_create(const rmx_config* cfg, rmx_handle** out_handle) {
       alloc(&h->moe_src_row, R * sizeof(int));
       alloc(&h->moe_row_gate, R * sizeof(float));
       alloc(&h->moe_pos, G * mb * sizeof(int));
-      alloc(&h->moe_hidden, R * size_t(cfg->moe_hidden) * 2);
-      alloc(&h->moe_out, R * size_t(cfg->D) * sizeof(float));
+      // hidden rows: row-major [R, h], or packed with every group on whole 256-row blocks
+      // (prepared expert weights), at most G * pk_rows(max_batch) rows
+      alloc(&h->moe_hidden, size_t(G) * size_t(pk_rows(int64_t(mb))) * size_t(cfg->moe_hidden) * 2);
+      alloc(&h->moe_out, R * size_t(cfg->D) * 2);
     }
   }
   if (!ok) {
@@ -605,6 +599,15 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
   auto S_of = [&](int n) -> void* { return train ? blk(n, lay.S) : h->S; };
   auto H_of = [&](int n) -> void* { return train ? blk(n, lay.H) : h->H; };
   auto Y_of = [&](int n) -> float* { return train ? reinterpret_cast<float*>(blk(n, lay.Y)) : h->Y; };
+  // After a Sparse-MoE block the next row pass forms the pre-LN2 rows itself from that
+  // block's S and gate-scaled expert rows (no Y in memory).
+  auto moe_combine_rows = [&](RowsArgs& ra) {
+    if (!moe) return;
+    ra.in = h->S;
+    ra.moe_ye = h->moe_out;
+    ra.moe_pos = h->moe_pos;
+    ra.moe_E = c.moe_experts;
+  };
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const char* bytes = nullptr;
@@ -681,6 +684,7 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
     } else {
       RowsArgs ra{};
       ra.in = n == 0 ? X : static_cast<const void*>(Y_of(n - 1));
+      if (n > 0) moe_combine_rows(ra);
       ra.ln2_g = n == 0 ? nullptr : at(w->ln2_g, size_t(n - 1) * D);
       ra.ln2_b = n == 0 ? nullptr : at(w->ln2_b, size_t(n - 1) * D);
       ra.ln1_g = at(w->ln1_g, size_t(n) * D);
@@ -714,8 +718,6 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
       ma.src_row = h->moe_src_row;
       ma.row_gate = h->moe_row_gate;
       ma.pos = h->moe_pos;
-      ma.Ye = h->moe_out;
-      ma.Y = h->Y;
       ma.B = Bi;
       ma.T = c.T;
       ma.D = c.D;
@@ -763,8 +765,8 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
       m2.group_start = h->moe_group_start;
       m2.tile_start = h->moe_tile_start;
       m2.row_gate = h->moe_row_gate;
-      if ((e = run_moe_gemm(h, s, EPI_MOE2, m2)) != hipSuccess) break;
-      e = run_moe_combine(h, s, ma);
+      // the combine S + sum of the gate-scaled expert rows runs inside the next row pass
+      e = run_moe_gemm(h, s, EPI_MOE2, m2);
       continue;
     }
 
@@ -829,6 +831,7 @@ static rmx_status forward_impl(rmx_handle* h, const void* X, int64_t B, const rm
   if (e == hipSuccess) {
     RowsArgs ra{};
     ra.in = Y_of(c.L - 1);
+    moe_combine_rows(ra);
     ra.ln2_g = at(w->ln2_g, size_t(c.L - 1) * D);
     ra.ln2_b = at(w->ln2_b, size_t(c.L - 1) * D);
     ra.pool = out;

@@ -433,7 +433,7 @@ __device__ __forceinline__ void tile_epilogue(const f32x16_t (&acc)[NI][NJ], flo
           const float gv = p.row_gate[orow];
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = gv * (v[e] + bias[e]);
-          store8(static_cast<float*>(p.C) + off, v);
+          store8(static_cast<bf16_t*>(p.C) + off, v);
         }
       }
     }
@@ -855,14 +855,15 @@ __device__ __forceinline__ void tile_epilogue6(const f32x16_t (&accA)[4][4], con
             for (int e = 0; e < 8; ++e) v[e] = v[e] + bias[s][e] + rr[e];
             store8(static_cast<float*>(p.C) + rmo, v);
           } else if constexpr (EPI == EPI_MOE1) {
+            // hidden rows in the packed layout, m a row of the group's tile-aligned blocks
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[s][e]);
-            store8(static_cast<bf16_t*>(p.C) + size_t(m) * size_t(N) + n, v);
+            store8(static_cast<bf16_t*>(p.C) + pk_off(m, n, N), v);
           } else {
             const float gv = p.row_gate[m];
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = gv * (v[e] + bias[s][e]);
-            store8(static_cast<float*>(p.C) + size_t(m) * size_t(N) + n, v);
+            store8(static_cast<bf16_t*>(p.C) + size_t(m) * size_t(N) + n, v);
           }
         }
       }
@@ -1194,10 +1195,12 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384g(GemmArgs
 
 // Sparse-MoE grouped GEMM on prepared expert weights with 256 x 384 tiles: the persistent
 // tile walk of gemm_bf16_moe (same device-built tile table, each XCD a contiguous range of
-// tiles, row tiles fastest inside a group), the K loop of gemm_bf16_mfma_n384 with A gathered
-// from row-major rows, and tile_epilogue6.  W is group g's W^T in the packed layout
-// (pk_rows(N) x K, N % 384 == 0).  Same products in the same order as gemm_bf16_moe, so
-// the two give the same bits.
+// tiles, row tiles fastest inside a group), the K loop of gemm_bf16_mfma_n384 and
+// tile_epilogue6.  W is group g's W^T in the packed layout (pk_rows(N) x K, N % 384 == 0).
+// Layer 1 gathers its A rows from S and writes the hidden rows in the packed layout, group g
+// on the blocks tile_start[g] .. tile_start[g + 1] - 1 (its row tile mt on block
+// tile_start[g] + mt); layer 2 reads those blocks as they are.  Same products in the same
+// order as gemm_bf16_moe, so the two give the same bits.
 template <int EPI>
 __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_moe_n384(GemmArgs p) {
   static_assert(EPI == EPI_MOE1 || EPI == EPI_MOE2, "the Sparse-MoE epilogues");
@@ -1220,42 +1223,47 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_moe_n384(GemmArgs p
     moe_tile_locate(p.tile_start, G, nNt, tile, g, mt, nt);
     const int row0 = p.group_start[g], rows = p.group_start[g + 1] - row0;
     const int m0 = mt * BM;
+    // the tile's block of the packed hidden rows: groups start on whole 256-row blocks
+    const int hblk = p.tile_start[g] + mt;
     const __amdgpu_buffer_rsrc_t rW =
         make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * (size_t(wbytes) / 2), wbytes);
-    // A rows: S through the row list (layer 1) or the group's compacted hidden rows (layer 2);
-    // rows past the group read as zeros (offset past the descriptor's end)
-    const uint32_t row_bytes = uint32_t(K) * 2u;
-    const uint32_t bytesA = uint32_t(EPI == EPI_MOE1 ? p.a_rows : rows) * row_bytes;
-    const __amdgpu_buffer_rsrc_t rA =
-        EPI == EPI_MOE1 ? make_rsrc(p.A, bytesA)
-                        : make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(row0) * K, bytesA);
+    // A: layer 1 gathers rows of S through the row list (rows past the group read as zeros:
+    // offset past the descriptor's end); layer 2 reads the tile's packed block of hidden
+    // rows, whose rows past the group are never stored
     uint32_t offA[4];
+    __amdgpu_buffer_rsrc_t rA;
+    if constexpr (EPI == EPI_MOE1) {
+      const uint32_t row_bytes = uint32_t(K) * 2u;
+      const uint32_t bytesA = uint32_t(p.a_rows) * row_bytes;
+      rA = make_rsrc(p.A, bytesA);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      // piece wave + 4 c of the K step: tile row r, chunk pk_gather_chunk of its 64 bytes
-      const int r = pk_gather_row(wave + 4 * c, lane);
-      const uint32_t chunk16 = uint32_t(pk_gather_chunk(r, lane)) * 16u;
-      if (m0 + r < rows) {
-        const uint32_t src = EPI == EPI_MOE1 ? uint32_t(p.src_row[row0 + m0 + r]) : uint32_t(m0 + r);
-        offA[c] = src * row_bytes + chunk16;
-      } else {
-        offA[c] = bytesA;
+      for (int c = 0; c < 4; ++c) {
+        // piece wave + 4 c of the K step: tile row r, chunk pk_gather_chunk of its 64 bytes
+        const int r = pk_gather_row(wave + 4 * c, lane);
+        const uint32_t chunk16 = uint32_t(pk_gather_chunk(r, lane)) * 16u;
+        offA[c] = m0 + r < rows ? uint32_t(p.src_row[row0 + m0 + r]) * row_bytes + chunk16 : bytesA;
       }
+    } else {
+      rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(hblk) * (size_t(blk) / 2), blk);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) offA[c] = 0u;
     }
+    constexpr bool GA = EPI == EPI_MOE1;
     // row blocks of this wave (32 rows each) that hold rows of the group: 4 except in a
     // group's last row tile, where the MFMA work past the rows is skipped
     const int nib = __builtin_amdgcn_readfirstlane(max(0, min(4, (rows - m0 - (wave >> 1) * 128 + 31) / 32)));
     f32x16_t accA[4][4], accV[4][2];
     switch (nib) {
-      case 4: mfma_tile_pk6<true, 4>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
-      case 3: mfma_tile_pk6<true, 3>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
-      case 2: mfma_tile_pk6<true, 2>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
-      case 1: mfma_tile_pk6<true, 1>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
-      default: mfma_tile_pk6<true, 0>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+      case 4: mfma_tile_pk6<GA, 4>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+      case 3: mfma_tile_pk6<GA, 3>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+      case 2: mfma_tile_pk6<GA, 2>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+      case 1: mfma_tile_pk6<GA, 1>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+      default: mfma_tile_pk6<GA, 0>(accA, accV, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
     }
     const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
+    // output rows: layer 1 the packed hidden block, layer 2 the compacted expert rows
     tile_epilogue6<EPI>(accA, accV, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN6, wave, lane,
-                        [&](int r) { return m0 + r < rows ? row0 + m0 + r : -1; }, nib);
+                        [&](int r) { return m0 + r < rows ? (GA ? hblk * BM + r : row0 + m0 + r) : -1; }, nib);
     // every wave is done with its staging rows before the next tile's copies reuse the ring
     __syncthreads();
   }

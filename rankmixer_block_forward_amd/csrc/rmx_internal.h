@@ -38,6 +38,13 @@ struct RowsArgs {
   // scales at s8_scale + t * pk_rows(B) * D / 32 bytes), nullable
   void* s8;
   void* s8_scale;
+  // ROWS_MID / ROWS_FINAL after a Sparse-MoE block (moe_ye non-null): the pre-LN2 rows are
+  // formed on the fly, Y[t, b] = S[t, b] + sum over e in order of Ye[pos[t][e][b]] (fp32,
+  // experts with pos < 0 skipped), with in = that block's S [T, B, D] (bf16), moe_ye its
+  // gate-scaled expert rows [rows, D] (bf16) and moe_pos [T * E][B].
+  const void* moe_ye;
+  const int* moe_pos;
+  int moe_E;
 };
 
 // Largest D the row kernel's per-lane registers hold.
@@ -141,8 +148,6 @@ struct MoeArgs {
   int* src_row;       // [T * E * B] compacted row -> S row (t * B + b)
   float* row_gate;    // [T * E * B] compacted row -> gate value
   int* pos;           // [T, E, B] -> compacted row, or -1 if the expert is inactive
-  const float* Ye;    // [rows, D] fp32 gate-scaled expert outputs (combine input)
-  float* Y;           // [T, B, D] fp32 pre-LN2 rows (combine output)
   int B, T, D, E, nchunk;
 };
 
@@ -151,7 +156,6 @@ hipError_t moe_init();
 // LDS bytes of the router kernel for D columns and E experts.
 size_t moe_gate_lds_bytes(int D, int E);
 hipError_t launch_moe_route(const MoeArgs& a, hipStream_t stream);
-hipError_t launch_moe_combine(const MoeArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- grouped GEMM
 // G independent products C_g = A_g W_g (+ epilogue), g = 0..G-1 (one per token):

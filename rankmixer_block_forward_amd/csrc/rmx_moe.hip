@@ -1,11 +1,12 @@
-// Sparse-MoE per-token FFN: ReLU router, token -> expert row lists, combine.
+// Sparse-MoE per-token FFN: ReLU router and token -> expert row lists.
 // RankMixer paper translation, section 3.4 eq (10): for token t with its own E experts,
 // G = ReLU(h(s_t)) and v_t = sum_e G_e * expert_e(s_t); an expert whose gate is zero is
 // not evaluated.  The expert FFNs themselves run as grouped GEMMs (rmx_gemm.hip) over the
 // compacted row lists built here, one group per (token, expert).
 //
 // Group gi = t * E + e.  All lists are deterministic: rows of a group appear in ascending
-// sample order, and the combine sums the experts of a row in expert order.
+// sample order.  The combine (S plus the gate-scaled expert rows, in expert order) runs in
+// the next row pass (rmx_rows.hip).
 #include "rmx_device.h"
 #include "rmx_internal.h"
 
@@ -176,32 +177,6 @@ __global__ __launch_bounds__(64) void moe_scatter_kernel(MoeArgs a) {
   }
 }
 
-// Combine: Y[t][b] = S[t][b] + sum_e (active ? Ye[pos[t][e][b]] : 0), experts in order.
-// Ye rows already carry their gate factor.  One 64-lane wave per (t, b) row.
-__global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * 4 + wave;  // row = t * B + b
-  if (row >= int64_t(a.T) * a.B) return;
-  const int t = int(row / a.B), b = int(row % a.B);
-  const int D = a.D;
-  const bf16_t* s = static_cast<const bf16_t*>(a.S) + size_t(row) * D;
-  float* y = a.Y + size_t(row) * D;
-  for (int c = lane; c < D / 8; c += 64) {
-    float acc[8];
-    load8(s + c * 8, acc);
-    for (int e = 0; e < a.E; ++e) {
-      const int pos = a.pos[size_t(t * a.E + e) * a.B + b];
-      if (pos >= 0) {
-        float v[8];
-        load8(a.Ye + size_t(pos) * D + c * 8, v);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] += v[u];
-      }
-    }
-    store8(y + c * 8, acc);
-  }
-}
-
 }  // namespace
 
 size_t moe_gate_lds_bytes(int D, int E) { return size_t(D / 8) * gate_blk(E) * sizeof(float); }
@@ -239,10 +214,5 @@ hipError_t launch_moe_route(const MoeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_moe_combine(const MoeArgs& a, hipStream_t stream) {
-  const int64_t rows = int64_t(a.T) * a.B;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
 
 }  // namespace rmx

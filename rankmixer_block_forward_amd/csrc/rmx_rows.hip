@@ -13,6 +13,8 @@
 //
 // LayerNorm statistics are two-pass (mean, then mean of squared deviations) in fp32
 // over values held in registers, reduced across the 64 lanes of one wavefront.
+#include <type_traits>
+
 #include "rmx_device.h"
 #include "rmx_internal.h"
 #include "rmx_rowops.h"
@@ -22,10 +24,70 @@ namespace rmx {
 namespace {
 
 // One block input row (token t of sample b) into registers: X0[b, t] (first block) or the
-// previous block's pre-LN2 row Y[t, b] (fp32).
-template <typename T, int W, int NC, int MODE>
+// previous block's pre-LN2 row Y[t, b] (fp32), which after a Sparse-MoE block is the
+// combine S[t, b] + sum over its active experts e, in expert order, of the gate-scaled
+// expert row (RankMixer paper translation, section 3.4 eq (10), plus the block residual).
+template <typename T, int W, int NC, int MODE, bool MOE>
 __device__ __forceinline__ void load_row(const RowsArgs& a, int b, int t, int lane, int nchunks,
                                          float (&v)[NC][W]) {
+  if constexpr (MOE) {
+    {
+      const T* src = static_cast<const T*>(a.in) + (size_t(t) * a.B + b) * a.D;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nchunks) loadw<W>(src + c * W, v[i]);
+      }
+      // The expert rows BAT at a time: a batch's row indices (wave-uniform scalars), then
+      // every load of the batch in flight, held as raw bf16 until added.  An inactive
+      // expert's load reads the S row again (cached) and its add is skipped, so the sum
+      // runs over the active experts in expert order.
+      const int* pos = a.moe_pos + size_t(t) * a.moe_E * a.B + b;
+      const int E = a.moe_E;
+      // registers of one expert row: NC x 4 (W = 8, 8 bf16 in 16 bytes) or NC (W = 1)
+      constexpr int PER = W == 8 ? NC * 4 : NC, BAT0 = 36 / PER;
+      constexpr int BAT = BAT0 < 1 ? 1 : (BAT0 > 4 ? 4 : BAT0);
+      using Raw = typename std::conditional<W == 8, uint4, uint16_t>::type;
+#pragma unroll 1
+      for (int e0 = 0; e0 < E; e0 += BAT) {
+        int r[BAT];
+#pragma unroll
+        for (int j = 0; j < BAT; ++j) r[j] = e0 + j < E ? pos[size_t(e0 + j) * a.B] : -1;
+        Raw u[BAT][NC];
+#pragma unroll
+        for (int j = 0; j < BAT; ++j) {
+          const T* ye = r[j] >= 0 ? static_cast<const T*>(a.moe_ye) + size_t(r[j]) * a.D : src;
+#pragma unroll
+          for (int i = 0; i < NC; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nchunks) u[j][i] = *reinterpret_cast<const Raw*>(ye + c * W);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < BAT; ++j) {
+          if (r[j] >= 0) {
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+              const int c = lane + 64 * i;
+              if (c < nchunks) {
+                if constexpr (W == 8) {
+                  const uint32_t wd[4] = {u[j][i].x, u[j][i].y, u[j][i].z, u[j][i].w};
+#pragma unroll
+                  for (int k = 0; k < 4; ++k) {
+                    v[i][2 * k] += __uint_as_float(wd[k] << 16);
+                    v[i][2 * k + 1] += __uint_as_float(wd[k] & 0xffff0000u);
+                  }
+                } else {
+                  v[i][0] += bf16_to_f32(u[j][i]);
+                }
+              }
+            }
+          }
+        }
+      }
+      return;
+    }
+  }
   if constexpr (MODE == ROWS_FIRST) {
     const T* src = static_cast<const T*>(a.in) + (size_t(b) * a.T + t) * a.D;
 #pragma unroll
@@ -49,12 +111,13 @@ __device__ __forceinline__ void load_row(const RowsArgs& a, int b, int t, int la
 // normalized.
 // Waves per sample: 16, or 8 where the registers of a wide row (or the pool's partial sums)
 // need the room.
-constexpr int rows_max_waves(int NC, int MODE) {
+constexpr int rows_max_waves(int NC, int MODE, bool MOE = false) {
   return MODE == ROWS_FINAL ? (NC > 4 ? 4 : 8) : (NC > 3 ? 8 : 16);
 }
 
-template <typename T, int W, int NC, int MODE>
-__global__ __launch_bounds__(64 * rows_max_waves(NC, MODE)) void rows_kernel(RowsArgs a) {
+template <typename T, int W, int NC, int MODE, bool MOE = false>
+__global__ __launch_bounds__(64 * rows_max_waves(NC, MODE, MOE)) void rows_kernel(RowsArgs a) {
+  static_assert(!MOE || (MODE != ROWS_FIRST && sizeof(T) == 2), "the combine follows a bf16 Sparse-MoE block");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -73,14 +136,14 @@ __global__ __launch_bounds__(64 * rows_max_waves(NC, MODE)) void rows_kernel(Row
 
   // Phase A: the block input rows X[b, t, :] for t = wave, wave + nw, ...
   float nxt[NC][W];
-  if (wave < Tn) load_row<T, W, NC, MODE>(a, b, wave, lane, nchunks, nxt);
+  if (wave < Tn) load_row<T, W, NC, MODE, MOE>(a, b, wave, lane, nchunks, nxt);
   for (int t = wave; t < Tn; t += nw) {
     float v[NC][W];
 #pragma unroll
     for (int i = 0; i < NC; ++i)
 #pragma unroll
       for (int e = 0; e < W; ++e) v[i][e] = nxt[i][e];
-    if (t + nw < Tn) load_row<T, W, NC, MODE>(a, b, t + nw, lane, nchunks, nxt);
+    if (t + nw < Tn) load_row<T, W, NC, MODE, MOE>(a, b, t + nw, lane, nchunks, nxt);
     if constexpr (MODE == ROWS_FIRST) {
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
@@ -218,7 +281,9 @@ __global__ __launch_bounds__(256) void token_mix_kernel(const T* __restrict__ X,
 
 template <typename T, int W, int NC>
 hipError_t launch_rows_nc(int mode, const RowsArgs& a, hipStream_t stream) {
-  const int maxw = rows_max_waves(NC, mode);
+  const bool moe = a.moe_ye != nullptr;
+  if (moe && (sizeof(T) != 2 || mode == ROWS_FIRST)) return hipErrorInvalidValue;
+  const int maxw = rows_max_waves(NC, mode, moe);
   int nw = a.T < maxw ? a.T : maxw;
   size_t lds;
   if (mode == ROWS_FINAL) {
@@ -228,6 +293,15 @@ hipError_t launch_rows_nc(int mode, const RowsArgs& a, hipStream_t stream) {
     lds = size_t(a.T) * a.D * sizeof(T);
   }
   dim3 grid(a.B), block(64 * nw);
+  if constexpr (sizeof(T) == 2) {
+    if (moe) {
+      if (mode == ROWS_MID)
+        hipLaunchKernelGGL((rows_kernel<T, W, NC, ROWS_MID, true>), grid, block, lds, stream, a);
+      else
+        hipLaunchKernelGGL((rows_kernel<T, W, NC, ROWS_FINAL, true>), grid, block, lds, stream, a);
+      return hipGetLastError();
+    }
+  }
   switch (mode) {
     case ROWS_FIRST:
       hipLaunchKernelGGL((rows_kernel<T, W, NC, ROWS_FIRST>), grid, block, lds, stream, a);
@@ -270,6 +344,14 @@ hipError_t set_rows_lds_limit_nc() {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_kernel<T, W, NC, ROWS_MID>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
+  if constexpr (sizeof(T) == 2) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_kernel<T, W, NC, ROWS_MID, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_kernel<T, W, NC, ROWS_FINAL, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+  }
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_kernel<T, W, NC, ROWS_FINAL>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
