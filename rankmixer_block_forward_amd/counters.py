@@ -47,7 +47,7 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 # Every source the grouped-GEMM kernels are compiled from: a record taken on other sources
 # no longer describes the kernels.
-GEMM_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("rmx_gemm.hip", "rmx_device.h", "rmx_internal.h")]
+GEMM_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("rmx_gemm.hip", "rmx_device.h", "rmx_internal.h", "rmx_layout.h")]
 
 # kernel-name patterns -> the names the library's profiling uses
 KERNELS = [
@@ -55,9 +55,9 @@ KERNELS = [
     (re.compile(r"gemm_bf16_mfma(_n384|_n192|_m64)?<1[,>]"), "gemm2_residual"),
     (re.compile(r"gemm_bf16_moe(_n384)?<2>"), "moe_ffn1"),
     (re.compile(r"gemm_bf16_moe(_n384)?<3>"), "moe_ffn2"),
-    (re.compile(r"rows_kernel<[^>]*, 0>"), "rows_first"),
-    (re.compile(r"rows_kernel<[^>]*, 1>"), "rows_ln2_mix_ln1"),
-    (re.compile(r"rows_kernel<[^>]*, 2>"), "rows_ln2_pool"),
+    (re.compile(r"rows_kernel<[^>]*, 0(, (false|true))?>"), "rows_first"),
+    (re.compile(r"rows_kernel<[^>]*, 1(, (false|true))?>"), "rows_ln2_mix_ln1"),
+    (re.compile(r"rows_kernel<[^>]*, 2(, (false|true))?>"), "rows_ln2_pool"),
     (re.compile(r"vectorized_elementwise_kernel<\d+, at::native::neg_kernel"), "copy"),
 ]
 

@@ -89,7 +89,7 @@ def test_request_record_prices_each_request_by_its_size(tmp_path):
     write, 32 per other write; no scale factor enters."""
     g1 = "void rmx::(anonymous namespace)::gemm_bf16_mfma_n192<0>(rmx::GemmArgs)"
     g2 = "void rmx::(anonymous namespace)::gemm_bf16_mfma_m64<1, true, 256>(rmx::GemmArgs)"
-    rows = "void rmx::(anonymous namespace)::rows_kernel<rmx::bf16_t, 8, 3, 1>(rmx::RowsArgs)"
+    rows = "void rmx::(anonymous namespace)::rows_kernel<rmx::bf16_t, 8, 3, 1, false>(rmx::RowsArgs)"
     rd = []
     for k, (a, b, c) in ((g1, (10.0, 20.0, 1000.0)), (g1, (30.0, 40.0, 3000.0)), (g2, (0.0, 0.0, 500.0)),
                          (rows, (0.0, 2.0, 64.0))):
