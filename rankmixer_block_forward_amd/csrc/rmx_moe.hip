@@ -15,98 +15,78 @@ namespace rmx {
 namespace {
 
 // Gate: g[t][e][b] = max(0, S[t][b] . Wg[t][:, e]) in fp32; counts of active rows per
-// (t, e, 64-row chunk).  Grid (chunks, T), 256 threads: wave w handles rows 16 w .. 16 w + 15
-// of the chunk, 8 rows at a time, each row split over 8 lanes (lane = 8 r + s takes the
-// 8-element pieces s, s + 8, ... of row r: the 8 lanes of a row read 128 contiguous bytes).
-// Wg[t] is staged in LDS as fp32, element (d, e) at (d / 8) * GATE_BLK + (d % 8) * EP + e with
-// EP = E rounded up to 4 (zero padded) and GATE_BLK = 8 EP + 4, so that the 8 pieces read
-// in one step fall in distinct banks.  Partial sums meet over the 8 lanes of a row by
-// butterfly exchange, in a fixed order.
+// (t, e, 64-row chunk).  Grid (ceil(B / 256), T), 256 threads: lane l of wave w owns sample
+// row b = 256 blockIdx.x + 64 w + l, which it streams in 16-byte pieces, so a wave covers
+// exactly one 64-row chunk and its counts are one ballot per expert.  Wg[t] is staged in
+// LDS as fp32, element (d, e) at d * EP + e (EP = E rounded up to 4, zero padded); every
+// lane of a wave reads the same weights at the same time (LDS broadcast).  The dot product
+// runs over d in order.  D % 32 == 0 (the expert products' K step).
 __host__ __device__ constexpr int gate_ep(int E) { return (E + 3) & ~3; }
-__host__ __device__ constexpr int gate_blk(int E) { return 8 * gate_ep(E) + 4; }
 
 template <int EP>
 __global__ __launch_bounds__(256) void moe_gate_kernel(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) float wg[];
-  __shared__ int wave_cnt[4][MOE_MAX_E];
-  const int t = blockIdx.y, chunk = blockIdx.x;
+  const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int D = a.D, E = a.E, B = a.B, T = a.T;
-  constexpr int BLK = 8 * EP + 4;
+  // Wg[t] ([D][E] bf16, contiguous, D * E % 8 == 0): 16-byte loads, fp32 into LDS
   const bf16_t* Wg = static_cast<const bf16_t*>(a.Wg) + size_t(t) * D * E;
-  for (int i = threadIdx.x; i < D * EP; i += blockDim.x) {
-    const int d = i / EP, e = i - d * EP;
-    wg[(d >> 3) * BLK + (d & 7) * EP + e] = e < E ? load1(Wg + d * E + e) : 0.f;
+  for (int i = threadIdx.x; i < D * E / 8; i += blockDim.x) {
+    float v[8];
+    load8(Wg + 8 * i, v);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = 8 * i + u, d = idx / E, e = idx - d * E;
+      wg[d * EP + e] = v[u];
+    }
   }
+  if (E < EP)
+    for (int i = threadIdx.x; i < D * (EP - E); i += blockDim.x) {
+      const int d = i / (EP - E), e = E + (i - d * (EP - E));
+      wg[d * EP + e] = 0.f;
+    }
   __syncthreads();
-  const int r = lane >> 3, sl = lane & 7;
-  const int nch = D / 8;
-  int my_cnt[MOE_MAX_E];  // active rows of expert e in this wave (uniform)
+  const int chunk = blockIdx.x * 4 + wave;
+  if (chunk >= a.nchunk) return;  // no barrier follows
+  const int b = chunk * 64 + lane;
+  const bool in = b < B;
+  float acc[EP];
 #pragma unroll
-  for (int e = 0; e < MOE_MAX_E; ++e) my_cnt[e] = 0;
-  for (int grp = 0; grp < 2; ++grp) {
-    const int b = chunk * 64 + wave * 16 + grp * 8 + r;
-    const bool in = b < B;
-    float acc[EP];
+  for (int e = 0; e < EP; ++e) acc[e] = 0.f;
+  if (in) {
+    const bf16_t* srow = static_cast<const bf16_t*>(a.S) + (size_t(t) * B + b) * D;
+    // four 16-byte pieces in flight per step (D % 32 == 0 on this path)
+    for (int c0 = 0; c0 < D / 8; c0 += 4) {
+      float v[4][8];
 #pragma unroll
-    for (int e = 0; e < EP; ++e) acc[e] = 0.f;
-    if (in) {
-      const bf16_t* srow = static_cast<const bf16_t*>(a.S) + (size_t(t) * B + b) * D;
-      for (int c = sl; c < nch; c += 8) {
-        float v[8];
-        load8(srow + c * 8, v);
-        const float* wb = wg + c * BLK;
+      for (int j = 0; j < 4; ++j) load8(srow + (c0 + j) * 8, v[j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float* wb = wg + (c0 + j) * 8 * EP;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
 #pragma unroll
           for (int e4 = 0; e4 < EP; e4 += 4) {
             const float4 w = *reinterpret_cast<const float4*>(wb + u * EP + e4);
-            acc[e4 + 0] = fmaf(v[u], w.x, acc[e4 + 0]);
-            acc[e4 + 1] = fmaf(v[u], w.y, acc[e4 + 1]);
-            acc[e4 + 2] = fmaf(v[u], w.z, acc[e4 + 2]);
-            acc[e4 + 3] = fmaf(v[u], w.w, acc[e4 + 3]);
+            acc[e4 + 0] = fmaf(v[j][u], w.x, acc[e4 + 0]);
+            acc[e4 + 1] = fmaf(v[j][u], w.y, acc[e4 + 1]);
+            acc[e4 + 2] = fmaf(v[j][u], w.z, acc[e4 + 2]);
+            acc[e4 + 3] = fmaf(v[j][u], w.w, acc[e4 + 3]);
           }
         }
       }
     }
-    // sum over the 8 lanes of the row (every lane ends with all totals)
-#pragma unroll
-    for (int e = 0; e < EP; ++e) {
-      float x = acc[e];
-      x += __shfl_xor(x, 1, 64);
-      x += __shfl_xor(x, 2, 64);
-      x += __shfl_xor(x, 4, 64);
-      acc[e] = x;
-    }
-    // lane s of the row writes experts s and s + 8
-#pragma unroll
-    for (int h = 0; h < (EP + 7) / 8; ++h) {
-      const int e = sl + 8 * h;
-      float tot = 0.f;
-#pragma unroll
-      for (int k = 0; k < EP; ++k)
-        if (k == e) tot = acc[k];
-      const float gv = tot > 0.f ? tot : 0.f;
-      const bool act = in && e < E && gv > 0.f;
-      if (in && e < E) {
-        a.g[(size_t(t) * E + e) * B + b] = gv;
-        if (a.gate_out) a.gate_out[(size_t(b) * T + t) * E + e] = gv;
-      }
-      const uint64_t m = __ballot(act);
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (8 * h + k < MOE_MAX_E) my_cnt[8 * h + k] += __popcll(m & (0x0101010101010101ull << k));
-    }
   }
-  if (lane == 0)
 #pragma unroll
-    for (int e = 0; e < MOE_MAX_E; ++e)
-      if (e < E) wave_cnt[wave][e] = my_cnt[e];
-  __syncthreads();
-  if (threadIdx.x < E) {
-    const int e = threadIdx.x;
-    a.cnt[(size_t(t) * E + e) * a.nchunk + chunk] =
-        wave_cnt[0][e] + wave_cnt[1][e] + wave_cnt[2][e] + wave_cnt[3][e];
+  for (int e = 0; e < EP; ++e) {
+    if (e >= E) break;
+    const float gv = acc[e] > 0.f ? acc[e] : 0.f;
+    if (in) {
+      a.g[(size_t(t) * E + e) * B + b] = gv;
+      if (a.gate_out) a.gate_out[(size_t(b) * T + t) * E + e] = gv;
+    }
+    const uint64_t m = __ballot(in && gv > 0.f);
+    if (lane == 0) a.cnt[(size_t(t) * E + e) * a.nchunk + chunk] = __popcll(m);
   }
 }
 
@@ -179,7 +159,7 @@ __global__ __launch_bounds__(64) void moe_scatter_kernel(MoeArgs a) {
 
 }  // namespace
 
-size_t moe_gate_lds_bytes(int D, int E) { return size_t(D / 8) * gate_blk(E) * sizeof(float); }
+size_t moe_gate_lds_bytes(int D, int E) { return size_t(D) * gate_ep(E) * sizeof(float); }
 
 hipError_t moe_init() {
   const int bytes = int(MOE_MAX_GATE_LDS);
@@ -199,7 +179,7 @@ hipError_t moe_init() {
 
 hipError_t launch_moe_route(const MoeArgs& a, hipStream_t stream) {
   const size_t lds = moe_gate_lds_bytes(a.D, a.E);
-  const dim3 grid(a.nchunk, a.T);
+  const dim3 grid((a.nchunk + 3) / 4, a.T);
   switch (gate_ep(a.E)) {
     case 4: hipLaunchKernelGGL((moe_gate_kernel<4>), grid, dim3(256), lds, stream, a); break;
     case 8: hipLaunchKernelGGL((moe_gate_kernel<8>), grid, dim3(256), lds, stream, a); break;
