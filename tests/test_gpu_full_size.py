@@ -124,7 +124,11 @@ def _check_gates_vs_oracle(g, g_ref, label):
 
 
 @pytest.mark.parametrize("B,T,D,E,h,L", [(100, 4, 64, 4, 64, 2), (300, 2, 256, 8, 96, 1), (1, 4, 64, 2, 32, 1),
-                                         (257, 8, 128, 3, 128, 2), (700, 2, 384, 8, 1152, 1)])
+                                         (257, 8, 128, 3, 128, 2), (700, 2, 384, 8, 1152, 1),
+                                         # D / T = 8 and one 8-column chunk per lane in the combine
+                                         (60, 16, 128, 2, 32, 2),
+                                         # the most experts a token may have
+                                         (130, 4, 64, 16, 32, 2)])
 def test_moe_routing_lists_bit_exact(B, T, D, E, h, L):
     cfg = synth.Config("moe", B=B, T=T, D=D, k=2, L=L, dtype="bf16", E=E, moe_hidden=h, bias_std=0.02)
     inp = synth.make_inputs(cfg, seed=B + E)
