@@ -421,10 +421,12 @@ rmx_status rmx_create(const rmx_config* cfg, rmx_handle** out_handle) {
       alloc(&h->aX, nS * esz);
       alloc(&h->a_pool, size_t(cfg->max_batch) * cfg->D * sizeof(float));
     }
-    alloc(&h->Y, nS * sizeof(float));
     if (cfg->moe_experts == 0) {
+      alloc(&h->Y, nS * sizeof(float));
       alloc(&h->H, prow * size_t(cfg->k) * cfg->D * esz);
     } else {
+      // no Y: the row pass after a Sparse-MoE block forms its pre-LN2 rows from S and the
+      // expert rows
       const size_t G = size_t(cfg->T) * cfg->moe_experts, mb = size_t(cfg->max_batch);
       const size_t nchunk = (mb + 63) / 64, R = G * mb;
       alloc(&h->moe_g, G * mb * sizeof(float));

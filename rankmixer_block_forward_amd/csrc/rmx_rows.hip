@@ -31,62 +31,60 @@ template <typename T, int W, int NC, int MODE, bool MOE>
 __device__ __forceinline__ void load_row(const RowsArgs& a, int b, int t, int lane, int nchunks,
                                          float (&v)[NC][W]) {
   if constexpr (MOE) {
-    {
-      const T* src = static_cast<const T*>(a.in) + (size_t(t) * a.B + b) * a.D;
+    const T* src = static_cast<const T*>(a.in) + (size_t(t) * a.B + b) * a.D;
 #pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const int c = lane + 64 * i;
-        if (c < nchunks) loadw<W>(src + c * W, v[i]);
-      }
-      // The expert rows BAT at a time: a batch's row indices (wave-uniform scalars), then
-      // every load of the batch in flight, held as raw bf16 until added.  An inactive
-      // expert's load reads the S row again (cached) and its add is skipped, so the sum
-      // runs over the active experts in expert order.
-      const int* pos = a.moe_pos + size_t(t) * a.moe_E * a.B + b;
-      const int E = a.moe_E;
-      // registers of one expert row: NC x 4 (W = 8, 8 bf16 in 16 bytes) or NC (W = 1)
-      constexpr int PER = W == 8 ? NC * 4 : NC, BAT0 = 36 / PER;
-      constexpr int BAT = BAT0 < 1 ? 1 : (BAT0 > 4 ? 4 : BAT0);
-      using Raw = typename std::conditional<W == 8, uint4, uint16_t>::type;
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunks) loadw<W>(src + c * W, v[i]);
+    }
+    // The expert rows BAT at a time: a batch's row indices (wave-uniform scalars), then
+    // every load of the batch in flight, held as raw bf16 until added.  An inactive
+    // expert's load reads the S row again (cached) and its add is skipped, so the sum
+    // runs over the active experts in expert order.
+    const int* pos = a.moe_pos + size_t(t) * a.moe_E * a.B + b;
+    const int E = a.moe_E;
+    // registers of one expert row: NC x 4 (W = 8, 8 bf16 in 16 bytes) or NC (W = 1)
+    constexpr int PER = W == 8 ? NC * 4 : NC, BAT0 = 36 / PER;
+    constexpr int BAT = BAT0 < 1 ? 1 : (BAT0 > 4 ? 4 : BAT0);
+    using Raw = typename std::conditional<W == 8, uint4, uint16_t>::type;
 #pragma unroll 1
-      for (int e0 = 0; e0 < E; e0 += BAT) {
-        int r[BAT];
+    for (int e0 = 0; e0 < E; e0 += BAT) {
+      int r[BAT];
 #pragma unroll
-        for (int j = 0; j < BAT; ++j) r[j] = e0 + j < E ? pos[size_t(e0 + j) * a.B] : -1;
-        Raw u[BAT][NC];
+      for (int j = 0; j < BAT; ++j) r[j] = e0 + j < E ? pos[size_t(e0 + j) * a.B] : -1;
+      Raw u[BAT][NC];
 #pragma unroll
-        for (int j = 0; j < BAT; ++j) {
-          const T* ye = r[j] >= 0 ? static_cast<const T*>(a.moe_ye) + size_t(r[j]) * a.D : src;
+      for (int j = 0; j < BAT; ++j) {
+        const T* ye = r[j] >= 0 ? static_cast<const T*>(a.moe_ye) + size_t(r[j]) * a.D : src;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const int c = lane + 64 * i;
+          if (c < nchunks) u[j][i] = *reinterpret_cast<const Raw*>(ye + c * W);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < BAT; ++j) {
+        if (r[j] >= 0) {
 #pragma unroll
           for (int i = 0; i < NC; ++i) {
             const int c = lane + 64 * i;
-            if (c < nchunks) u[j][i] = *reinterpret_cast<const Raw*>(ye + c * W);
-          }
-        }
+            if (c < nchunks) {
+              if constexpr (W == 8) {
+                const uint32_t wd[4] = {u[j][i].x, u[j][i].y, u[j][i].z, u[j][i].w};
 #pragma unroll
-        for (int j = 0; j < BAT; ++j) {
-          if (r[j] >= 0) {
-#pragma unroll
-            for (int i = 0; i < NC; ++i) {
-              const int c = lane + 64 * i;
-              if (c < nchunks) {
-                if constexpr (W == 8) {
-                  const uint32_t wd[4] = {u[j][i].x, u[j][i].y, u[j][i].z, u[j][i].w};
-#pragma unroll
-                  for (int k = 0; k < 4; ++k) {
-                    v[i][2 * k] += __uint_as_float(wd[k] << 16);
-                    v[i][2 * k + 1] += __uint_as_float(wd[k] & 0xffff0000u);
-                  }
-                } else {
-                  v[i][0] += bf16_to_f32(u[j][i]);
+                for (int k = 0; k < 4; ++k) {
+                  v[i][2 * k] += __uint_as_float(wd[k] << 16);
+                  v[i][2 * k + 1] += __uint_as_float(wd[k] & 0xffff0000u);
                 }
+              } else {
+                v[i][0] += bf16_to_f32(u[j][i]);
               }
             }
           }
         }
       }
-      return;
     }
+    return;
   }
   if constexpr (MODE == ROWS_FIRST) {
     const T* src = static_cast<const T*>(a.in) + (size_t(b) * a.T + t) * a.D;
