@@ -68,7 +68,9 @@ typedef enum {
  *   k        FFN expansion: the hidden width is k*D (paper section 3.3.2 eq (7)).
  *   L        number of stacked blocks (paper section 3.1 eq (1)), L >= 1.
  *   dtype    storage and MFMA input type of X, every weight, S and the hidden
- *            activations.  Accumulation, LayerNorm and GELU are always fp32.
+ *            activations (and of the Sparse-MoE PFFN's gate-scaled expert outputs, which
+ *            the combine sums in fp32).  Accumulation, LayerNorm and GELU are always fp32;
+ *            the dense block's pre-LN2 rows stay fp32.
  *   ln_eps   LayerNorm epsilon (1e-5 in "RankMixer 详解（1）", section 6.1).
  *   max_batch  largest B a forward call may pass; the workspace is sized for it.
  *   moe_experts  0 = dense per-token FFN; E > 0 = Sparse-MoE PFFN with E experts per
