@@ -51,8 +51,8 @@ GEMM_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("rmx_gemm.hip", "rmx_devi
 
 # kernel-name patterns -> the names the library's profiling uses
 KERNELS = [
-    (re.compile(r"gemm_bf16_mfma(_n384|_n192|_m64)?<0[,>]"), "gemm1_gelu"),
-    (re.compile(r"gemm_bf16_mfma(_n384|_n192|_m64)?<1[,>]"), "gemm2_residual"),
+    (re.compile(r"gemm_bf16_mfma(_n384|_n192|_m64|_w8)?<0[,>]"), "gemm1_gelu"),
+    (re.compile(r"gemm_bf16_mfma(_n384|_n192|_m64|_w8)?<1[,>]"), "gemm2_residual"),
     (re.compile(r"gemm_bf16_moe(_n384)?<2>"), "moe_ffn1"),
     (re.compile(r"gemm_bf16_moe(_n384)?<3>"), "moe_ffn2"),
     (re.compile(r"rows_kernel<[^>]*, 0(, (false|true))?>"), "rows_first"),

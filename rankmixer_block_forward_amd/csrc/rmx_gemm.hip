@@ -1149,6 +1149,172 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_n192(GemmArgs 
   tile_epilogue3<EPI, TM>(acc, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN3, mt * TM, wave, lane);
 }
 
+// ------------------------------------------ 256 x 384 tiles on eight waves, one per CU
+// The 256 x 384 tile's single wave per SIMD leaves the matrix cores idle during its epilogue
+// and during LDS reads that the ring does not hide; two 256 x 192 workgroups per CU fill
+// those gaps but copy each A block twice.  Here one workgroup of eight waves takes a
+// 256 x 384 tile as two groups of four: group 0 computes columns 0..191, group 1 columns
+// 192..383, each wave a 128 x 96 part (4 x 3 blocks of 32 x 32, 192 AGPR accumulators), so
+// a SIMD runs two waves and A is staged once for both halves.  A stage holds the 16 KB A
+// block and the tile's 384 W^T rows (24 KB) as 40 pieces of 1 KB: wave w copies A pieces w
+// and w + 8 and W^T pieces w, w + 8, w + 16 (rows 16 q .. 16 q + 15 of the tile), five
+// copies per K step, in a 3-stage ring (120 KB).  The next step's copies are issued between
+// the second sub-step's MFMAs (after products 1, 3, 5, 7 and 9 of its 12), where they keep
+// the copy queue busy without stalling the LDS reads.  Measured at the 1B shape, B = 2048:
+// GELU product 1.12 ms against 1.18 for 256 x 192 tiles two to a CU, residual product
+// 0.98 ms against 1.05 for the four-wave 256 x 384 tile.  Per block the same MFMAs in the
+// same K order as the other tile shapes, so the bits are the same.
+constexpr int W8_THREADS = 512;
+constexpr int W8_NS = 3;
+
+__device__ __forceinline__ void mfma_tile_w8(f32x16_t (&acc)[4][3], __amdgpu_buffer_rsrc_t rA,
+                                             __amdgpu_buffer_rsrc_t rW, lds_u8* smem, uint32_t lds0, int K, int nt,
+                                             int wave, int lane) {
+  constexpr int NI = 4;                      // row blocks per wave
+  constexpr int APW = 2;                     // A pieces per wave and K step
+  constexpr int NCP = 5;                     // copies per wave and K step
+  constexpr int SA = A_STAGE_BYTES;          // A part of a stage
+  constexpr int SG = STAGE6_BYTES;           // stage bytes
+  const int nk = K / BK;
+  // W^T piece q = wave + 8 c holds rows 16 q .. 16 q + 15 of the tile (inside one 256-row
+  // packed block, since 384 nt and 16 q are multiples of 16)
+  uint32_t voffW[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const int row = BN6 * nt + 16 * (wave + 8 * c);
+    voffW[c] = uint32_t(row >> 8) * uint32_t(nk) * 16384u + uint32_t(row & 255) * 64u + uint32_t(lane) * 16u;
+  }
+  // copy c of K step kt into a stage; steps past the last re-read the last (never consumed)
+  auto copy = [&](int kt, int stage, int c) {
+    kt = kt < nk ? kt : nk - 1;
+    const uint32_t sbase = lds0 + uint32_t(stage) * SG;
+    if (c < APW) {
+      const uint32_t piece = uint32_t(wave + 8 * c);
+      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), piece * 1024u + uint32_t(lane) * 16u, rA,
+                  kt * 16384);
+    } else {
+      const uint32_t q = uint32_t(wave + 8 * (c - APW));
+      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + SA + q * 1024u), voffW[c - APW], rW, kt * 16384);
+    }
+  };
+  const int grp = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
+  uint32_t aoff[2], boff[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int c = kk * 2 + (lane >> 5);
+    aoff[kk] = pk_lds_off(wm * 128 + (lane & 31), c);
+    boff[kk] = uint32_t(SA) + pk_lds_off(grp * BN3 + wn * 96 + (lane & 31), c);
+  }
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  u32x4_t a0[NI], a1[NI], b[3];
+  auto read_a = [&](u32x4_t (&a)[NI], const lds_u8* sp, int kk) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) a[i] = *reinterpret_cast<const lds_u32x4*>(sp + aoff[kk] + i * 2048);
+  };
+  auto read_b = [&](const lds_u8* sp, int kk, int j) {
+    b[j] = *reinterpret_cast<const lds_u32x4*>(sp + boff[kk] + j * 2048);
+  };
+  auto mm = [&](const u32x4_t (&a)[NI], int i, int j) {
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[j]),
+                                                        __builtin_bit_cast(bf16x8_t, a[i]), acc[i][j], 0, 0, 0);
+  };
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#pragma unroll
+  for (int st = 0; st < W8_NS; ++st)
+#pragma unroll
+    for (int c = 0; c < NCP; ++c) copy(st, st, c);
+  // step 0 has landed when at most the two later steps' copies (10) are outstanding
+  asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+  read_a(a0, smem, 0);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) read_b(smem, 0, j);
+  int stage = 0;
+  for (int it = 0; it < nk; ++it) {
+    const lds_u8* sp = smem + stage * SG;
+    const int nstage = stage + 1 == W8_NS ? 0 : stage + 1;
+    // sub-step 0 (K columns 0..15 of the step) while the fragments of sub-step 1 are read
+    read_a(a1, sp, 1);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) mm(a0, i, j);
+      __builtin_amdgcn_sched_barrier(0);
+      read_b(sp, 1, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // every wave has read this stage and step it + 1 has landed (the copies of step it + 2,
+    // five per wave, may still be outstanding)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // sub-step 1 while step it + 3 is copied into the stage just consumed and the next
+    // stage's sub-step 0 fragments are read
+    const lds_u8* np = smem + nstage * SG;
+    read_a(a0, np, 0);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        mm(a1, i, j);
+        const int q = NI * j + i;
+        if (q & 1 && q <= 9) {
+          __builtin_amdgcn_sched_barrier(0);
+          copy(it + W8_NS, stage, q / 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      read_b(np, 0, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    stage = nstage;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// Dense per-token product on packed operands with 256 x 384 tiles of eight waves:
+// G * ceil(M/256) * N/384 workgroups of 512 threads, N % 384 == 0; EPI_GELU or EPI_RESID.
+template <int EPI>
+__global__ __launch_bounds__(W8_THREADS, 1) void gemm_bf16_mfma_w8(GemmArgs p) {
+  static_assert(EPI == EPI_GELU || EPI == EPI_RESID, "eight-wave tiles serve the inference epilogues");
+  static_assert(8 * 32 * LD3 * 4 <= W8_NS * STAGE6_BYTES, "epilogue staging fits in the ring");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[W8_NS * STAGE6_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_g;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nMt = (M + BM - 1) / BM, nNt = N / BN6;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = id / (nMt * nNt);
+  const int rem = id - g * nMt * nNt;
+  // bands of TILE_BAND row tiles, M-fastest inside a band (as in the 256 x 256 kernel)
+  int mt, nt;
+  band_tile(rem, nMt, nNt, mt, nt);
+  // the tile's A block (packed row block, K/32 x 16 KB) and the token's whole W^T
+  // (pk_rows(N) rows; slices < 2^31 bytes, checked at launch)
+  const uint32_t blk = uint32_t(K / BK) * 16384u;
+  const uint32_t wbytes = uint32_t(pk_rows(N) / 256) * blk;
+  const __amdgpu_buffer_rsrc_t rA =
+      make_rsrc(static_cast<const uint16_t*>(p.A) + (size_t(g) * nMt + mt) * (size_t(blk) / 2), blk);
+  const __amdgpu_buffer_rsrc_t rW =
+      make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * (size_t(wbytes) / 2), wbytes);
+  f32x16_t acc[4][3];
+  mfma_tile_w8(acc, rA, rW, smem, lds0, K, nt, wave, lane);
+  const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
+  // each group stores its 256 x 192 half with the 256 x 192 tile's epilogue (staging rows
+  // of its four waves after the other group's)
+  const int grp = wave >> 2;
+  tile_epilogue3<EPI, 256>(acc, reinterpret_cast<float*>(smem_g) + grp * 4 * 32 * LD3, p, g, bias_g,
+                           nt * BN6 + grp * BN3, mt * BM, wave & 3, lane);
+}
+
 // Dense per-token product with row-major A (the training forward's saved S and H) and
 // prepared W^T, 256 x 384 tiles: A rows are gathered straight into the packed LDS layout (the
 // K loop of the Sparse-MoE kernel), the epilogue writes row-major outputs.  Per block the
@@ -1849,13 +2015,23 @@ namespace {
 //   128 x 192, two per CU: 17 per round of 2 CUs tiles, 12 when the launch holds at most
 //       one tile per CU (RankMixer-100M GEMM2, B = 512: 256 tiles, 56 us against 77 us for
 //       its 128 x 384 tiles, which leave half of the CUs idle)
+//   256 x 384 on eight waves: 26 per round of CUs tiles (1B, B = 2048: GELU product 1.12
+//       against 1.18 ms on 256 x 192 tiles, residual product 0.98 against 1.05 ms)
 // The fewest units win; ties go to the shape listed first.  384-wide tiles need
 // N % 384 == 0, 192-wide ones N % 192 == 0, all of them a token's packed W^T below 2^31
 // bytes (their buffer descriptor spans it).
-// The environment variable RMX_WIDE_TILES = always / half / pair / pairhalf / never forces
-// 256 x 384, 128 x 384, 256 x 192, 128 x 192 or 256 x 256 (tests and tuning; read at each
-// launch; a shape N does not divide falls back to 256 x 256); all give the same bits.
-enum TileShape { TILES_256 = 0, TILES_256x384 = 1, TILES_128x384 = 2, TILES_256x192 = 3, TILES_128x192 = 4 };
+// The environment variable RMX_WIDE_TILES = always / half / pair / pairhalf / wide8 / never
+// forces 256 x 384, 128 x 384, 256 x 192, 128 x 192, 256 x 384 on eight waves or 256 x 256
+// (tests and tuning; read at each launch; a shape N does not divide falls back to
+// 256 x 256); all give the same bits.
+enum TileShape {
+  TILES_256 = 0,
+  TILES_256x384 = 1,
+  TILES_128x384 = 2,
+  TILES_256x192 = 3,
+  TILES_128x192 = 4,
+  TILES_256x384w8 = 5
+};
 
 TileShape pick_tiles(const GemmArgs& a, int epi) {
   const char* force = getenv("RMX_WIDE_TILES");
@@ -1867,6 +2043,7 @@ TileShape pick_tiles(const GemmArgs& a, int epi) {
     if (strcmp(force, "half") == 0) return n384 ? TILES_128x384 : TILES_256;
     if (strcmp(force, "pair") == 0) return n192 ? TILES_256x192 : TILES_256;
     if (strcmp(force, "pairhalf") == 0) return n192 ? TILES_128x192 : TILES_256;
+    if (strcmp(force, "wide8") == 0) return n384 ? TILES_256x384w8 : TILES_256;
   }
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1882,6 +2059,7 @@ TileShape pick_tiles(const GemmArgs& a, int epi) {
   };
   if (n384) {
     consider(TILES_256x384, 28 * rounds(G * m256 * (a.N / BN6), cus));
+    consider(TILES_256x384w8, 26 * rounds(G * m256 * (a.N / BN6), cus));
     consider(TILES_128x384, 17 * rounds(G * m128 * (a.N / BN6), cus));
   }
   if (n192) {
@@ -1930,6 +2108,14 @@ hipError_t launch_dense_mfma(int epi, const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const TileShape shape = PK && (epi == EPI_GELU || epi == EPI_RESID) ? pick_tiles(a, epi) : TILES_256;
+  if (shape == TILES_256x384w8) {
+    const int tiles6 = a.G * ((a.M + BM - 1) / BM) * (a.N / BN6);
+    if (epi == EPI_GELU)
+      hipLaunchKernelGGL((gemm_bf16_mfma_w8<EPI_GELU>), dim3(tiles6), dim3(W8_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_mfma_w8<EPI_RESID>), dim3(tiles6), dim3(W8_THREADS), 0, stream, a);
+    return hipGetLastError();
+  }
   if (shape == TILES_256x192) {
     const int tiles3 = a.G * ((a.M + BM - 1) / BM) * (a.N / BN3);
     if (epi == EPI_GELU)

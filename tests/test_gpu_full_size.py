@@ -49,14 +49,21 @@ def _inputs(cfg, B=None):
     return dataclasses.replace(base, cfg=cfg, X=synth.make_x(cfg, seed=0, B=B))
 
 
-def test_rankmixer_1b_full_size_256_samples():
-    """RankMixer-1B at B = 2048: prepared weights (the benchmark's launch) and row-major
-    weights give the same bits; 256 samples (32 in each of the 8 row tiles) against the
-    oracle, on X_L and on the pooled output."""
+def test_rankmixer_1b_full_size_256_samples(monkeypatch):
+    """RankMixer-1B at B = 2048: prepared weights (the benchmark's launch), the same with the
+    256 x 192 and four-wave 256 x 384 tiles forced, and row-major weights give the same
+    bits; 256 samples (32 in each of the 8 row tiles) against the oracle, on X_L and on the
+    pooled output."""
     cfg = synth.B1
     inp = _inputs(cfg)
     print(f"case 1B B={cfg.B} prepared weights", flush=True)
     o_pk, xl_pk = run_gpu(cfg, inp, packed=True)
+    for policy in ("pair", "always"):
+        print(f"case 1B B={cfg.B} prepared weights, RMX_WIDE_TILES={policy}", flush=True)
+        monkeypatch.setenv("RMX_WIDE_TILES", policy)
+        o_f, xl_f = run_gpu(cfg, inp, packed=True)
+        monkeypatch.delenv("RMX_WIDE_TILES")
+        assert np.array_equal(o_pk, o_f) and np.array_equal(xl_pk, xl_f), policy
     print(f"case 1B B={cfg.B} row-major weights", flush=True)
     o_rm, xl_rm = run_gpu(cfg, inp)
     assert np.array_equal(o_pk, o_rm) and np.array_equal(xl_pk, xl_rm)

@@ -146,7 +146,8 @@ def test_prepared_weights_bit_identical(B, T, D, k, L, monkeypatch):
     """Weights prepared by rmx_pack_weights (and the packed S and H they bring) give the
     same bits as the row-major path, and match the oracle; the same with the 256 x 384 tiles
     (RMX_WIDE_TILES=always) or the 128 x 384 tiles (=half) forced where N % 384 == 0, the
-    256 x 192 or 128 x 192 tiles two to a CU (=pair, =pairhalf) where N % 192 == 0, with
+    256 x 192 or 128 x 192 tiles two to a CU (=pair, =pairhalf) where N % 192 == 0, the
+    256 x 384 tiles on eight waves (=wide8) where N % 384 == 0, with
     both forbidden (=never), and, up to 128 rows per token, with the 64 x 128 tiles forced
     or forbidden (RMX_NARROW_TILES), since at these sizes the launch picks by occupancy."""
     cfg = synth.Config("pk", B=B, T=T, D=D, k=k, L=L, dtype="bf16", bias_std=0.02)
@@ -155,7 +156,7 @@ def test_prepared_weights_bit_identical(B, T, D, k, L, monkeypatch):
     o2, xl2 = run_gpu(cfg, inp, packed=True)
     assert np.array_equal(o1, o2) and np.array_equal(xl1, xl2)
     for var, policy in (("RMX_WIDE_TILES", "always"), ("RMX_WIDE_TILES", "half"), ("RMX_WIDE_TILES", "pair"),
-                        ("RMX_WIDE_TILES", "pairhalf"), ("RMX_WIDE_TILES", "never"),
+                        ("RMX_WIDE_TILES", "pairhalf"), ("RMX_WIDE_TILES", "wide8"), ("RMX_WIDE_TILES", "never"),
                         ("RMX_NARROW_TILES", "always"), ("RMX_NARROW_TILES", "never")):
         monkeypatch.setenv(var, policy)
         o3, xl3 = run_gpu(cfg, inp, packed=True)
