@@ -1167,10 +1167,16 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void gemm_bf16_mfma_n192(GemmArgs 
 constexpr int W8_THREADS = 512;
 constexpr int W8_NS = 3;
 
+// K loop of an eight-wave 256 x 384 tile.  GATHER_A: A is gathered from row-major rows as in
+// mfma_tile_pk6; offA[c] is this lane's byte offset of piece wave + 8 c at K step 0.  NI < 4:
+// only the wave's first NI row blocks hold rows; the others are neither read nor multiplied
+// and their accumulators stay zero.  Copies and barriers are the same for every NI, so the
+// waves of one workgroup may run different NI.
+template <bool GATHER_A, int NI>
 __device__ __forceinline__ void mfma_tile_w8(f32x16_t (&acc)[4][3], __amdgpu_buffer_rsrc_t rA,
                                              __amdgpu_buffer_rsrc_t rW, lds_u8* smem, uint32_t lds0, int K, int nt,
-                                             int wave, int lane) {
-  constexpr int NI = 4;                      // row blocks per wave
+                                             int wave, int lane, const uint32_t (&offA)[2]) {
+  static_assert(NI >= 0 && NI <= 4, "row blocks of a wave");
   constexpr int APW = 2;                     // A pieces per wave and K step
   constexpr int NCP = 5;                     // copies per wave and K step
   constexpr int SA = A_STAGE_BYTES;          // A part of a stage
@@ -1190,8 +1196,11 @@ __device__ __forceinline__ void mfma_tile_w8(f32x16_t (&acc)[4][3], __amdgpu_buf
     const uint32_t sbase = lds0 + uint32_t(stage) * SG;
     if (c < APW) {
       const uint32_t piece = uint32_t(wave + 8 * c);
-      copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), piece * 1024u + uint32_t(lane) * 16u, rA,
-                  kt * 16384);
+      if constexpr (GATHER_A)
+        copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), offA[c], rA, kt * BK * 2);
+      else
+        copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + piece * 1024u), piece * 1024u + uint32_t(lane) * 16u, rA,
+                    kt * 16384);
     } else {
       const uint32_t q = uint32_t(wave + 8 * (c - APW));
       copy_to_lds(__builtin_amdgcn_readfirstlane(sbase + SA + q * 1024u), voffW[c - APW], rW, kt * 16384);
@@ -1206,20 +1215,21 @@ __device__ __forceinline__ void mfma_tile_w8(f32x16_t (&acc)[4][3], __amdgpu_buf
     boff[kk] = uint32_t(SA) + pk_lds_off(grp * BN3 + wn * 96 + (lane & 31), c);
   }
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
-  u32x4_t a0[NI], a1[NI], b[3];
-  auto read_a = [&](u32x4_t (&a)[NI], const lds_u8* sp, int kk) {
+  constexpr int NA = NI > 0 ? NI : 1;
+  u32x4_t a0[NA], a1[NA], b[3];
+  auto read_a = [&](u32x4_t (&a)[NA], const lds_u8* sp, int kk) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) a[i] = *reinterpret_cast<const lds_u32x4*>(sp + aoff[kk] + i * 2048);
   };
   auto read_b = [&](const lds_u8* sp, int kk, int j) {
-    b[j] = *reinterpret_cast<const lds_u32x4*>(sp + boff[kk] + j * 2048);
+    if constexpr (NI > 0) b[j] = *reinterpret_cast<const lds_u32x4*>(sp + boff[kk] + j * 2048);
   };
-  auto mm = [&](const u32x4_t (&a)[NI], int i, int j) {
+  auto mm = [&](const u32x4_t (&a)[NA], int i, int j) {
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[j]),
                                                         __builtin_bit_cast(bf16x8_t, a[i]), acc[i][j], 0, 0, 0);
   };
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 3; ++j)
 #pragma unroll
@@ -1254,15 +1264,16 @@ __device__ __forceinline__ void mfma_tile_w8(f32x16_t (&acc)[4][3], __amdgpu_buf
     asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     // sub-step 1 while step it + 3 is copied into the stage just consumed and the next
-    // stage's sub-step 0 fragments are read
+    // stage's sub-step 0 fragments are read; the copies go after products 1, 3, 5, 7, 9 of
+    // the sub-step's twelve (by position, whether or not a row block is multiplied)
     const lds_u8* np = smem + nstage * SG;
     read_a(a0, np, 0);
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        mm(a1, i, j);
-        const int q = NI * j + i;
+      for (int i = 0; i < 4; ++i) {
+        if (i < NI) mm(a1, i, j);
+        const int q = 4 * j + i;
         if (q & 1 && q <= 9) {
           __builtin_amdgcn_sched_barrier(0);
           copy(it + W8_NS, stage, q / 2);
@@ -1277,6 +1288,100 @@ __device__ __forceinline__ void mfma_tile_w8(f32x16_t (&acc)[4][3], __amdgpu_buf
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+}
+
+// Epilogue of an eight-wave 256 x 384 tile: each group of four waves stores its 256 x 192
+// half as tile_epilogue3 does (32-column blocks staged through LDS, four lanes per row with
+// eight columns each, 16 rows per pass), its staging rows after the other group's.  Tile row
+// r is output row row_of(r) (-1: not stored); a wave's row blocks from nib on hold no rows
+// and are skipped.  The arithmetic of each epilogue is that of tile_epilogue6.
+template <int EPI, bool RM = false, typename RowOf>
+__device__ __forceinline__ void tile_epilogue_w8(const f32x16_t (&acc)[4][3], float* smem_f, const GemmArgs& p,
+                                                 int g, const bf16_t* bias_g, int n0, int wave, int lane,
+                                                 RowOf row_of, int nib = 4) {
+  const int M = p.M, N = p.N;
+  const int wg = wave & 3;
+  const int wrow0 = (wg >> 1) * 128, wcol0 = (wave >> 2) * BN3 + (wg & 1) * 96;
+  float* st = smem_f + wave * 32 * LD3;
+  const int col8 = (lane & 3) * 8;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int n = n0 + wcol0 + j * 32 + col8;
+    float bias[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bias[e] = 0.f;
+    if (bias_g) load8(bias_g + n, bias);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= nib) break;  // row blocks past the rows (wave-uniform)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(st + (lane & 31) * LD3 + 8 * g4 + 4 * (lane >> 5)) =
+            make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]);
+      // the staging rows are private to this wave, whose LDS operations complete in order
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int row = pass * 16 + (lane >> 2);
+        const int m = row_of(wrow0 + i * 32 + row);
+        float v[8];
+        const float4 x0 = *reinterpret_cast<const float4*>(st + row * LD3 + col8);
+        const float4 x1 = *reinterpret_cast<const float4*>(st + row * LD3 + col8 + 4);
+        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+        if (m >= 0) {
+          const size_t rmo = size_t(g) * size_t(p.sc) + size_t(m) * size_t(p.ldc) + n;  // row-major
+          if constexpr (EPI == EPI_GELU) {
+            const size_t pko = size_t(g) * size_t(pk_rows(M)) * N + pk_off(m, n, N);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[e]);
+            store8(static_cast<bf16_t*>(p.C) + pko, v);
+          } else if constexpr (EPI == EPI_GELU_SAVE) {
+            static_assert(RM, "the training epilogue writes row-major H and GELU'");
+            float gd[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = gelu_erf_and_grad(v[e] + bias[e], &gd[e]);
+            store8(static_cast<bf16_t*>(p.U) + rmo, gd);
+            store8(static_cast<bf16_t*>(p.C) + rmo, v);
+          } else if constexpr (EPI == EPI_RESID) {
+            const size_t pko = RM ? rmo : size_t(g) * size_t(pk_rows(M)) * N + pk_off(m, n, N);
+            float rr[8];
+            load8(static_cast<const bf16_t*>(p.R) + pko, rr);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = v[e] + bias[e] + rr[e];
+            store8(static_cast<float*>(p.C) + rmo, v);
+          } else if constexpr (EPI == EPI_MOE1) {
+            // hidden rows in the packed layout, m a row of the group's tile-aligned blocks
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e] + bias[e]);
+            store8(static_cast<bf16_t*>(p.C) + pk_off(m, n, N), v);
+          } else {
+            static_assert(EPI == EPI_MOE2, "an epilogue of the eight-wave tiles");
+            const float gv = p.row_gate[m];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = gv * (v[e] + bias[e]);
+            store8(static_cast<bf16_t*>(p.C) + size_t(m) * size_t(N) + n, v);
+          }
+        }
+      }
+      asm volatile("" ::: "memory");
+    }
+  }
+}
+
+// Byte offsets of a lane's two gathered A pieces (wave and wave + 8) at K step 0: tile row
+// r = pk_gather_row(piece, lane) is source row src(r) (negative: past the rows, read as zeros
+// through an offset past the descriptor's end, `bytes`).
+template <typename SrcRow>
+__device__ __forceinline__ void w8_gather_offsets(uint32_t (&offA)[2], int wave, int lane, uint32_t row_bytes,
+                                                  uint32_t bytes, SrcRow src) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int r = pk_gather_row(wave + 8 * c, lane);
+    const uint32_t chunk16 = uint32_t(pk_gather_chunk(r, lane)) * 16u;
+    const int s = src(r);
+    offA[c] = s >= 0 ? uint32_t(s) * row_bytes + chunk16 : bytes;
+  }
 }
 
 // Dense per-token product on packed operands with 256 x 384 tiles of eight waves:
@@ -1306,13 +1411,12 @@ __global__ __launch_bounds__(W8_THREADS, 1) void gemm_bf16_mfma_w8(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t rW =
       make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * (size_t(wbytes) / 2), wbytes);
   f32x16_t acc[4][3];
-  mfma_tile_w8(acc, rA, rW, smem, lds0, K, nt, wave, lane);
+  const uint32_t no_gather[2] = {0u, 0u};
+  mfma_tile_w8<false, 4>(acc, rA, rW, smem, lds0, K, nt, wave, lane, no_gather);
   const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
-  // each group stores its 256 x 192 half with the 256 x 192 tile's epilogue (staging rows
-  // of its four waves after the other group's)
-  const int grp = wave >> 2;
-  tile_epilogue3<EPI, 256>(acc, reinterpret_cast<float*>(smem_g) + grp * 4 * 32 * LD3, p, g, bias_g,
-                           nt * BN6 + grp * BN3, mt * BM, wave & 3, lane);
+  const int m0 = mt * BM;
+  tile_epilogue_w8<EPI>(acc, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN6, wave, lane,
+                        [&](int r) { return m0 + r < M ? m0 + r : -1; });
 }
 
 // Dense per-token product with row-major A (the training forward's saved S and H) and
@@ -1357,6 +1461,39 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_mfma_n384g(GemmArgs
   const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
   tile_epilogue6<EPI, 256, true>(accA, accV, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN6, wave, lane,
                                  [&](int r) { return m0 + r < M ? m0 + r : -1; });
+}
+
+// The training forward's products on eight-wave 256 x 384 tiles: gemm_bf16_mfma_n384g's
+// operands and outputs, mfma_tile_w8's K loop with gathered A.  Same bits.
+template <int EPI>
+__global__ __launch_bounds__(W8_THREADS, 1) void gemm_bf16_mfma_w8g(GemmArgs p) {
+  static_assert(EPI == EPI_GELU_SAVE || EPI == EPI_RESID, "the training forward's epilogues");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[W8_NS * STAGE6_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_g;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nMt = (M + BM - 1) / BM, nNt = N / BN6;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = id / (nMt * nNt);
+  const int rem = id - g * nMt * nNt;
+  int mt, nt;
+  band_tile(rem, nMt, nNt, mt, nt);
+  const int m0 = mt * BM;
+  const uint32_t blk = uint32_t(K / BK) * 16384u;
+  const uint32_t wbytes = uint32_t(pk_rows(N) / 256) * blk;
+  const __amdgpu_buffer_rsrc_t rW =
+      make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * (size_t(wbytes) / 2), wbytes);
+  // A: the token's rows [M x K]; rows past M read as zeros
+  const uint32_t row_bytes = uint32_t(K) * 2u, bytesA = uint32_t(M) * row_bytes;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(g) * size_t(p.sa), bytesA);
+  uint32_t offA[2];
+  w8_gather_offsets(offA, wave, lane, row_bytes, bytesA, [&](int r) { return m0 + r < M ? m0 + r : -1; });
+  f32x16_t acc[4][3];
+  mfma_tile_w8<true, 4>(acc, rA, rW, smem, lds0, K, nt, wave, lane, offA);
+  const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
+  tile_epilogue_w8<EPI, true>(acc, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN6, wave, lane,
+                              [&](int r) { return m0 + r < M ? m0 + r : -1; });
 }
 
 // Sparse-MoE grouped GEMM on prepared expert weights with 256 x 384 tiles: the persistent
@@ -1430,6 +1567,64 @@ __global__ __launch_bounds__(MFMA_THREADS, 1) void gemm_bf16_moe_n384(GemmArgs p
     // output rows: layer 1 the packed hidden block, layer 2 the compacted expert rows
     tile_epilogue6<EPI>(accA, accV, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN6, wave, lane,
                         [&](int r) { return m0 + r < rows ? (GA ? hblk * BM + r : row0 + m0 + r) : -1; }, nib);
+    // every wave is done with its staging rows before the next tile's copies reuse the ring
+    __syncthreads();
+  }
+}
+
+// The Sparse-MoE grouped products on eight-wave 256 x 384 tiles: gemm_bf16_moe_n384's tile
+// walk, operands and outputs, mfma_tile_w8's K loop.  A wave's row blocks past the group's
+// rows are skipped as there.  Same bits.
+template <int EPI>
+__global__ __launch_bounds__(W8_THREADS, 1) void gemm_bf16_moe_w8(GemmArgs p) {
+  static_assert(EPI == EPI_MOE1 || EPI == EPI_MOE2, "the Sparse-MoE epilogues");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_g[W8_NS * STAGE6_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_g;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int N = p.N, K = p.K, G = p.G;
+  const int nNt = N / BN6;
+  const int total = p.tile_start[G] * nNt;
+  const int per_xcd = int(gridDim.x) / NUM_XCD;  // gridDim.x is a multiple of NUM_XCD
+  const int xcd = int(blockIdx.x) % NUM_XCD, slot = int(blockIdx.x) / NUM_XCD;
+  int lo, hi;
+  moe_xcd_span(total, xcd, NUM_XCD, lo, hi);
+  const uint32_t blk = uint32_t(K / BK) * 16384u;
+  const uint32_t wbytes = uint32_t(pk_rows(N) / 256) * blk;
+  constexpr bool GA = EPI == EPI_MOE1;
+
+  for (int tile = lo + slot; tile < hi; tile += per_xcd) {
+    int g, mt, nt;
+    moe_tile_locate(p.tile_start, G, nNt, tile, g, mt, nt);
+    const int row0 = p.group_start[g], rows = p.group_start[g + 1] - row0;
+    const int m0 = mt * BM;
+    const int hblk = p.tile_start[g] + mt;  // the tile's block of the packed hidden rows
+    const __amdgpu_buffer_rsrc_t rW =
+        make_rsrc(static_cast<const uint16_t*>(p.W) + size_t(g) * (size_t(wbytes) / 2), wbytes);
+    uint32_t offA[2] = {0u, 0u};
+    __amdgpu_buffer_rsrc_t rA;
+    if constexpr (GA) {
+      const uint32_t row_bytes = uint32_t(K) * 2u;
+      const uint32_t bytesA = uint32_t(p.a_rows) * row_bytes;
+      rA = make_rsrc(p.A, bytesA);
+      w8_gather_offsets(offA, wave, lane, row_bytes, bytesA,
+                        [&](int r) { return m0 + r < rows ? p.src_row[row0 + m0 + r] : -1; });
+    } else {
+      rA = make_rsrc(static_cast<const uint16_t*>(p.A) + size_t(hblk) * (size_t(blk) / 2), blk);
+    }
+    const int nib =
+        __builtin_amdgcn_readfirstlane(max(0, min(4, (rows - m0 - ((wave >> 1) & 1) * 128 + 31) / 32)));
+    f32x16_t acc[4][3];
+    switch (nib) {
+      case 4: mfma_tile_w8<GA, 4>(acc, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+      case 3: mfma_tile_w8<GA, 3>(acc, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+      case 2: mfma_tile_w8<GA, 2>(acc, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+      case 1: mfma_tile_w8<GA, 1>(acc, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+      default: mfma_tile_w8<GA, 0>(acc, rA, rW, smem, lds0, K, nt, wave, lane, offA); break;
+    }
+    const bf16_t* bias_g = p.bias ? static_cast<const bf16_t*>(p.bias) + size_t(g) * N : nullptr;
+    tile_epilogue_w8<EPI>(acc, reinterpret_cast<float*>(smem_g), p, g, bias_g, nt * BN6, wave, lane,
+                          [&](int r) { return m0 + r < rows ? (GA ? hblk * BM + r : row0 + m0 + r) : -1; }, nib);
     // every wave is done with its staging rows before the next tile's copies reuse the ring
     __syncthreads();
   }
@@ -1979,6 +2174,14 @@ bool gemm_moe_supported(int N, int K, int64_t a_rows, bool packed) {
          uint64_t(a_rows) * N * 2 < lim;
 }
 
+// The training forward's and the Sparse-MoE products on prepared weights run eight-wave
+// 256 x 384 tiles; RMX_WIDE_TILES=always keeps them on the four-wave ones (tests and tuning;
+// read at each launch; the same bits).
+static bool four_wave_tiles() {
+  const char* force = getenv("RMX_WIDE_TILES");
+  return force && strcmp(force, "always") == 0;
+}
+
 hipError_t launch_gemm_moe(int epi, const GemmArgs& args, hipStream_t stream) {
   if (args.G == 0) return hipSuccess;
   GemmArgs a = args;  // outputs are the compacted rows [rows, N]
@@ -1990,10 +2193,16 @@ hipError_t launch_gemm_moe(int epi, const GemmArgs& args, hipStream_t stream) {
   const int grid = ((cus + NUM_XCD - 1) / NUM_XCD) * NUM_XCD;  // one workgroup per CU, whole XCDs
   if (a.packed) {
     if (a.N % BN6 != 0) return hipErrorInvalidValue;
-    if (epi == EPI_MOE1)
-      hipLaunchKernelGGL((gemm_bf16_moe_n384<EPI_MOE1>), dim3(grid), dim3(MFMA_THREADS), 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_bf16_moe_n384<EPI_MOE2>), dim3(grid), dim3(MFMA_THREADS), 0, stream, a);
+    if (four_wave_tiles()) {
+      if (epi == EPI_MOE1)
+        hipLaunchKernelGGL((gemm_bf16_moe_n384<EPI_MOE1>), dim3(grid), dim3(MFMA_THREADS), 0, stream, a);
+      else
+        hipLaunchKernelGGL((gemm_bf16_moe_n384<EPI_MOE2>), dim3(grid), dim3(MFMA_THREADS), 0, stream, a);
+    } else if (epi == EPI_MOE1) {
+      hipLaunchKernelGGL((gemm_bf16_moe_w8<EPI_MOE1>), dim3(grid), dim3(W8_THREADS), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((gemm_bf16_moe_w8<EPI_MOE2>), dim3(grid), dim3(W8_THREADS), 0, stream, a);
+    }
   } else if (epi == EPI_MOE1) {
     hipLaunchKernelGGL((gemm_bf16_moe<EPI_MOE1>), dim3(grid), dim3(MFMA_THREADS), 0, stream, a);
   } else {
@@ -2327,10 +2536,16 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& args, hipStream_t str
         a.lda != a.K || a.ldc != a.N || a.sa != int64_t(a.M) * a.K || a.sc != int64_t(a.M) * a.N)
       return hipErrorInvalidValue;
     const int tiles = a.G * ((a.M + BM - 1) / BM) * (a.N / BN6);
-    if (epi == EPI_GELU_SAVE)
-      hipLaunchKernelGGL((gemm_bf16_mfma_n384g<EPI_GELU_SAVE>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_bf16_mfma_n384g<EPI_RESID>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+    if (four_wave_tiles()) {
+      if (epi == EPI_GELU_SAVE)
+        hipLaunchKernelGGL((gemm_bf16_mfma_n384g<EPI_GELU_SAVE>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+      else
+        hipLaunchKernelGGL((gemm_bf16_mfma_n384g<EPI_RESID>), dim3(tiles), dim3(MFMA_THREADS), 0, stream, a);
+    } else if (epi == EPI_GELU_SAVE) {
+      hipLaunchKernelGGL((gemm_bf16_mfma_w8g<EPI_GELU_SAVE>), dim3(tiles), dim3(W8_THREADS), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((gemm_bf16_mfma_w8g<EPI_RESID>), dim3(tiles), dim3(W8_THREADS), 0, stream, a);
+    }
     return hipGetLastError();
   }
   if (a.packed) {
