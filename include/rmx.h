@@ -215,7 +215,9 @@ rmx_status rmx_pack_weights(rmx_handle* h, const rmx_weights* w, int32_t L, void
  * tuning; every choice gives the same bits): RMX_WIDE_TILES = always | half | pair | pairhalf |
  * wide8 | never (256 x 384, 128 x 384, 256 x 192 or 128 x 192 with two workgroups per CU,
  * 256 x 384 with eight waves, or 256 x 256 tiles, above 128 rows per token; the 384-wide
- * shapes need N % 384 == 0, the 192-wide ones N % 192 == 0) and
+ * shapes need N % 384 == 0, the 192-wide ones N % 192 == 0; `always` also keeps the
+ * training forward's and the Sparse-MoE products on four-wave instead of eight-wave
+ * 256 x 384 tiles) and
  * RMX_NARROW_TILES = always | never (64 x 128 or 64 x 256 tiles up to 128 rows per token).
  * Other values are ignored. */
 
